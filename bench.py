@@ -1,10 +1,31 @@
 #!/usr/bin/env python3
-"""Placeholder; replaced by the full benchmark below once the HIP path exists."""
+"""Benchmark: sparse MLA prefill (indexer -> top-k -> absorbed sparse MLA) on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+mla_indexer_score, mla_topk_select and mla_sparse_prefill (or, for a dense
+workload, mla_sparse_prefill alone). Inputs are resident in HBM before the
+timed region starts. Prints one JSON line.
+
+Default workload: 32,768-token sparse prefill, 64 heads, indexer 64 x 128
+(bf16), top-2,048, FP8-E4M3 latent KV with a per-token scale.
+"""
 from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
 D_QK, D_V = 576, 512
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}     # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
 
 
 # ------------------------------------------------------------- accounting --
@@ -45,5 +66,191 @@ def workload_flops(wl) -> dict:
     return {"indexer": f_idx, "attention": f_attn, **pc}
 
 
+def kernel_bytes(wl, kv_dtype: str) -> dict:
+    """Algorithmic HBM bytes per launch of each kernel (inputs read once,
+    outputs written once; gathered rows counted per selected pair)."""
+    pc = pair_counts(wl)
+    row = D_QK + 4 if kv_dtype == "fp8" else 2 * D_QK
+    q_bytes = wl.total_q * wl.n_heads * (2 * D_QK + 2 * D_V + 4)
+    out = {"attention": pc["selected"] * (row + (0 if wl.dense else 4)) + q_bytes}
+    if not wl.dense:
+        out["indexer"] = pc["causal"] * 4 + wl.total_q * wl.idx_heads * (2 * wl.idx_dim + 4) \
+            + wl.total_kv * 2 * wl.idx_dim
+        out["topk"] = pc["causal"] * 4 + wl.total_q * wl.topk * 4
+    return out
+
+
+# ------------------------------------------------------------------ bench --
+def cpu_baseline(inp, wl, budget_s: float = 12.0, seed: int = 7) -> dict:
+    """The fp64 oracle (indexer -> top-k -> attention) timed on the host cores
+    on a sample of query rows, extrapolated to the whole workload by FLOP
+    weight (row costs span orders of magnitude)."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    q_pos = wl.q_pos()
+    fl_pair_i = indexer_flop_per_pair(wl.idx_heads, wl.idx_dim) if not wl.dense else 0
+    fl_pair_a = attn_flop_per_pair(wl.n_heads)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        if wl.dense:
+            oracle.attention_rows(inp, rows, None)
+        else:
+            sc = oracle.indexer_rows(inp, rows)
+            idx = oracle.topk_rows(sc, q_pos[rows], wl.topk)
+            oracle.attention_rows(inp, rows, idx)
+        dt = time.perf_counter() - t0
+        p = q_pos[rows].astype(np.int64)
+        sel = p + 1 if wl.dense else np.minimum(p + 1, wl.topk)
+        return dt, float(((p + 1) * fl_pair_i + sel * fl_pair_a).sum())
+
+    oracle.lib()
+    rows = np.sort(rng.choice(wl.total_q, 8, replace=False))
+    dt, fl = run(rows)                                 # calibration sample
+    n = int(min(wl.total_q, max(8, 8 * budget_s / max(dt, 1e-3))))
+    rows = np.sort(rng.choice(wl.total_q, n, replace=False))
+    dt, fl = run(rows)
+    total_fl = sum(workload_flops(wl)[k] for k in ("indexer", "attention"))
+    t_full = dt * total_fl / fl
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": wl.total_q / t_full, "unit": "query-tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d uniformly drawn query rows of the same workload (whole path in fp64: "
+                      "indexer over every earlier key, top-k, attention), %.1f s wall, "
+                      "extrapolated by FLOP weight" % (n, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sparse32k")
+    ap.add_argument("--kv-dtype", default=None, help="override the workload's KV dtype (bf16/fp8)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(one GPU runs its own context-parallel share; see --workload cp131k).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_inputs
+    import sparse_mla_long_amd as sm
+
+    sm.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = mla_inputs.WORKLOADS[args.workload]
+    kv_dtype = args.kv_dtype or wl.kv_dtype
+    inp = mla_inputs.make_inputs(wl, dev, kv_dtype=kv_dtype)
+    batch = sm.Batch.from_inputs(inp, dev)
+    scores = None if wl.dense else torch.empty((wl.total_q, wl.max_kv_len), dtype=torch.float32,
+                                               device=dev)
+    indices = None if wl.dense else torch.empty((wl.total_q, wl.topk), dtype=torch.int32,
+                                                device=dev)
+    out = torch.empty((wl.total_q, wl.n_heads, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.total_q, wl.n_heads), dtype=torch.float32, device=dev)
+    names = ["attention"] if wl.dense else ["indexer", "topk", "attention"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        if wl.dense:
+            mark(0)
+            sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], None, wl.sm_scale,
+                              out=out, lse=lse)
+            mark(1)
+            return
+        mark(0)
+        sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"], scores=scores)
+        mark(1)
+        sm.topk_select(batch, scores, wl.topk, indices=indices)
+        mark(2)
+        sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], indices, wl.sm_scale,
+                          out=out, lse=lse)
+        mark(3)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per_kernel_ms = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
+                                       for s in range(args.steps)]))
+                     for i, n in enumerate(names)}
+    fl = workload_flops(wl)
+    byts = kernel_bytes(wl, kv_dtype)
+    kern = {}
+    for n in names:
+        t = per_kernel_ms[n] * 1e-3
+        d = {"ms": per_kernel_ms[n]}
+        if n in ("indexer", "attention"):
+            tf = fl[n] / t / 1e12
+            d.update({"tflops": tf, "bound": "mfma", "peak_tflops": PEAK_TFLOPS["bf16"],
+                      "frac": tf / PEAK_TFLOPS["bf16"]})
+        if n in byts:
+            d["algo_bytes"] = byts[n]
+            d["gbs"] = byts[n] / t / 1e9
+        kern[n] = d
+    kern["topk"] = kern.get("topk", {})
+    if "topk" in per_kernel_ms:
+        kern["topk"].update({"bound": "hbm", "peak_gbs": PEAK_HBM_GBS,
+                             "frac": kern["topk"]["gbs"] / PEAK_HBM_GBS})
+    else:
+        kern.pop("topk")
+    dominant = max(names, key=lambda n: per_kernel_ms[n])
+    dk = kern[dominant]
+    if dk.get("bound") == "mfma":
+        roof = {"bound": "mfma", "kernel": dominant, "achieved": dk["tflops"],
+                "peak": dk["peak_tflops"], "unit": "TFLOP/s", "frac": dk["frac"], "traffic": None}
+    else:
+        roof = {"bound": "hbm", "kernel": dominant, "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": dk["frac"], "traffic": None}
+
+    ms_step = elapsed / args.steps * 1e3
+    t_kernels = sum(per_kernel_ms.values()) * 1e-3
+    p_attn = PEAK_TFLOPS["fp8" if kv_dtype == "fp8" else "bf16"]
+    mfma_frac = (fl["indexer"] / (PEAK_TFLOPS["bf16"] * 1e12) +
+                 fl["attention"] / (p_attn * 1e12)) / (ms_step * 1e-3)
+    res = {
+        "metric": "prefill query-tokens/s on 1 MI355X + % MFMA peak (64 heads, top-k 2048)",
+        "value": wl.total_q / (ms_step * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "seq_lens": list(wl.kv_lens), "total_q": wl.total_q,
+                   "n_heads": wl.n_heads, "indexer": "%dx%d" % (wl.idx_heads, wl.idx_dim),
+                   "topk": None if wl.dense else wl.topk, "kv_dtype": kv_dtype,
+                   "dense": wl.dense, "parallelism": "single GPU"},
+        "mfma_peak_frac": mfma_frac,
+        "mfma_peak_frac_note": "(F_indexer/P_bf16 + F_attention/P_attn)/t_step, P_attn = fp8 peak "
+                               "for FP8 KV whatever MFMA type the kernel uses",
+        "flops": {"indexer": fl["indexer"], "attention": fl["attention"]},
+        "kernels": kern,
+        "kernel_sum_ms": t_kernels * 1e3,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
 if __name__ == "__main__":
-    raise SystemExit("benchmark not built yet")
+    main()

@@ -1,0 +1,157 @@
+/*
+ * mla_sparse.h -- C ABI of an MI355X (gfx950) library for GLM-style causal
+ * prefill attention over a multi-head latent attention (MLA) KV cache.
+ *
+ * The path has three calls, run in this order for one attention layer:
+ *
+ *   mla_indexer_score   the indexer scores every earlier token of each query
+ *                       (spke.com GLM-5.3 PCP/DCP article, section "Warum nicht
+ *                       TP oder DP?": it scores every earlier token to pick the
+ *                       2,048 that sparse MLA attends to; its cost grows with
+ *                       the square of the prompt length, section "PCP").
+ *   mla_topk_select     keeps the k best-scoring earlier tokens per query.
+ *   mla_sparse_prefill  absorbed (MQA-form) MLA attention over the kept tokens:
+ *                       one 576-value latent row per token (512 latent + 64
+ *                       rope) serves every head, QK over 576 dims and PV over
+ *                       the first 512 (same article, footnote 1), with the
+ *                       log-sum-exp of every (query, head) as a second output
+ *                       (the mergeable quantity of its section "DCP").
+ *
+ * Batches are packed: sequence b owns query rows [cu_q[b], cu_q[b+1]) and
+ * latent-KV rows [cu_kv[b], cu_kv[b+1]); every query carries its true
+ * absolute position p_i = q_pos[i] inside its sequence, 0 <= p_i < L_b. One
+ * call therefore covers whole prompts, one GPU's context-parallel share (the
+ * queries of chunks r and 2N-1-r of a 2N-chunk prompt against the full
+ * gathered KV -- article, section "PCP") or new suffix tokens resuming behind
+ * a cached prefix. A query attends to the keys j <= p_i of its own sequence
+ * (its own token included).
+ *
+ * Conventions shared by every call:
+ *  - Pointers marked "device" must point to GPU memory of the current HIP
+ *    device; "host" pointers to CPU memory read during the call only.
+ *  - The caller owns every buffer. The library allocates no memory, keeps no
+ *    pointer after a call returns, holds no mutable global state and is safe
+ *    to call from several host threads.
+ *  - Calls validate their arguments on the host, enqueue kernels on `stream`
+ *    (a hipStream_t; NULL means the null stream) and return without waiting.
+ *    Outputs are valid once the stream has reached that point; inputs must
+ *    stay alive until then.
+ *  - Return codes: MLA_OK; MLA_ERR_INVALID_ARG (nothing was enqueued: a null
+ *    required pointer, a bad scalar, host cu_seqlens that are not monotone or
+ *    do not end at the totals, a misaligned pointer or stride);
+ *    MLA_ERR_UNSUPPORTED (a valid shape this build has no kernel for; nothing
+ *    enqueued); MLA_ERR_HIP (a HIP call or launch failed). mla_last_error()
+ *    gives a human-readable reason for the last failure on this thread.
+ *  - q_pos[i] < L_b is a caller contract on device data; it is not checked
+ *    (checking would need a device synchronisation).
+ *  - bf16 is IEEE bfloat16; fp8 is OCP E4M3 (e4m3fn: bias 7, max 448, no inf).
+ */
+#ifndef MLA_SPARSE_H
+#define MLA_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+#define MLA_QK_DIM 576 /* absorbed query / latent KV row width: 512 latent + 64 rope */
+#define MLA_V_DIM 512  /* output width per head: the latent part of the row */
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1,
+    MLA_ERR_UNSUPPORTED = 2,
+    MLA_ERR_HIP = 3
+} mla_status_t;
+
+typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_dtype_t;
+
+/* Ragged batch description. The host copies of cu_seqlens are validated and
+ * used to size the launches; the device copies must hold the same values. */
+typedef struct {
+    int32_t num_seqs;               /* B >= 1                                         */
+    int32_t total_q;                /* cu_seqlens_q[B]  (>= 0)                          */
+    int32_t total_kv;               /* cu_seqlens_kv[B] (>= 0)                          */
+    int32_t max_kv_len;             /* max_b L_b                                       */
+    const int32_t *cu_seqlens_q_host;  /* host   [B+1], cu[0] = 0, non-decreasing       */
+    const int32_t *cu_seqlens_kv_host; /* host   [B+1], cu[0] = 0, non-decreasing       */
+    const int32_t *cu_seqlens_q;       /* device [B+1], same values                     */
+    const int32_t *cu_seqlens_kv;      /* device [B+1], same values                     */
+    const int32_t *q_pos;              /* device [total_q], 0 <= q_pos[i] < L_b(i)      */
+} mla_batch_t;
+
+/* Indexer scores (spke.com article, section "Warum nicht TP oder DP?"; one
+ * indexer key per token shared by all indexer heads, footnote 3). For every
+ * query i and every key j <= q_pos[i] of its sequence:
+ *
+ *     scores[i * ld_scores + j] = sum_h w[i, h] * max(0, sum_d q_idx[i, h, d] * k_idx[j, d])
+ *
+ * with fp32 accumulation of exact bf16 x bf16 products. Entries j > q_pos[i]
+ * are not written.
+ *   q_idx   device [total_q, n_heads, head_dim] bf16, 16-byte aligned
+ *   k_idx   device [total_kv, head_dim] bf16 (row = cu_seqlens_kv[b] + j), 16-byte aligned
+ *   w       device [total_q, n_heads] fp32
+ *   scores  device [total_q, ld_scores] fp32; ld_scores >= max_kv_len
+ * Supported: 1 <= n_heads <= 64, head_dim in {64, 128}. */
+mla_status_t mla_indexer_score(const mla_batch_t *batch, const void *q_idx, const void *k_idx,
+                               const float *w, int32_t n_heads, int32_t head_dim, float *scores,
+                               int64_t ld_scores, void *stream);
+
+/* Top-k selection over the indexer scores of each query (same section: keep
+ * the 2,048 best earlier tokens). For query i with n_i = q_pos[i] + 1 scored
+ * keys: if n_i <= k, every key 0..n_i-1 is kept; otherwise the k largest
+ * scores are kept, equal scores going to the smaller j (-0.0 equals +0.0).
+ * indices[i, 0:k] lists the kept local key indices in ascending order and is
+ * padded with -1. Scores must not be NaN.
+ *   scores  device [total_q, ld_scores] fp32 (row i read for j <= q_pos[i])
+ *   indices device [total_q, k] int32
+ * Supported: 1 <= k <= 4096. */
+mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int64_t ld_scores,
+                             int32_t k, int32_t *indices, void *stream);
+
+/* Absorbed MLA attention over selected latent rows (spke.com article,
+ * footnote 1 and section "PCP": one latent row read per selected key serves
+ * all heads; QK over 576 dims, PV over 512; dense path of section
+ * "Ausprobieren" when indices == NULL). For query i, head h and the set S_i of
+ * its selected keys (entries of indices[i, :] with 0 <= j <= q_pos[i];
+ * others are skipped; with indices == NULL, S_i = {0..q_pos[i]}):
+ *
+ *     K_j     = decode(kv row cu_seqlens_kv[b] + j)   (bf16, or e4m3 * kv_scale)
+ *     z_j     = sm_scale * sum_{d<576} q[i, h, d] * K_j[d]
+ *     lse[i,h]= ln sum_{j in S_i} exp(z_j)
+ *     out[i,h,c] = sum_{j in S_i} exp(z_j - lse[i,h]) * K_j[c],   c < 512
+ *
+ * An empty S_i gives out = 0 and lse = -inf. Duplicate entries in a row of
+ * indices are a caller error (the key would be counted twice).
+ *   q        device [total_q, n_heads, 576] bf16, 16-byte aligned
+ *   kv       device, row r at byte offset r * kv_row_stride: 576 bf16 or 576 e4m3 codes;
+ *            16-byte aligned, kv_row_stride a multiple of 16 and >= the row size
+ *   kv_scale device fp32, scale of row r at byte offset r * kv_scale_stride (a
+ *            multiple of 4); required for MLA_KV_FP8_E4M3, ignored for bf16
+ *   indices  device [total_q, k] int32 local key indices, or NULL (dense causal)
+ *   out      device [total_q, n_heads, 512] bf16 (round to nearest even)
+ *   lse      device [total_q, n_heads] fp32, natural log (sm_scale included)
+ * Supported: n_heads in {8, 16, 32, 64}; 1 <= k <= 65536 when indices != NULL. */
+mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const void *kv,
+                                const float *kv_scale, mla_kv_dtype_t kv_dtype,
+                                int64_t kv_row_stride, int64_t kv_scale_stride,
+                                const int32_t *indices, int32_t k, int32_t n_heads,
+                                float sm_scale, void *out, float *lse, void *stream);
+
+/* Static description of a status code. */
+const char *mla_status_string(mla_status_t status);
+
+/* Reason for the last non-OK status returned on the calling thread ("" if none). */
+const char *mla_last_error(void);
+
+/* MLA_ABI_VERSION of the built library. */
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_SPARSE_H */

@@ -175,19 +175,31 @@ def _seq_of_rows(cu_q: np.ndarray, rows: np.ndarray) -> np.ndarray:
     return np.searchsorted(cu_q, rows, side="right") - 1
 
 
+def _take_rows(x, rows: np.ndarray) -> np.ndarray:
+    """Rows of a (possibly device-resident) tensor, copied to host numpy."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return as_numpy(x[torch.as_tensor(rows, dtype=torch.long, device=x.device)])
+    except ImportError:
+        pass
+    return np.asarray(x)[rows]
+
+
 def indexer_rows(batch: dict, rows: Sequence[int]):
     """Oracle scores for selected global query rows of a packed batch.
     Returns a list of fp32 arrays, row r of length q_pos[r] + 1."""
     rows = np.asarray(rows, dtype=np.int64)
     cu_q, cu_kv = batch["cu_seqlens_q_host"], batch["cu_seqlens_kv_host"]
     q_pos = np.asarray(batch["q_pos_host"])
-    qI, kI, w = as_numpy(batch["q_idx"]), as_numpy(batch["k_idx"]), as_numpy(batch["w"])
+    kI = as_numpy(batch["k_idx"])
+    qI, w = _take_rows(batch["q_idx"], rows), _take_rows(batch["w"], rows)
     seq = _seq_of_rows(cu_q, rows)
     result = [None] * len(rows)
     for b in np.unique(seq):
         sel = np.nonzero(seq == b)[0]
         r = rows[sel]
-        sc = indexer_seq(qI[r], kI[cu_kv[b]:cu_kv[b + 1]], w[r], q_pos[r])
+        sc = indexer_seq(qI[sel], kI[cu_kv[b]:cu_kv[b + 1]], w[sel], q_pos[r])
         for t, s in zip(sel, sc):
             result[t] = s[: q_pos[rows[t]] + 1].copy()
     return result
@@ -212,7 +224,7 @@ def attention_rows(batch: dict, rows: Sequence[int], indices=None, sm_scale=None
     q_pos = np.asarray(batch["q_pos_host"])
     if sm_scale is None:
         sm_scale = batch["workload"].sm_scale
-    q = as_numpy(batch["q"])
+    q = _take_rows(batch["q"], rows)
     kv = as_numpy(batch["kv"])
     fp8 = batch["kv_dtype"] == "fp8"
     scale = as_numpy(batch["kv_scale"]) if fp8 else None
@@ -224,7 +236,7 @@ def attention_rows(batch: dict, rows: Sequence[int], indices=None, sm_scale=None
         sel = np.nonzero(seq == b)[0]
         r = rows[sel]
         lo, hi = cu_kv[b], cu_kv[b + 1]
-        o, l = attention_seq(q[r], kv[lo:hi], q_pos[r], sm_scale,
+        o, l = attention_seq(q[sel], kv[lo:hi], q_pos[r], sm_scale,
                              kv_scale=None if scale is None else scale[lo:hi],
                              indices=None if indices is None else np.asarray(indices)[sel],
                              kv_fmt=FMT_E4M3 if fp8 else FMT_BF16)

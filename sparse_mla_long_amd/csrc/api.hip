@@ -1,0 +1,199 @@
+// C ABI of the sparse-MLA prefill library: host-side validation and launch.
+//
+// Every check runs on the host before the first HIP call, so a rejected call
+// enqueues nothing and touches no device. Device data (q_pos, indices) is
+// trusted; kernels clamp positions into their sequence so a bad q_pos cannot
+// read outside the sequence's rows.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+#include "kernels.h"
+#include "mla_sparse.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status_t fail(mla_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+mla_status_t fail(mla_status_t s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+mla_status_t ok() {
+    g_last_error.clear();
+    return MLA_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validates the batch description; on success fills the device view.
+mla_status_t check_batch(const mla_batch_t *b, mla::BatchDev *dev) {
+    if (!b) return fail(MLA_ERR_INVALID_ARG, "batch is NULL");
+    if (b->num_seqs < 1) return fail(MLA_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", b->num_seqs);
+    if (b->total_q < 0 || b->total_kv < 0 || b->max_kv_len < 0)
+        return fail(MLA_ERR_INVALID_ARG, "negative total_q / total_kv / max_kv_len");
+    if (!b->cu_seqlens_q_host || !b->cu_seqlens_kv_host)
+        return fail(MLA_ERR_INVALID_ARG, "host cu_seqlens are NULL");
+    const int32_t *cq = b->cu_seqlens_q_host, *ck = b->cu_seqlens_kv_host;
+    if (cq[0] != 0 || ck[0] != 0) return fail(MLA_ERR_INVALID_ARG, "cu_seqlens must start at 0");
+    int32_t max_len = 0;
+    for (int32_t s = 0; s < b->num_seqs; ++s) {
+        if (cq[s + 1] < cq[s] || ck[s + 1] < ck[s])
+            return fail(MLA_ERR_INVALID_ARG, "cu_seqlens decrease at sequence %d", s);
+        const int32_t nq = cq[s + 1] - cq[s], nk = ck[s + 1] - ck[s];
+        if (nq > 0 && nk == 0)
+            return fail(MLA_ERR_INVALID_ARG, "sequence %d has queries but no KV rows", s);
+        if (nk > max_len) max_len = nk;
+    }
+    if (cq[b->num_seqs] != b->total_q || ck[b->num_seqs] != b->total_kv)
+        return fail(MLA_ERR_INVALID_ARG, "cu_seqlens end at (%d, %d), totals are (%d, %d)",
+                    cq[b->num_seqs], ck[b->num_seqs], b->total_q, b->total_kv);
+    if (b->max_kv_len != max_len)
+        return fail(MLA_ERR_INVALID_ARG, "max_kv_len is %d, longest sequence has %d rows",
+                    b->max_kv_len, max_len);
+    if (b->total_q > 0 && (!b->cu_seqlens_q || !b->cu_seqlens_kv || !b->q_pos))
+        return fail(MLA_ERR_INVALID_ARG, "device cu_seqlens / q_pos are NULL");
+    dev->cu_q = b->cu_seqlens_q;
+    dev->cu_kv = b->cu_seqlens_kv;
+    dev->q_pos = b->q_pos;
+    dev->num_seqs = b->num_seqs;
+    dev->total_q = b->total_q;
+    return MLA_OK;
+}
+
+mla_status_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_indexer_score(const mla_batch_t *batch, const void *q_idx, const void *k_idx,
+                               const float *w, int32_t n_heads, int32_t head_dim, float *scores,
+                               int64_t ld_scores, void *stream) {
+    mla::IndexerArgs a{};
+    mla_status_t st = check_batch(batch, &a.batch);
+    if (st != MLA_OK) return st;
+    if (n_heads < 1) return fail(MLA_ERR_INVALID_ARG, "n_heads must be >= 1 (got %d)", n_heads);
+    if (head_dim < 1) return fail(MLA_ERR_INVALID_ARG, "head_dim must be >= 1 (got %d)", head_dim);
+    if (n_heads > 64) return fail(MLA_ERR_UNSUPPORTED, "indexer n_heads %d > 64", n_heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(MLA_ERR_UNSUPPORTED, "indexer head_dim %d not in {64, 128}", head_dim);
+    if (ld_scores < batch->max_kv_len)
+        return fail(MLA_ERR_INVALID_ARG, "ld_scores %lld < max_kv_len %d", (long long)ld_scores,
+                    batch->max_kv_len);
+    if (batch->total_q == 0) return ok();
+    if (!q_idx || !k_idx || !w || !scores)
+        return fail(MLA_ERR_INVALID_ARG, "q_idx / k_idx / w / scores is NULL");
+    if (!aligned(q_idx, 16) || !aligned(k_idx, 16))
+        return fail(MLA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
+    if (!aligned(w, 4) || !aligned(scores, 4))
+        return fail(MLA_ERR_INVALID_ARG, "w and scores must be 4-byte aligned");
+    int64_t blocks = 0;
+    for (int32_t s = 0; s < batch->num_seqs; ++s) {
+        const int32_t nq = batch->cu_seqlens_q_host[s + 1] - batch->cu_seqlens_q_host[s];
+        blocks += (nq + mla::kIdxQueriesPerBlock - 1) / mla::kIdxQueriesPerBlock;
+    }
+    a.q_idx = (const __bf16 *)q_idx;
+    a.k_idx = (const __bf16 *)k_idx;
+    a.w = w;
+    a.scores = scores;
+    a.ld = ld_scores;
+    a.n_heads = n_heads;
+    a.head_dim = head_dim;
+    a.n_blocks = (int32_t)blocks;
+    return hip_status(mla::launch_indexer(a, (hipStream_t)stream), "indexer launch");
+}
+
+mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int64_t ld_scores,
+                             int32_t k, int32_t *indices, void *stream) {
+    mla::TopkArgs a{};
+    mla_status_t st = check_batch(batch, &a.batch);
+    if (st != MLA_OK) return st;
+    if (k < 1) return fail(MLA_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+    if (k > 4096) return fail(MLA_ERR_UNSUPPORTED, "k %d > 4096", k);
+    if (ld_scores < batch->max_kv_len)
+        return fail(MLA_ERR_INVALID_ARG, "ld_scores %lld < max_kv_len %d", (long long)ld_scores,
+                    batch->max_kv_len);
+    if (batch->total_q == 0) return ok();
+    if (!scores || !indices) return fail(MLA_ERR_INVALID_ARG, "scores / indices is NULL");
+    if (!aligned(scores, 4) || !aligned(indices, 4))
+        return fail(MLA_ERR_INVALID_ARG, "scores and indices must be 4-byte aligned");
+    a.scores = scores;
+    a.ld = ld_scores;
+    a.indices = indices;
+    a.k = k;
+    a.max_row = batch->max_kv_len;
+    return hip_status(mla::launch_topk(a, (hipStream_t)stream), "top-k launch");
+}
+
+mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const void *kv,
+                                const float *kv_scale, mla_kv_dtype_t kv_dtype,
+                                int64_t kv_row_stride, int64_t kv_scale_stride,
+                                const int32_t *indices, int32_t k, int32_t n_heads,
+                                float sm_scale, void *out, float *lse, void *stream) {
+    mla::AttnArgs a{};
+    mla_status_t st = check_batch(batch, &a.batch);
+    if (st != MLA_OK) return st;
+    if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
+        return fail(MLA_ERR_INVALID_ARG, "unknown kv_dtype %d", (int)kv_dtype);
+    const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
+    const int64_t row_bytes = fp8 ? MLA_QK_DIM : 2 * MLA_QK_DIM;
+    if (kv_row_stride < row_bytes || kv_row_stride % 16 != 0)
+        return fail(MLA_ERR_INVALID_ARG, "kv_row_stride %lld must be >= %lld and a multiple of 16",
+                    (long long)kv_row_stride, (long long)row_bytes);
+    if (fp8 && (kv_scale_stride < 4 || kv_scale_stride % 4 != 0))
+        return fail(MLA_ERR_INVALID_ARG, "kv_scale_stride %lld must be a positive multiple of 4",
+                    (long long)kv_scale_stride);
+    if (!(sm_scale > 0.f) || !(sm_scale < 1e30f))
+        return fail(MLA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+    if (indices && k < 1) return fail(MLA_ERR_INVALID_ARG, "k must be >= 1 with indices (got %d)", k);
+    if (n_heads != 8 && n_heads != 16 && n_heads != 32 && n_heads != 64)
+        return fail(MLA_ERR_UNSUPPORTED, "n_heads %d not in {8, 16, 32, 64}", n_heads);
+    if (indices && k > 65536) return fail(MLA_ERR_UNSUPPORTED, "k %d > 65536", k);
+    if (batch->total_q == 0) return ok();
+    if (!q || !kv || !out || !lse || (fp8 && !kv_scale))
+        return fail(MLA_ERR_INVALID_ARG, "q / kv / out / lse%s is NULL", fp8 ? " / kv_scale" : "");
+    if (!aligned(q, 16) || !aligned(kv, 16))
+        return fail(MLA_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");
+    if (!aligned(out, 2) || !aligned(lse, 4) || (fp8 && !aligned(kv_scale, 4)) ||
+        (indices && !aligned(indices, 4)))
+        return fail(MLA_ERR_INVALID_ARG, "out / lse / kv_scale / indices misaligned");
+    a.q = (const __bf16 *)q;
+    a.kv = (const uint8_t *)kv;
+    a.kv_scale = (const uint8_t *)kv_scale;
+    a.kv_stride = kv_row_stride;
+    a.scale_stride = kv_scale_stride;
+    a.indices = indices;
+    a.k = indices ? k : 0;
+    a.n_heads = n_heads;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    a.out = (__bf16 *)out;
+    a.lse = lse;
+    return hip_status(mla::launch_attention(a, fp8, (hipStream_t)stream), "attention launch");
+}
+
+const char *mla_status_string(mla_status_t s) {
+    switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument, nothing enqueued";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape not supported, nothing enqueued";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP call or kernel launch failed";
+    }
+    return "unknown mla_status_t";
+}
+
+const char *mla_last_error(void) { return g_last_error.c_str(); }
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Launch interfaces of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct BatchDev {
+    const int32_t *cu_q;
+    const int32_t *cu_kv;
+    const int32_t *q_pos;
+    int32_t num_seqs;
+    int32_t total_q;
+};
+
+struct IndexerArgs {
+    BatchDev batch;
+    const __bf16 *q_idx;   // [total_q, n_heads, head_dim]
+    const __bf16 *k_idx;   // [total_kv, head_dim]
+    const float *w;        // [total_q, n_heads]
+    float *scores;         // [total_q, ld]
+    int64_t ld;
+    int32_t n_heads;
+    int32_t head_dim;
+    int32_t n_blocks;      // sum over sequences of ceil(n_q(b) / queries per block)
+};
+constexpr int kIdxQueriesPerBlock = 8;
+
+struct TopkArgs {
+    BatchDev batch;
+    const float *scores;
+    int64_t ld;
+    int32_t *indices;      // [total_q, k]
+    int32_t k;
+    int32_t max_row;       // max_kv_len: longest possible score row
+};
+
+struct AttnArgs {
+    BatchDev batch;
+    const __bf16 *q;            // [total_q, n_heads, 576]
+    const uint8_t *kv;          // row r at kv + r * kv_stride
+    const uint8_t *kv_scale;    // fp32 scale of row r at kv_scale + r * scale_stride
+    int64_t kv_stride;
+    int64_t scale_stride;
+    const int32_t *indices;     // [total_q, k] or null (dense causal)
+    int32_t k;
+    int32_t n_heads;
+    float scale_log2;           // sm_scale * log2(e)
+    __bf16 *out;                // [total_q, n_heads, 512]
+    float *lse;                 // [total_q, n_heads]
+};
+
+hipError_t launch_indexer(const IndexerArgs &a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs &a, bool fp8, hipStream_t s);
+
+}  // namespace mla

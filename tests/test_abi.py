@@ -1,0 +1,160 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call
+(so the failure paths are exercised here with fake device pointers that are
+never dereferenced)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_mla_long_amd as sm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_sparse.h")
+FAKE = 0x10000          # 16-byte aligned, never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sm.LIB_PATH):
+        pytest.skip("library not built (run __graft_entry__.build())")
+    return sm.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z_ ]+\*?\s*(mla_[a-z_]+)\(", text, flags=re.M)))
+
+
+def test_header_declares_the_path(lib):
+    names = declared_functions()
+    assert {"mla_indexer_score", "mla_topk_select", "mla_sparse_prefill"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_exports_match_the_header():
+    if not os.path.exists(sm.LIB_PATH):
+        pytest.skip("library not built")
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", sm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (mla_[a-z_]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mla_abi_version() == 1
+    for s in range(4):
+        assert lib.mla_status_string(s)
+    assert b"unknown" in lib.mla_status_string(99)
+
+
+def make_batch(cu_q=(0, 4), cu_kv=(0, 10), max_kv=None, total_q=None, total_kv=None, num=None):
+    cq = np.asarray(cu_q, np.int32)
+    ck = np.asarray(cu_kv, np.int32)
+    keep = (cq, ck)
+    b = sm.MlaBatch(len(cq) - 1 if num is None else num,
+                    int(cq[-1]) if total_q is None else total_q,
+                    int(ck[-1]) if total_kv is None else total_kv,
+                    int(np.diff(ck).max()) if max_kv is None else max_kv,
+                    cq.ctypes.data, ck.ctypes.data, FAKE, FAKE, FAKE)
+    return b, keep
+
+
+def idx_call(lib, b, q=FAKE, k=FAKE, w=FAKE, H=64, D=128, s=FAKE, ld=None):
+    ld = b.max_kv_len if ld is None else ld
+    return lib.mla_indexer_score(ctypes.byref(b), q, k, w, H, D, s, ld, None)
+
+
+def topk_call(lib, b, s=FAKE, ld=None, k=8, out=FAKE):
+    ld = b.max_kv_len if ld is None else ld
+    return lib.mla_topk_select(ctypes.byref(b), s, ld, k, out, None)
+
+
+def attn_call(lib, b, q=FAKE, kv=FAKE, sc=FAKE, dtype=1, stride=576, sstride=4, idx=FAKE, k=8,
+              H=64, scale=0.07, out=FAKE, lse=FAKE):
+    return lib.mla_sparse_prefill(ctypes.byref(b), q, kv, sc, dtype, stride, sstride, idx, k, H,
+                                  scale, out, lse, None)
+
+
+INVALID, UNSUPPORTED = sm.MLA_ERR_INVALID_ARG, sm.MLA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu_q=(1, 4)), INVALID),                      # does not start at 0
+    (dict(cu_q=(0, 5, 4), cu_kv=(0, 5, 10)), INVALID),  # decreasing
+    (dict(total_q=3), INVALID),                        # totals mismatch
+    (dict(total_kv=11), INVALID),
+    (dict(max_kv=9), INVALID),                         # max_kv_len wrong
+    (dict(cu_q=(0, 2, 4), cu_kv=(0, 10, 10)), INVALID),  # queries without KV
+    (dict(num=0), INVALID),
+])
+def test_bad_batches_rejected_by_every_call(lib, kw, code):
+    b, keep = make_batch(**kw)
+    assert idx_call(lib, b) == code
+    assert lib.mla_last_error()
+    assert topk_call(lib, b) == code
+    assert attn_call(lib, b) == code
+
+
+def test_null_batch(lib):
+    assert lib.mla_indexer_score(None, FAKE, FAKE, FAKE, 64, 128, FAKE, 10, None) == INVALID
+    assert b"NULL" in lib.mla_last_error()
+
+
+def test_indexer_argument_checks(lib):
+    b, keep = make_batch()
+    assert idx_call(lib, b, H=0) == INVALID
+    assert idx_call(lib, b, H=65) == UNSUPPORTED
+    assert idx_call(lib, b, D=96) == UNSUPPORTED
+    assert idx_call(lib, b, ld=9) == INVALID
+    assert idx_call(lib, b, q=None) == INVALID
+    assert idx_call(lib, b, q=FAKE + 8) == INVALID            # misaligned bf16 rows
+    assert idx_call(lib, b, s=FAKE + 2) == INVALID
+
+
+def test_topk_argument_checks(lib):
+    b, keep = make_batch()
+    assert topk_call(lib, b, k=0) == INVALID
+    assert topk_call(lib, b, k=4097) == UNSUPPORTED
+    assert topk_call(lib, b, ld=5) == INVALID
+    assert topk_call(lib, b, out=None) == INVALID
+
+
+def test_attention_argument_checks(lib):
+    b, keep = make_batch()
+    assert attn_call(lib, b, dtype=7) == INVALID
+    assert attn_call(lib, b, stride=584) == INVALID           # not a multiple of 16
+    assert attn_call(lib, b, stride=560) == INVALID           # shorter than an fp8 row
+    assert attn_call(lib, b, dtype=0, stride=1136) == INVALID  # shorter than a bf16 row
+    assert attn_call(lib, b, sstride=2) == INVALID
+    assert attn_call(lib, b, sc=None) == INVALID              # fp8 needs scales
+    assert attn_call(lib, b, scale=0.0) == INVALID
+    assert attn_call(lib, b, scale=float("nan")) == INVALID
+    assert attn_call(lib, b, k=0) == INVALID
+    assert attn_call(lib, b, H=12) == UNSUPPORTED
+    assert attn_call(lib, b, k=70000) == UNSUPPORTED
+    assert attn_call(lib, b, q=FAKE + 4) == INVALID
+    assert attn_call(lib, b, lse=None) == INVALID
+
+
+def test_empty_batch_enqueues_nothing(lib):
+    """total_q == 0 returns OK without any HIP call (so it works with no GPU)."""
+    b, keep = make_batch(cu_q=(0, 0), cu_kv=(0, 10))
+    assert idx_call(lib, b, q=None, k=None, w=None, s=None) == sm.MLA_OK
+    assert topk_call(lib, b, s=None, out=None) == sm.MLA_OK
+    assert attn_call(lib, b, q=None, kv=None, sc=None, out=None, lse=None) == sm.MLA_OK
+    assert lib.mla_last_error() == b""
+
+
+def test_binding_refuses_wrong_dtypes_before_the_library():
+    import torch
+    b = sm.Batch.__new__(sm.Batch)
+    b.device = torch.device("cpu")
+    b.total_q, b.total_kv, b.max_kv_len = 4, 10, 10
+    with pytest.raises(TypeError):
+        sm.indexer_score(b, torch.zeros(4, 64, 128), torch.zeros(10, 128, dtype=torch.bfloat16),
+                         torch.zeros(4, 64))

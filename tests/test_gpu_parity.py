@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Staged so errors do not compound (the comparison procedure of the method):
+  * indexer scores vs the oracle's, |g - r| <= 1e-3 |r| + 1e-4 (fp32 sums of
+    exact bf16 products); bit-exact on small-integer inputs;
+  * top-k bit-exact: the oracle's selection run on the GPU's own score rows;
+  * attention on the GPU's own index lists, |g - r| <= atol + rtol |r| with
+    atol = rtol = 2e-2 for bf16 KV and 6e-2 for FP8 KV (out and LSE);
+  * the set overlap when each side uses its own scores is reported, not gated.
+The tiny workload is checked on every row; the full-size workloads run the
+whole path in the launch configuration the benchmark times and are checked
+on sampled rows.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp8": 6e-2}
+
+
+@pytest.fixture(scope="module")
+def sm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_mla_long_amd as sm
+    sm.load_library()
+    return sm
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def assert_close(name, got, ref, atol, rtol):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
+    err = np.abs(got - ref)
+    bad = ~(both_inf | (err <= atol + rtol * np.abs(ref)))
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d / %d outside tolerance (atol=%g rtol=%g); first at %s: "
+                             "got %r ref %r; max err %g" % (name, bad.sum(), bad.size, atol, rtol,
+                                                            tuple(i), got[tuple(i)],
+                                                            ref[tuple(i)], np.nanmax(err)))
+
+
+def to_gpu(inp):
+    out = dict(inp)
+    for k, v in inp.items():
+        if isinstance(v, torch.Tensor):
+            out[k] = v.cuda()
+    return out
+
+
+def check_path(sm, inp, rows, label, check_indexer=True):
+    """Run indexer -> top-k -> attention on the GPU for the whole batch and
+    check the given rows against the oracle, stage by stage."""
+    wl = inp["workload"]
+    batch = sm.Batch.from_inputs(inp)
+    say("[%s] GPU path: %d queries, %d KV rows, H=%d, k=%d, kv=%s" %
+        (label, wl.total_q, wl.total_kv, wl.n_heads, wl.topk, inp["kv_dtype"]))
+    scores = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
+    idx = sm.topk_select(batch, scores, wl.topk)
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale)
+    torch.cuda.synchronize()
+    q_pos = inp["q_pos_host"]
+    rows = np.asarray(rows)
+    rt = torch.as_tensor(rows, device="cuda")
+    g_scores = [scores[int(r), : q_pos[r] + 1].cpu().numpy() for r in rows]
+    g_idx = idx[rt].cpu().numpy()
+    if check_indexer:
+        say("[%s] oracle indexer on %d rows" % (label, len(rows)))
+        r_scores = oracle.indexer_rows(inp, rows)
+        for t, r in enumerate(rows):
+            assert_close("%s indexer row %d" % (label, r), g_scores[t], r_scores[t], 1e-4, 1e-3)
+    say("[%s] oracle top-k on the GPU's scores" % label)
+    r_idx = oracle.topk_rows(g_scores, q_pos[rows], wl.topk)
+    mism = np.nonzero((r_idx != g_idx).any(axis=1))[0]
+    assert len(mism) == 0, "%s top-k differs on rows %s" % (label, rows[mism][:8])
+    say("[%s] oracle attention on the GPU's index lists" % label)
+    r_out, r_lse = oracle.attention_rows(inp, rows, g_idx)
+    tol = TOL[inp["kv_dtype"]]
+    assert_close("%s out" % label, out[rt].float().cpu().numpy(), r_out, tol, tol)
+    assert_close("%s lse" % label, lse[rt].cpu().numpy(), r_lse, tol, tol)
+    return scores, idx, out, lse
+
+
+# ------------------------------------------------------------------ tiny --
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_tiny_all_rows(sm, kv_dtype):
+    wl = mla_inputs.WORKLOADS["tiny"]
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu", kv_dtype=kv_dtype))
+    scores, idx, out, lse = check_path(sm, inp, np.arange(wl.total_q), "tiny-" + kv_dtype)
+    # end-to-end overlap with the oracle's own selection (reported)
+    rows = np.arange(0, wl.total_q, 37)
+    ref_idx = oracle.topk_rows(oracle.indexer_rows(inp, rows), inp["q_pos_host"][rows], wl.topk)
+    g = idx[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+    ov = np.mean([len(set(a) & set(b)) / len(set(a)) for a, b in zip(ref_idx, g)])
+    say("tiny end-to-end top-k set overlap (own scores each side): %.4f" % ov)
+    assert ov > 0.99
+
+
+@pytest.mark.parametrize("n_heads", [8, 16, 32, 64])
+def test_dense_attention_small(sm, n_heads):
+    wl = mla_inputs.Workload("dense-small", (300, 77), (((0, 300),), ((0, 77),)), n_heads=n_heads,
+                             idx_heads=4, idx_dim=64, topk=512, kv_dtype="bf16", dense=True, seed=21)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu"))
+    batch = sm.Batch.from_inputs(inp)
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], None, None, wl.sm_scale)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.total_q)
+    r_out, r_lse = oracle.attention_rows(inp, rows, None)
+    assert_close("dense out", out.float().cpu().numpy(), r_out, 2e-2, 2e-2)
+    assert_close("dense lse", lse.cpu().numpy(), r_lse, 2e-2, 2e-2)
+
+
+def test_dense_equals_sparse_with_full_lists(sm):
+    """With every earlier token listed, the sparse path equals the dense one."""
+    wl = mla_inputs.Workload("full", (200,), (((0, 200),),), n_heads=64, idx_heads=4, idx_dim=64,
+                             topk=256, kv_dtype="fp8", seed=22)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu"))
+    batch = sm.Batch.from_inputs(inp)
+    full = torch.arange(256, device="cuda", dtype=torch.int32)[None].repeat(200, 1)
+    full = torch.where(full <= inp["q_pos"][:, None], full, torch.full_like(full, -1))
+    o1, l1 = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], full, wl.sm_scale)
+    o2, l2 = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], None, wl.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# --------------------------------------------------------------- indexer --
+@pytest.mark.parametrize("H,D", [(64, 128), (4, 64), (33, 128)])
+def test_indexer_small_integers_bit_exact(sm, H, D):
+    """Small-integer inputs make every product and partial sum an exact fp32
+    integer, so any summation order gives the oracle's value exactly."""
+    g = torch.Generator().manual_seed(H + D)
+    L, nq = 333, 333
+    q = torch.randint(-8, 9, (nq, H, D), generator=g).to(torch.bfloat16)
+    k = torch.randint(-8, 9, (L, D), generator=g).to(torch.bfloat16)
+    w = torch.randint(0, 5, (nq, H), generator=g).float()
+    inp = {"q_idx": q, "k_idx": k, "w": w, "cu_seqlens_q_host": np.array([0, nq], np.int32),
+           "cu_seqlens_kv_host": np.array([0, L], np.int32),
+           "q_pos_host": np.arange(nq, dtype=np.int32)}
+    batch = sm.Batch([0, nq], [0, L], np.arange(nq), "cuda")
+    sc = sm.indexer_score(batch, q.cuda(), k.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    ref = oracle.indexer_rows(inp, np.arange(nq))
+    for i in range(nq):
+        assert np.array_equal(sc[i, : i + 1].cpu().numpy(), ref[i]), i
+
+
+# ----------------------------------------------------------------- top-k --
+@pytest.mark.parametrize("kind", ["all_equal", "relu_zeros", "small_int", "signed_zero", "normal"])
+def test_topk_ties_bit_exact(sm, kind):
+    g = torch.Generator().manual_seed(3)
+    n, L, k = 24, 70000, 2048
+    pos = torch.tensor([0, 1, 2046, 2047, 2048, 2049, 5000, 32767, 32768, 32769, 40000, 69999] +
+                       torch.randint(0, L, (12,), generator=g).tolist(), dtype=torch.int32)
+    if kind == "all_equal":
+        s = torch.full((n, L), 7.5)
+    elif kind == "relu_zeros":
+        s = torch.relu(torch.randn(n, L, generator=g))
+    elif kind == "small_int":
+        s = torch.randint(0, 6, (n, L), generator=g).float()
+    elif kind == "signed_zero":
+        s = torch.where(torch.rand(n, L, generator=g) < 0.5, -0.0, 0.0)
+        s[:, ::97] = 1.0
+    else:
+        s = torch.randn(n, L, generator=g) * 100
+    batch = sm.Batch([0, n], [0, L], pos, "cuda")
+    idx = sm.topk_select(batch, s.cuda(), k)
+    torch.cuda.synchronize()
+    ref = oracle.topk_seq(s.numpy(), pos.numpy(), k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------ ragged and layout --
+def test_ragged_small_batch_all_rows(sm):
+    """Empty sequence, gaps in the positions (a CP-style share), rows shorter
+    than k, a one-token sequence and a ragged tail."""
+    wl = mla_inputs.Workload("ragged-small", (300, 0, 1000, 1, 130),
+                             (((0, 300),), (), ((0, 70), (930, 1000)), ((0, 1),), ((64, 130),)),
+                             n_heads=64, idx_heads=64, idx_dim=128, topk=96, kv_dtype="fp8", seed=23)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu"))
+    check_path(sm, inp, np.arange(wl.total_q), "ragged-small")
+
+
+def test_inline_scale_row_layout(sm):
+    """sigma stored inline at the tail of a 640-byte row (byte strides) gives
+    the same result as separate arrays."""
+    wl = mla_inputs.Workload("inline", (500,), (((0, 500),),), n_heads=64, idx_heads=4,
+                             idx_dim=64, topk=128, kv_dtype="fp8", seed=24)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu"))
+    batch = sm.Batch.from_inputs(inp)
+    sc = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
+    idx = sm.topk_select(batch, sc, wl.topk)
+    o1, l1 = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale)
+    packed = torch.zeros((wl.total_kv, 640), dtype=torch.uint8, device="cuda")
+    packed[:, :576] = inp["kv"]
+    packed[:, 576:580] = inp["kv_scale"].view(torch.uint8).view(-1, 4)
+    o2, l2 = sm.sparse_prefill(batch, inp["q"], packed, packed[:, 576:].view(torch.float32)[:, 0],
+                               idx, wl.sm_scale, kv_row_stride=640, kv_scale_stride=640)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------- full-size workloads --
+FULL = [("sparse32k", "fp8"), ("sparse32k", "bf16"), ("dense16k", "bf16"), ("cp131k", "fp8"),
+        ("ragged", "fp8")]
+
+
+@pytest.mark.parametrize("name,kv_dtype", FULL)
+def test_full_size_sampled_rows(sm, name, kv_dtype):
+    wl = mla_inputs.WORKLOADS[name]
+    n_rows = int(os.environ.get("MLA_PARITY_ROWS", "48"))
+    rows = mla_inputs.sample_rows(wl, n_rows)
+    say("[%s/%s] generating inputs on the GPU" % (name, kv_dtype))
+    inp = mla_inputs.make_inputs(wl, "cuda", kv_dtype=kv_dtype)
+    if wl.dense:
+        batch = sm.Batch.from_inputs(inp)
+        out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], None, None, wl.sm_scale)
+        torch.cuda.synchronize()
+        say("[%s] oracle dense attention on %d rows" % (name, len(rows)))
+        r_out, r_lse = oracle.attention_rows(inp, rows, None)
+        rt = torch.as_tensor(rows, device="cuda")
+        assert_close("dense16k out", out[rt].float().cpu().numpy(), r_out, 2e-2, 2e-2)
+        assert_close("dense16k lse", lse[rt].cpu().numpy(), r_lse, 2e-2, 2e-2)
+    else:
+        check_path(sm, inp, rows, "%s-%s" % (name, kv_dtype))
+    del inp
+    torch.cuda.empty_cache()
