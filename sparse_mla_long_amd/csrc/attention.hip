@@ -3,24 +3,38 @@
 // Every token has one latent row of 576 values (512 latent + 64 rope) shared
 // by all heads; a query's heads attend with QK over all 576 dims and PV over
 // the first 512 (spke.com GLM-5.3 PCP/DCP article, footnote 1). One gathered
-// row therefore serves every head (section "PCP"), which is what this kernel
-// is built around: each 64-key block of rows is gathered into LDS once and
-// used by all 64 heads for both products.
+// row therefore serves every head (section "PCP"): the kernel lands each
+// block of 32 gathered rows in LDS once and runs QK and PV of all 64 heads on
+// it.
 //
-// One query per 256-thread workgroup (4 waves):
-//  * QK: S^T[key x head] = K[key x 576] . Q^T[576 x head]. Wave w takes keys
-//    32*(w&1).. of the block and heads 32*(w>>1)..; its Q^T fragments (36
-//    k-steps) stay in registers for the whole query. In the 32x32 accumulator
-//    a lane owns one head and 16 keys, so the online-softmax state (running
-//    max m and sum l, base 2) is per lane; the two key halves exchange their
-//    block maxima through LDS.
-//  * P (bf16, with the FP8 row scale folded in) goes to LDS as [head][key].
-//  * PV: O[head x dim] += P[head x key] . V[key x dim]; wave w owns output
-//    dims 128*w.. for all 64 heads (128 fp32 accumulators per lane), read
-//    with V taken column-wise from the same LDS rows.
-//  * FP8 rows are decoded exactly to bf16 while being staged (E4M3 values are
-//    bf16-representable); the per-token scale sigma_j multiplies the logit
-//    and the probability instead of the row, so no rounding is added.
+// Work split: one query per 128-thread workgroup, two waves; wave w owns heads
+// 32w..32w+31 for everything (QK over all keys of a block, the online softmax
+// of its heads and PV into all 512 output dims), so the two waves share only
+// the gathered rows. Two workgroups fit on a CU, one wave per SIMD.
+//
+//  * Gather: rows move HBM -> LDS with global_load_lds_dwordx4 (each lane's
+//    16 bytes land at LDS base + 16*lane), through a ring of 3 (FP8) or 2
+//    (bf16) blocks, issued two blocks (one) ahead. No registers hold rows in
+//    flight; the only wait is `vmcnt` for this wave's older blocks plus one
+//    barrier per block. Key indices and FP8 scales are copied to LDS before
+//    the loop so no ordinary global load interleaves with the ring.
+//  * Rows keep their storage type in LDS (E4M3 codes or bf16), 16-byte chunks
+//    XOR-swizzled per row so both read patterns below are bank-conflict-free.
+//  * QK: S^T[key x head] = K[key x 576] . Q^T[576 x head] on 32x32x16 bf16
+//    MFMA; the wave's Q^T fragments stay in registers for the whole query.
+//    FP8 K is decoded to bf16 on the fly (exact: E4M3 values are bf16
+//    representable). Accumulator row m reads LDS row 16*((m>>2)&1) +
+//    4*(m>>3) + (m&3), so lane half g of the 32x32 accumulator holds LDS rows
+//    16g..16g+15 of the block, in order.
+//  * PV: O[head x dim] += P[head x key] . V[key x dim]: the accumulator above
+//    already is P in the A-operand layout (k-step t = LDS rows 16g+8t..+7), so
+//    P never leaves registers. V is read key-major from the same LDS rows with
+//    the gfx950 transpose reads: ds_read_b64_tr_b8 for E4M3 (a lane receives 8
+//    rows of one column) and ds_read_b64_tr_b16 for bf16 (4 rows).
+//  * Online softmax in base 2 with lazy rescaling: the running max used for
+//    the exponentials only moves when a block exceeds it by more than 2^8, so
+//    the 256 fp32 accumulators per lane are almost never rescaled.
+//  * FP8 scales sigma_j multiply the logit and the probability, not the row.
 // Entries of the index list outside 0..p_i are masked (probability 0).
 #include "common.h"
 #include "kernels.h"
@@ -28,30 +42,91 @@
 namespace mla {
 namespace {
 
-constexpr int kAttnThreads = 256;
-constexpr int kBlk = 64;                 // keys per block
+constexpr int kThreads = 256;              // 4 waves: (head group, dim half)
+constexpr int kBlk = 32;                    // keys per block
 constexpr int kQK = 576, kV = 512;
-constexpr int KV_LD = kQK + 8;           // LDS row pitch in bf16 (+16 B against bank aliasing)
-constexpr int P_LD = kBlk + 8;
+constexpr int kQKHalf = kQK / 2, kVHalf = kV / 2;
+constexpr float kLazyRescale = 8.0f;        // log2 headroom before the running max moves
+constexpr int O_LD = kVHalf + 8;            // epilogue staging pitch (bf16)
 
-__device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(uint32_t w, bool hi) {
-    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
-              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 *lds_bf16x4_ptr;
+typedef __attribute__((address_space(3))) v2i32 *lds_v2i32_ptr;
+
+template <bool FP8> struct Cfg;
+template <> struct Cfg<true> {              // E4M3 rows: 576 B = 36 chunks of 16 dims
+    static constexpr int kRowBytes = 576, kChunks = 36, kRing = 5, kIdx = 2048;
+};
+template <> struct Cfg<false> {             // bf16 rows: 1152 B = 72 chunks of 8 dims
+    static constexpr int kRowBytes = 1152, kChunks = 72, kRing = 3, kIdx = 1024;
+};
+constexpr int kXchgBytes = 2 * 4 * 64 * 16 * 4;   // [parity][wave][4 x 64 lanes x f32x4]
+
+// Chunk swizzle of LDS row r (XOR on the low chunk bits); rows 0..31 of a block.
+template <bool FP8> __device__ __forceinline__ int swz(int r) {
+    if (FP8) return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+    return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Wait until at most n*D of this wave's vector-memory operations are in flight
+// (D = the fewest DMA instructions any wave issues per block; waves issuing
+// more wait slightly longer, which is safe).
+template <int D> __device__ __forceinline__ void wait_vm_blocks(int n) {
+    switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * D) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory"); break;
+    }
+}
+
+typedef __attribute__((address_space(3))) void *lds_void_ptr;
+
+// 16 bytes per lane, global -> LDS at (wave-uniform) dst + 16 * lane; completion
+// is tracked with explicit vmcnt waits.
+__device__ __forceinline__ void dma16(const void *src, uint8_t *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x8 &d, int at) {
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    d[at] = lo[0];
+    d[at + 1] = lo[1];
+    d[at + 2] = hi[0];
+    d[at + 3] = hi[1];
+}
+
+template <bool FP8> constexpr size_t lds_bytes() {          // dynamic part: ring + exchange
+    using C = Cfg<FP8>;
+    return (size_t)C::kRing * kBlk * C::kRowBytes + kXchgBytes;
+}
+template <bool FP8> constexpr size_t lds_static_bytes() {   // entry table
+    using C = Cfg<FP8>;
+    return (size_t)C::kIdx * 4 + (FP8 ? C::kIdx : 4) * 4;
 }
 
 template <bool FP8>
-__global__ __attribute__((amdgpu_flat_work_group_size(kAttnThreads, kAttnThreads),
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void attn_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 s_kv[kBlk * KV_LD];
-    __shared__ __attribute__((aligned(16))) __bf16 s_p[64 * P_LD];
-    __shared__ float s_sig[kBlk];        // sigma_j of each staged key (1 for bf16 rows)
-    __shared__ int s_valid[kBlk];
-    __shared__ float s_red[2][2][32];    // [head block][key half][head]
-    __shared__ __attribute__((aligned(16))) float s_alpha[64];
-    __shared__ __attribute__((aligned(16))) float s_lfin[64];
+    using C = Cfg<FP8>;
+    constexpr int kBlockBytes = kBlk * C::kRowBytes;
+    constexpr int kDma = kBlockBytes / 1024;                    // 16 B x 64 lanes per DMA
+    static_assert(kDma * 1024 == kBlockBytes && kDma >= 16, "DMA split");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t *ring = smem;                                            // kRing blocks
+    f32x4 *xchg = (f32x4 *)(smem + C::kRing * kBlockBytes);          // partial S^T exchange
+    // entry table in its own LDS object, so LDS reads of it are not ordered
+    // behind the in-flight ring DMA
+    __shared__ __attribute__((aligned(16))) int32_t s_row[C::kIdx];           // row, or -1
+    __shared__ __attribute__((aligned(16))) float s_mul[FP8 ? C::kIdx : 4];   // sigma_j*scale*log2e
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
-    const int hb = wv >> 1, kb = wv & 1;
+    const int hg = wv >> 1, dh = wv & 1;                             // head group, dim half
+    const int tid = threadIdx.x;
     const int qi = a.batch.total_q - 1 - (int)blockIdx.x;
     const int b = seq_of_row(a.batch.cu_q, a.batch.num_seqs, qi);
     const int64_t kv0 = a.batch.cu_kv[b];
@@ -60,196 +135,276 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kAttnThreads, kAttnThreads
     const int H = a.n_heads;
     const bool dense = a.indices == nullptr;
     const int n_keys = dense ? pos + 1 : a.k;
-    const int n_blk = n_keys > 0 ? (n_keys + kBlk - 1) / kBlk : 0;
     const int32_t *idx_row = dense ? nullptr : a.indices + (int64_t)qi * a.k;
+    const uint8_t *kvq = a.kv + kv0 * a.kv_stride;                   // row 0 of this sequence
+    const bool table = FP8 || !dense;        // bf16 dense rows need no per-entry table
+    const int chunk_len = table ? C::kIdx : n_keys;
 
-    // Q^T fragments of heads 32*hb + col (B operand), all 36 k-steps
-    bf16x8 qf[kQK / 16];
+    // Q^T fragments (B operand) of head 32*hg + col over this wave's 288 dims.
+    // k-step 2t+u uses dims 288*dh + 16*(2t+g) + 8u .. +7.
+    const int head = 32 * hg + col;
+    bf16x8 qf[kQKHalf / 16];
     {
-        const int h = 32 * hb + col;
-        const bool hv = h < H;
-        const __bf16 *qrow = a.q + ((int64_t)qi * H + (hv ? h : 0)) * kQK + 8 * g;
+        const bool hv = head < H;
+        const __bf16 *qrow = a.q + ((int64_t)qi * H + (hv ? head : 0)) * kQK + kQKHalf * dh;
 #pragma unroll
-        for (int ks = 0; ks < kQK / 16; ++ks)
-            qf[ks] = hv ? *(const bf16x8 *)(qrow + 16 * ks) : zero_bf16x8();
+        for (int t = 0; t < kQKHalf / 32; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bf16x8 v = *(const bf16x8 *)(qrow + 16 * (2 * t + g) + 8 * u);
+                qf[2 * t + u] = hv ? v : zero_bf16x8();
+            }
+        // settle the fragment loads here, so no wait on them lands inside the
+        // block loop (where it would also drain the KV ring)
+#pragma unroll
+        for (int t = 0; t < kQKHalf / 16; ++t) asm volatile("" ::"v"(qf[t]));
     }
 
-    // gather: thread t stages key row t/4, 16-byte chunks (t%4) + 4s
-    const int gr = threadIdx.x >> 2, gq = threadIdx.x & 3;
-    constexpr int NCH = FP8 ? (kQK / 16 / 4) : (kQK * 2 / 16 / 4);   // 9 or 18
-    u32x4 st[NCH];
-    float st_sig = 0.f;
-    bool st_valid = false;
-    auto gather = [&](int blk) {
-        const int e = blk * kBlk + gr;
-        int j = -1;
-        if (e < n_keys) j = dense ? e : idx_row[e];
-        st_valid = j >= 0 && j <= pos;
-        const uint8_t *rowp = a.kv + (kv0 + (st_valid ? j : 0)) * a.kv_stride;
+    float m_run = -INFINITY, l_run = 0.f;       // head `col`, this lane's keys
+    f32x16 o[kVHalf / 32];
 #pragma unroll
-        for (int s = 0; s < NCH; ++s)
-            st[s] = st_valid ? *(const u32x4 *)(rowp + 16 * (gq + 4 * s)) : u32x4{0u, 0u, 0u, 0u};
-        if (FP8)
-            st_sig = st_valid ? *(const float *)(a.kv_scale + (kv0 + j) * a.scale_stride) : 0.f;
-        else
-            st_sig = 1.f;
-    };
-    auto stage = [&]() {
-        __bf16 *dst = s_kv + gr * KV_LD;
-#pragma unroll
-        for (int s = 0; s < NCH; ++s) {
-            const int c = gq + 4 * s;
-            if (!FP8) {
-                *(u32x4 *)(dst + 8 * c) = st[s];
-            } else {
-                bf16x8 lo, hi;
-                const u32x4 v = st[s];
-                bf16x2 t;
-                t = fp8x2_to_bf16x2(v[0], false); lo[0] = t[0]; lo[1] = t[1];
-                t = fp8x2_to_bf16x2(v[0], true);  lo[2] = t[0]; lo[3] = t[1];
-                t = fp8x2_to_bf16x2(v[1], false); lo[4] = t[0]; lo[5] = t[1];
-                t = fp8x2_to_bf16x2(v[1], true);  lo[6] = t[0]; lo[7] = t[1];
-                t = fp8x2_to_bf16x2(v[2], false); hi[0] = t[0]; hi[1] = t[1];
-                t = fp8x2_to_bf16x2(v[2], true);  hi[2] = t[0]; hi[3] = t[1];
-                t = fp8x2_to_bf16x2(v[3], false); hi[4] = t[0]; hi[5] = t[1];
-                t = fp8x2_to_bf16x2(v[3], true);  hi[6] = t[0]; hi[7] = t[1];
-                *(bf16x8 *)(dst + 16 * c) = lo;
-                *(bf16x8 *)(dst + 16 * c + 8) = hi;
+    for (int nb = 0; nb < kVHalf / 32; ++nb) o[nb] = zero16();
+    const float inv_c = 1.0f / a.scale_log2;
+    // row this lane feeds into the QK A operand: accumulator row m = col
+    const int qk_row = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
+    const int qk_swz = swz<FP8>(qk_row);
+    int parity = 0;
+
+    for (int c0 = 0; c0 < n_keys; c0 += chunk_len) {
+        const int cn = min(chunk_len, n_keys - c0);               // entries in this chunk
+        const int n_blk = (cn + kBlk - 1) / kBlk;
+        if (table) {
+            // entry table of the chunk: row (or -1 when masked) and FP8 multiplier
+            for (int e = tid; e < n_blk * kBlk; e += kThreads) {
+                const int ge = c0 + e;
+                int j = -1;
+                if (e < cn) j = dense ? ge : idx_row[ge];
+                const bool v = j >= 0 && j <= pos;
+                s_row[e] = v ? j : -1;
+                if (FP8)
+                    s_mul[e] = v ? *(const float *)(a.kv_scale + (kv0 + j) * a.scale_stride) * a.scale_log2
+                                 : 0.f;
             }
+            __syncthreads();
         }
-        if (gq == 0) {
-            s_sig[gr] = st_sig;
-            s_valid[gr] = st_valid ? 1 : 0;
-        }
-    };
-
-    float m_run = -INFINITY, l_run = 0.f;   // per lane: head 32*hb + col, this lane's keys
-    f32x16 o[2][4];
+        auto row_of = [&](int e) -> int {                       // e: entry within the chunk
+            if (table) return s_row[e];
+            return e < cn ? c0 + e : -1;
+        };
+        // DMA one block into ring slot `slot`: this wave issues instructions wv, wv+4, ...
+        auto issue = [&](int blk, int slot) {
+            uint8_t *dst = ring + slot * kBlockBytes;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) o[mb][nb] = zero16();
-
-    if (n_blk > 0) gather(0);
-    for (int blk = 0; blk < n_blk; ++blk) {
-        __syncthreads();                    // previous block's PV is done with s_kv / s_p
-        stage();
-        __syncthreads();
-        if (blk + 1 < n_blk) gather(blk + 1);
-
-        // ---- S^T = K Q^T for keys 32*kb.., heads 32*hb..
-        f32x16 s = zero16();
-        const __bf16 *krow = s_kv + (32 * kb + col) * KV_LD + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < kQK / 16; ++ks) s = mfma32x32x16(*(const bf16x8 *)(krow + 16 * ks), qf[ks], s);
-
-        float t[16];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-            t[e] = s_valid[r] ? s[e] * (a.scale_log2 * s_sig[r]) : -INFINITY;
-            mx = fmaxf(mx, t[e]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (g == 0) s_red[hb][kb][col] = mx;
-        __syncthreads();
-        const float m_new = fmaxf(m_run, fmaxf(mx, s_red[hb][kb ^ 1][col]));
-        const float msub = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bf16x4 pk;
-            const int r0 = 32 * kb + 8 * i + 4 * g;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float p = __builtin_amdgcn_exp2f(t[4 * i + j] - msub);
-                psum += p;
-                pk[j] = (__bf16)(FP8 ? p * s_sig[r0 + j] : p);
-            }
-            *(bf16x4 *)(s_p + (32 * hb + col) * P_LD + r0) = pk;
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (kb == 0 && g == 0) s_alpha[32 * hb + col] = alpha;
-        __syncthreads();
-
-        // ---- O[head x dim 128*wv..] = O * alpha + P V
-        float al[2][16];
-        bool rescale = false;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 v = *(const f32x4 *)(s_alpha + 32 * mb + 8 * i + 4 * g);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    al[mb][4 * i + j] = v[j];
-                    rescale |= v[j] != 1.f;
+            for (int u = 0; u < (kDma + 3) / 4; ++u) {
+                const int ins = wv + 4 * u;
+                if (ins < kDma) {
+                    const int sidx = ins * 64 + lane;             // 16-byte slot in the block
+                    const int r = sidx / C::kChunks, pc = sidx % C::kChunks;
+                    const int lc = pc ^ swz<FP8>(r);              // logical chunk stored at pc
+                    const int j = row_of(blk * kBlk + r);
+                    const uint8_t *src = kvq + (int64_t)(j >= 0 ? j : 0) * a.kv_stride + 16 * lc;
+                    dma16(src, dst + ins * 1024);
                 }
             }
-        if (__any(rescale)) {
+        };
+
+        for (int p = 0; p < C::kRing - 1 && p < n_blk; ++p) issue(p, p);
+        for (int blk = 0; blk < n_blk; ++blk) {
+            const int slot = blk % C::kRing;
+            wait_vm_blocks<kDma / 4>(min(C::kRing - 2, n_blk - 1 - blk));
+            lds_barrier();                               // block blk landed; slot of blk-1 free
+            if (blk + C::kRing - 1 < n_blk) issue(blk + C::kRing - 1, (blk + C::kRing - 1) % C::kRing);
+            const uint8_t *kb = ring + slot * kBlockBytes;
+
+            // ---- partial S^T = K Q^T over this wave's 288 dims
+            f32x16 s = zero16();
+            {
+                const uint8_t *krow = kb + qk_row * C::kRowBytes;
+                if (FP8) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+                    for (int t = 0; t < kQKHalf / 32; ++t) {
+                        if (t % 3 == 0) __builtin_amdgcn_sched_barrier(0);
+                        const int lc = 18 * dh + 2 * t + g;
+                        const u32x4 raw = *(const u32x4 *)(krow + 16 * (lc ^ qk_swz));
+                        bf16x8 k0, k1;
+                        fp8x4_to_bf16(raw[0], k0, 0);
+                        fp8x4_to_bf16(raw[1], k0, 4);
+                        fp8x4_to_bf16(raw[2], k1, 0);
+                        fp8x4_to_bf16(raw[3], k1, 4);
+                        s = mfma32x32x16(k0, qf[2 * t], s);
+                        s = mfma32x32x16(k1, qf[2 * t + 1], s);
+                    }
+                } else {
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
+                    for (int t = 0; t < kQKHalf / 32; ++t) {
+                        if (t % 3 == 0) __builtin_amdgcn_sched_barrier(0);
+                        const int lc = 36 * dh + 2 * (2 * t + g);
+                        const bf16x8 k0 = *(const bf16x8 *)(krow + 16 * (lc ^ qk_swz));
+                        const bf16x8 k1 = *(const bf16x8 *)(krow + 16 * ((lc + 1) ^ qk_swz));
+                        s = mfma32x32x16(k0, qf[2 * t], s);
+                        s = mfma32x32x16(k1, qf[2 * t + 1], s);
+                    }
+                }
+            }
+            // ---- exchange partial sums with the other dim half of this head group
+            {
+                f32x4 *mine = xchg + ((parity * 4 + wv) * 4) * 64;
+                const f32x4 *other = xchg + ((parity * 4 + (wv ^ 1)) * 4) * 64;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) o[mb][nb][e] *= al[mb][e];
-        }
+                for (int q4 = 0; q4 < 4; ++q4)
+                    mine[q4 * 64 + lane] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+                lds_barrier();
 #pragma unroll
-        for (int ks = 0; ks < kBlk / 16; ++ks) {
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 v = other[q4 * 64 + lane];
+                    // same sum order in both waves (dim half 0 first) -> identical S
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        s[4 * q4 + j] = dh == 0 ? s[4 * q4 + j] + v[j] : v[j] + s[4 * q4 + j];
+                }
+                parity ^= 1;
+            }
+
+            // ---- online softmax (base 2) for head `col`; element e <-> LDS row 16g + e
+            const int e0 = blk * kBlk + 16 * g;
+            float mx = -INFINITY;
+            int rw[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float mu[4];
+                if (table) {
+                    *(int4 *)&rw[4 * q4] = *(const int4 *)&s_row[e0 + 4 * q4];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) rw[4 * q4 + j] = row_of(e0 + 4 * q4 + j);
+                }
+                if (FP8) {
+                    *(f32x4 *)mu = *(const f32x4 *)&s_mul[e0 + 4 * q4];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) mu[j] = a.scale_log2;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int e = 4 * q4 + j;
+                    s[e] = rw[e] >= 0 ? s[e] * mu[j] : -INFINITY;
+                    mx = fmaxf(mx, s[e]);
+                    if (FP8) rw[e] = __float_as_int(rw[e] >= 0 ? mu[j] * inv_c : 0.f);  // reuse: sigma_j
+                }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const bool grow = mx > m_run + kLazyRescale;
+            if (__any(grow)) {                                   // rare: move the running max
+                const float m_new = grow ? mx : m_run;
+                const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+                m_run = m_new;
+                // O rows are heads 8i + 4g + j; their alphas live in lanes 0..31
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float ar = __shfl(alpha, 8 * i + 4 * g + j);
+#pragma unroll
+                        for (int nb = 0; nb < kVHalf / 32; ++nb) o[nb][4 * i + j] *= ar;
+                    }
+            }
+            const float msub = m_run == -INFINITY ? 0.f : m_run;
             bf16x8 pa[2];
+            float psum = 0.f;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                pa[mb] = *(const bf16x8 *)(s_p + (32 * mb + col) * P_LD + 16 * ks + 8 * g);
+            for (int e = 0; e < 16; ++e) {
+                const float p = __builtin_amdgcn_exp2f(s[e] - msub);
+                psum += p;
+                pa[e >> 3][e & 7] = (__bf16)(FP8 ? p * __int_as_float(rw[e]) : p);
+            }
+            l_run += psum;
+
+            // ---- O[:, 256*dh ..] += P V; k-step t = LDS rows 16g + 8t .. +7
+            {
+                const int gi = lane & 15, hh = (lane >> 4) & 1;
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                const __bf16 *vp = s_kv + (16 * ks + 8 * g) * KV_LD + 128 * wv + 32 * nb + col;
-                bf16x8 vb;
+                for (int nb = 0; nb < kVHalf / 32; ++nb) {
+                    if (nb % 2 == 0) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vb[e] = vp[e * KV_LD];
+                    for (int t = 0; t < 2; ++t) {
+                        const int R0 = 16 * g + 8 * t;
+                        bf16x8 vb;
+                        if (FP8) {
+                            const int r = R0 + (gi >> 1);
+                            const int lc = 16 * dh + 2 * nb + hh;
+                            const uint8_t *src = kb + r * C::kRowBytes + 16 * (lc ^ swz<FP8>(r)) + 8 * (gi & 1);
+                            const v2i32 w8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_ptr)src);
+                            fp8x4_to_bf16((uint32_t)w8[0], vb, 0);
+                            fp8x4_to_bf16((uint32_t)w8[1], vb, 4);
+                        } else {
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) o[mb][nb] = mfma32x32x16(pa[mb], vb, o[mb][nb]);
+                            for (int v = 0; v < 2; ++v) {
+                                const int r = R0 + 4 * v + (gi >> 2);
+                                const int lc = 32 * dh + 4 * nb + 2 * hh + ((gi & 3) >> 1);
+                                const uint8_t *src = kb + r * C::kRowBytes + 16 * (lc ^ swz<FP8>(r)) + 8 * (gi & 1);
+                                const bf16x4 w16 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)src);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) vb[4 * v + e] = w16[e];
+                            }
+                        }
+                        o[nb] = mfma32x32x16(pa[t], vb, o[nb]);
+                    }
+                }
             }
         }
+        lds_barrier();        // every wave is done with the ring and the entry table
     }
 
-    // ---- epilogue: l over both lane halves and both key-half waves; LSE; O / l
-    const float lh = l_run + __shfl_xor(l_run, 32);
-    if (g == 0) s_red[hb][kb][col] = lh;
-    __syncthreads();
-    if (kb == 0 && g == 0) {
-        const int h = 32 * hb + col;
-        const float lt = s_red[hb][0][col] + s_red[hb][1][col];
-        s_lfin[h] = lt;
-        if (h < H) a.lse[(int64_t)qi * H + h] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
-    }
-    __syncthreads();
+    // ---- epilogue: l over both lane halves; LSE; O / l staged through LDS as bf16
+    const float lt = l_run + __shfl_xor(l_run, 32);
+    if (dh == 0 && g == 0 && head < H)
+        a.lse[(int64_t)qi * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    __bf16 *stage = (__bf16 *)smem + wv * 32 * O_LD;          // 32 heads x 256 bf16 per wave
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int h = 32 * mb + 8 * (e >> 2) + 4 * g + (e & 3);
-            if (h < H) {
-                const float lt = s_lfin[h];
-                const float inv = lt > 0.f ? 1.f / lt : 0.f;
-                __bf16 *orow = a.out + ((int64_t)qi * H + h) * kV + 128 * wv + col;
+        for (int j = 0; j < 4; ++j) {
+            const int hr = 8 * i + 4 * g + j;
+            const float ir = __shfl(inv, hr);
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) orow[32 * nb] = (__bf16)(o[mb][nb][e] * inv);
-            }
+            for (int nb = 0; nb < kVHalf / 32; ++nb)
+                stage[hr * O_LD + 32 * nb + col] = (__bf16)(o[nb][4 * i + j] * ir);
         }
+    lds_barrier();
+    // 32 rows x 512 B per wave: two rows per pass, 16 B per lane
+#pragma unroll
+    for (int pr = 0; pr < 16; ++pr) {
+        const int hr = 2 * pr + (lane >> 5);
+        const int h = 32 * hg + hr;
+        if (h < H) {
+            const u32x4 v = *(const u32x4 *)(stage + hr * O_LD + 8 * col);
+            *(u32x4 *)(a.out + ((int64_t)qi * H + h) * kV + kVHalf * dh + 8 * col) = v;
+        }
+    }
+}
+
+static_assert(lds_bytes<true>() >= 4 * 32 * O_LD * 2 && lds_bytes<false>() >= 4 * 32 * O_LD * 2,
+              "epilogue staging must fit");
+static_assert(lds_bytes<true>() + lds_static_bytes<true>() <= 160 * 1024 &&
+                  lds_bytes<false>() + lds_static_bytes<false>() <= 160 * 1024,
+              "LDS budget");
+
+template <bool FP8> hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
+    const size_t lds = lds_bytes<FP8>();
+    hipError_t e = hipFuncSetAttribute((const void *)attn_kernel<FP8>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_kernel<FP8>, dim3(a.batch.total_q), dim3(kThreads), lds, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, bool fp8, hipStream_t s) {
     if (a.batch.total_q <= 0) return hipSuccess;
-    if (fp8)
-        hipLaunchKernelGGL(attn_kernel<true>, dim3(a.batch.total_q), dim3(kAttnThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(attn_kernel<false>, dim3(a.batch.total_q), dim3(kAttnThreads), 0, s, a);
-    return hipGetLastError();
+    return fp8 ? launch_t<true>(a, s) : launch_t<false>(a, s);
 }
 
 }  // namespace mla
