@@ -3,21 +3,31 @@
 // nicht TP oder DP?": the indexer picks the 2,048 tokens sparse MLA attends
 // to). Ties go to the smaller key index; the kept indices come out ascending.
 //
-// One workgroup per query row. Scores become order-preserving 32-bit keys
-// (-0 folded onto +0); an exact radix select over four 8-bit digits finds the
-// key T of the k-th largest score and how many keys equal to T are needed;
-// a final ordered pass emits every key > T and the first needed keys == T
-// with a block-wide ballot scan. Rows that fit are staged once in LDS; longer
-// rows are re-read from global memory on each pass.
+// One 512-thread workgroup per query row. Scores become order-preserving
+// 32-bit keys (-0 folded onto +0). The row is read once for its key range
+// [kmin, kmax] (and staged in LDS when it fits); the k-th largest key T is
+// then found by an MSD radix select on v = key - kmin whose first 11-bit
+// digit spans the row's actual range, so it already splits typical score
+// distributions finely. A classify pass marks every key whose first digit is
+// above T's in a bitmap and collects the keys of T's bin (usually a few
+// dozen) into an LDS candidate list; the remaining digits are resolved on
+// that list alone. Candidates above T join the bitmap, candidates equal to T
+// go to a tie bitmap, and the output is the selected bits in index order --
+// the first (k - #above) ties by index -- written with two block scans.
+// Long rows cost three global reads; rows in LDS read global memory once.
 #include "common.h"
 #include "kernels.h"
 
 namespace mla {
 namespace {
 
-constexpr int kTopkThreads = 512;
-constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kLdsCapKeys = 32768;           // 128 KiB of keys
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kBins = 2048;                  // 11-bit digits
+constexpr int kDigit = 11;
+constexpr int kBatch = 8;                    // keys per thread per pass iteration
+constexpr int kVecBatch = 16;                // 16-byte loads per thread in the first pass
+constexpr size_t kLdsBudget = 160 * 1024 - 12 * 1024;   // minus static LDS and slack
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -25,8 +35,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Lanes with pred add one to hist[d]; the leader's digit is added in one
-// atomic (scores of a row often share their top bits).
+// Lanes with pred add one to hist[d]; the first active lane's digit is added in
+// one atomic (neighbouring scores often share a digit).
 __device__ __forceinline__ void hist_add(uint32_t *hist, bool pred, uint32_t d) {
     const uint64_t act = __ballot(pred);
     if (act == 0) return;
@@ -37,110 +47,348 @@ __device__ __forceinline__ void hist_add(uint32_t *hist, bool pred, uint32_t d) 
     if (pred && d != d0) atomicAdd(&hist[d], 1u);
 }
 
-// Block-wide exclusive count of pred over thread order.
-__device__ __forceinline__ void block_scan(bool pred, uint32_t *slot, int &before, int &total) {
-    const uint64_t m = __ballot(pred);
+// Exclusive prefix sum over thread order; `total` receives the block sum.
+__device__ __forceinline__ int block_excl_scan(int x, int *s_w, int &total) {
     const int lane = lane_id(), wv = wave_id();
-    const int lane_before = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) slot[wv] = (uint32_t)__popcll(m);
-    __syncthreads();
-    int wb = 0, tot = 0;
+    int inc = x;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
-        const int c = (int)slot[w];
-        wb += (w < wv) ? c : 0;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+    }
+    if (lane == kWave - 1) s_w[wv] = inc;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int c = s_w[w];
+        woff += (w < wv) ? c : 0;
         tot += c;
     }
     __syncthreads();
-    before = wb + lane_before;
     total = tot;
+    return woff + inc - x;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int lds_cap) {
-    extern __shared__ uint32_t s_keys[];
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t s_scan[2][kTopkWaves];
-    __shared__ uint32_t s_sel[2];
+struct TopkLds {        // dynamic LDS carve-up, decided on the host
+    int32_t stage_cap;  // rows up to this length are staged as keys in LDS
+    int32_t words;      // bitmap words (max_row / 32, rounded up)
+    int32_t cand_cap;   // candidate list entries
+};
 
-    const int tid = threadIdx.x;
+__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a, TopkLds lay) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+    __shared__ uint32_t hist[kBins];
+    __shared__ int s_w[kWaves];
+    __shared__ uint32_t s_mm[2 * kWaves];
+    __shared__ int s_sel[2];
+    __shared__ int s_cand_n;
+    uint32_t *keys = dyn;                                        // [stage_cap]
+    uint32_t *bm_sel = dyn + lay.stage_cap;                      // [words]
+    uint32_t *bm_eq = bm_sel + lay.words;                        // [words]
+    uint2 *cand = (uint2 *)(bm_eq + lay.words);                  // [cand_cap] (key, index)
+
+    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
     const int qi = a.batch.total_q - 1 - (int)blockIdx.x;
     const int n = min(a.batch.q_pos[qi] + 1, a.max_row);
     const int k = a.k;
     int32_t *out = a.indices + (int64_t)qi * k;
     if (n <= k) {                                      // keep every earlier token
-        for (int j = tid; j < k; j += kTopkThreads) out[j] = j < n ? j : -1;
+        for (int j = tid; j < k; j += kThreads) out[j] = j < n ? j : -1;
         return;
     }
     const float *row = a.scores + (int64_t)qi * a.ld;
-    const bool in_lds = n <= lds_cap;
-    if (in_lds) {
-        for (int j = tid; j < n; j += kTopkThreads) s_keys[j] = order_key(row[j]);
-        __syncthreads();
-    }
-    auto key_at = [&](int j) -> uint32_t { return in_lds ? s_keys[j] : order_key(row[j]); };
-
-    uint32_t prefix = 0u, mask = 0u;
-    int rem = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int t = tid; t < 256; t += kTopkThreads) hist[t] = 0u;
-        __syncthreads();
-        for (int base = 0; base < n; base += kTopkThreads) {
-            const int j = base + tid;
-            bool pred = false;
-            uint32_t d = 0u;
-            if (j < n) {
-                const uint32_t key = key_at(j);
-                pred = (key & mask) == prefix;
-                d = (key >> shift) & 255u;
+    const bool staged = n <= lay.stage_cap;
+    // kBatch keys per thread: element base + u*kThreads + tid (0 past the row end)
+    auto load_keys = [&](int base, uint32_t (&kb)[kBatch]) {
+        if (staged) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int j = base + u * kThreads + tid;
+                kb[u] = j < n ? keys[j] : 0u;
             }
-            hist_add(hist, pred, d);
+        } else {
+            float f[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int j = base + u * kThreads + tid;
+                f[u] = j < n ? row[j] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) kb[u] = order_key(f[u]);
         }
-        __syncthreads();
-        if (wave_id() == 0) {
-            // digit d with  above(d) < rem <= above(d) + hist[d],  above = count of larger digits
-            const int lane = lane_id();
-            uint32_t h[4];
+    };
+    const int W = (n + 31) >> 5;
+
+    // ---- pass 1: key range (and staging); clear the bitmaps. Loads are
+    // batched kBatch deep per thread so a workgroup keeps ~16 KiB in flight.
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    const bool vec = (((uintptr_t)row) & 15) == 0;
+    // 16-byte loads, kVecBatch per thread: a 32k-key row is in flight at once
+    for (int base = 0; vec && base < n; base += kThreads * 4 * kVecBatch) {
+        f32x4 f[kVecBatch];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = hist[4 * lane + e];
-            const uint32_t s = h[0] + h[1] + h[2] + h[3];
-            uint32_t suf = s;                          // inclusive suffix sum over lanes
+        for (int u = 0; u < kVecBatch; ++u) {
+            const int j = base + (u * kThreads + tid) * 4;
+            if (j + 3 < n) {
+                f[u] = *(const f32x4 *)(row + j);
+            } else {
 #pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const uint32_t v = __shfl_down(suf, off);
-                if (lane + off < kWave) suf += v;
+                for (int e = 0; e < 4; ++e) f[u][e] = j + e < n ? row[j + e] : 0.f;
             }
-            uint32_t acc = suf - s;
+        }
 #pragma unroll
-            for (int e = 3; e >= 0; --e) {
-                if (acc < (uint32_t)rem && (uint32_t)rem <= acc + h[e]) {
-                    s_sel[0] = (uint32_t)(4 * lane + e);
-                    s_sel[1] = acc;
+        for (int u = 0; u < kVecBatch; ++u) {
+            const int j = base + (u * kThreads + tid) * 4;
+            uint32_t kk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kk[e] = order_key(f[u][e]);
+                if (j + e < n) {
+                    kmin = min(kmin, kk[e]);
+                    kmax = max(kmax, kk[e]);
                 }
-                acc += h[e];
+            }
+            if (staged) {
+                if (j + 3 < n) {
+                    *(u32x4 *)(keys + j) = u32x4{kk[0], kk[1], kk[2], kk[3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) if (j + e < n) keys[j + e] = kk[e];
+                }
             }
         }
-        __syncthreads();
-        prefix |= s_sel[0] << shift;
-        mask |= 255u << shift;
-        rem -= (int)s_sel[1];
-        __syncthreads();
     }
+    for (int base = 0; !vec && base < n; base += kThreads * kBatch) {
+        float f[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = base + u * kThreads + tid;
+            f[u] = j < n ? row[j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = base + u * kThreads + tid;
+            if (j < n) {
+                const uint32_t key = order_key(f[u]);
+                if (staged) keys[j] = key;
+                kmin = min(kmin, key);
+                kmax = max(kmax, key);
+            }
+        }
+    }
+    for (int w = tid; w < W; w += kThreads) {
+        bm_sel[w] = 0u;
+        bm_eq[w] = 0u;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+    }
+    if (lane == 0) {
+        s_mm[wv] = kmin;
+        s_mm[kWaves + wv] = kmax;
+    }
+    if (tid == 0) s_cand_n = 0;
+    __syncthreads();
+    kmin = s_mm[0];
+    kmax = s_mm[kWaves];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        kmin = min(kmin, s_mm[w]);
+        kmax = max(kmax, s_mm[kWaves + w]);
+    }
+    const uint32_t range = kmax - kmin;
 
-    const uint32_t T = prefix;
-    const int need_eq = rem;                            // >= 1 keys equal to T are kept
-    int eq_seen = 0, sel_seen = 0;
-    for (int base = 0; base < n && sel_seen < k; base += kTopkThreads) {
-        const int j = base + tid;
-        const uint32_t key = j < n ? key_at(j) : 0u;
-        const bool gt = j < n && key > T;
-        const bool eq = j < n && key == T;
-        int eq_before, eq_total, sel_before, sel_total;
-        block_scan(eq, s_scan[0], eq_before, eq_total);
-        const bool take = gt || (eq && eq_seen + eq_before < need_eq);
-        block_scan(take, s_scan[1], sel_before, sel_total);
-        if (take && sel_seen + sel_before < k) out[sel_seen + sel_before] = j;
-        eq_seen += eq_total;
-        sel_seen += sel_total;
+    // ---- radix select on v = key - kmin: T (as v) and the number of ties needed
+    uint32_t prefix = 0u, pmask = 0u;
+    int rem = k;
+    bool use_list = false;
+    if (range != 0u) {
+        const int top = 32 - __clz((int)range);            // significant bits of range
+        int s = max(0, top - kDigit);
+        int width = top - s;
+        for (int level = 0;; ++level) {
+            const uint32_t dmask = (1u << width) - 1u;
+            for (int t = tid; t < (1 << width); t += kThreads) hist[t] = 0u;
+            __syncthreads();
+            if (use_list) {
+                const int cn = s_cand_n;
+                for (int base = 0; base < cn; base += kThreads) {
+                    const int i = base + tid;
+                    bool p = false;
+                    uint32_t d = 0u;
+                    if (i < cn) {
+                        const uint32_t v = cand[i].x - kmin;
+                        p = (v & pmask) == prefix;
+                        d = (v >> s) & dmask;
+                    }
+                    hist_add(hist, p, d);
+                }
+            } else {
+                for (int base = 0; base < n; base += kThreads * kBatch) {
+                    uint32_t kb[kBatch];
+                    load_keys(base, kb);
+#pragma unroll
+                    for (int u = 0; u < kBatch; ++u) {
+                        const int j = base + u * kThreads + tid;
+                        const uint32_t v = kb[u] - kmin;
+                        const bool p = j < n && (v & pmask) == prefix;
+                        hist_add(hist, p, (v >> s) & dmask);
+                    }
+                }
+            }
+            __syncthreads();
+            // digit d with above(d) < rem <= above(d) + hist[d], above = count of larger digits
+            {
+                const int nb = 1 << width;
+                uint32_t h[4];
+                int loc = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int bin = 4 * tid + e;
+                    h[e] = bin < nb ? hist[bin] : 0u;
+                    loc += (int)h[e];
+                }
+                int total;
+                const int before = block_excl_scan(loc, s_w, total);   // count in lower bins
+                int cum = before;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int above = total - cum - (int)h[e];
+                    if (above < rem && rem <= above + (int)h[e]) {
+                        s_sel[0] = 4 * tid + e;
+                        s_sel[1] = above;
+                    }
+                    cum += (int)h[e];
+                }
+            }
+            __syncthreads();
+            const uint32_t d = (uint32_t)s_sel[0];
+            rem -= s_sel[1];
+            prefix |= d << s;
+            pmask |= dmask << s;
+            const int in_bin = (int)hist[d];
+            __syncthreads();
+            if (level == 0) {
+                // classify: above T's first digit -> selected; in its bin -> candidate
+                const bool fits = in_bin <= lay.cand_cap;
+                for (int base = 0; base < n; base += kThreads * kBatch) {
+                  uint32_t kb[kBatch];
+                  load_keys(base, kb);
+#pragma unroll
+                  for (int u = 0; u < kBatch; ++u) {
+                    const int j = base + u * kThreads + tid;
+                    const int c = j >> 6;                        // 64-key chunk of this wave
+                    const uint32_t v = kb[u] - kmin;
+                    const uint32_t dj = v >> s;
+                    const bool above = j < n && dj > d;
+                    const bool inb = j < n && dj == d;
+                    const uint64_t ma = __ballot(above);
+                    if (lane == 0 && 2 * c < W) {
+                        bm_sel[2 * c] = (uint32_t)ma;
+                        if (2 * c + 1 < W) bm_sel[2 * c + 1] = (uint32_t)(ma >> 32);
+                    }
+                    if (fits) {
+                        const uint64_t mc = __ballot(inb);
+                        int cb = 0;
+                        if (lane == 0 && mc) cb = atomicAdd(&s_cand_n, __popcll(mc));
+                        cb = __shfl(cb, 0);
+                        if (inb)
+                            cand[cb + __popcll(mc & ((1ull << lane) - 1ull))] =
+                                make_uint2(v + kmin, (uint32_t)j);
+                    }
+                  }
+                }
+                __syncthreads();
+                use_list = fits;
+            }
+            if (s == 0) break;
+            const int s_next = max(0, s - kDigit);
+            width = s - s_next;
+            s = s_next;
+        }
+    }
+    const uint32_t T = kmin + prefix;
+    const int need_eq = rem;                           // >= 1 keys equal to T are kept
+
+    // ---- mark keys above T and ties in the bitmaps
+    if (range == 0u) {
+        // every key equal: nothing above T, all ties
+        for (int c = wv; c * 64 < n; c += kWaves) {
+            const int j = c * 64 + lane;
+            const uint64_t m = __ballot(j < n);
+            if (lane == 0) {
+                bm_eq[2 * c] = (uint32_t)m;
+                if (2 * c + 1 < W) bm_eq[2 * c + 1] = (uint32_t)(m >> 32);
+            }
+        }
+    } else if (use_list) {
+        const int cn = s_cand_n;
+        for (int i = tid; i < cn; i += kThreads) {
+            const uint2 ce = cand[i];
+            if (ce.x > T) atomicOr(&bm_sel[ce.y >> 5], 1u << (ce.y & 31));
+            else if (ce.x == T) atomicOr(&bm_eq[ce.y >> 5], 1u << (ce.y & 31));
+        }
+    } else {
+        // candidate bin too large for the list: one more pass over the row
+        for (int base = 0; base < n; base += kThreads * kBatch) {
+          uint32_t kb[kBatch];
+          load_keys(base, kb);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int j = base + u * kThreads + tid;
+            const int c = j >> 6;
+            const uint32_t key = kb[u];
+            const uint64_t mg = __ballot(j < n && key > T);
+            const uint64_t me = __ballot(j < n && key == T);
+            if (lane == 0 && 2 * c < W) {
+                bm_sel[2 * c] |= (uint32_t)mg;
+                bm_eq[2 * c] = (uint32_t)me;
+                if (2 * c + 1 < W) {
+                    bm_sel[2 * c + 1] |= (uint32_t)(mg >> 32);
+                    bm_eq[2 * c + 1] = (uint32_t)(me >> 32);
+                }
+            }
+          }
+        }
+    }
+    __syncthreads();
+
+    // ---- ordered output: every selected bit plus the first need_eq ties
+    const int per = (W + kThreads - 1) / kThreads;
+    const int w0 = min(W, tid * per), w1 = min(W, w0 + per);
+    int ecount = 0;
+    for (int w = w0; w < w1; ++w) ecount += __popc(bm_eq[w]);
+    int etot;
+    int ebefore = block_excl_scan(ecount, s_w, etot);
+    int scount = 0;
+    for (int w = w0; w < w1; ++w) {
+        uint32_t eq = bm_eq[w];
+        const int avail = __popc(eq);
+        const int take = max(0, min(avail, need_eq - ebefore));
+        ebefore += avail;
+        uint32_t keep = 0u;
+        for (int t = 0; t < take; ++t) {
+            const uint32_t low = eq & (0u - eq);
+            keep |= low;
+            eq ^= low;
+        }
+        const uint32_t f = bm_sel[w] | keep;
+        bm_sel[w] = f;
+        scount += __popc(f);
+    }
+    int stot;
+    int pos_out = block_excl_scan(scount, s_w, stot);
+    for (int w = w0; w < w1; ++w) {
+        uint32_t f = bm_sel[w];
+        while (f) {
+            const int bit = __ffs(f) - 1;
+            f &= f - 1u;
+            if (pos_out < k) out[pos_out] = 32 * w + bit;
+            ++pos_out;
+        }
     }
 }
 
@@ -148,13 +396,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a, int lds_
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     if (a.batch.total_q <= 0) return hipSuccess;
-    const int cap = a.max_row < kLdsCapKeys ? a.max_row : kLdsCapKeys;
-    const size_t lds = (size_t)cap * sizeof(uint32_t);
+    TopkLds lay;
+    lay.words = (a.max_row + 31) / 32;
+    const size_t bitmaps = (size_t)2 * lay.words * 4;
+    const size_t min_cand = 512 * 8;
+    const size_t room = kLdsBudget > bitmaps + min_cand ? kLdsBudget - bitmaps - min_cand : 0;
+    int stage = (int)(room / 4);
+    if (stage > 32768) stage = 32768;
+    if (stage > a.max_row) stage = a.max_row;
+    lay.stage_cap = stage;
+    const size_t used = (size_t)stage * 4 + bitmaps;
+    lay.cand_cap = used < kLdsBudget ? (int)((kLdsBudget - used) / 8) : 0;
+    const size_t lds = used + (size_t)lay.cand_cap * 8;
     const hipError_t e = hipFuncSetAttribute((const void *)topk_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)(kLdsCapKeys * sizeof(uint32_t)));
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_kernel, dim3(a.batch.total_q), dim3(kTopkThreads), lds, s, a, cap);
+    hipLaunchKernelGGL(topk_kernel, dim3(a.batch.total_q), dim3(kThreads), lds, s, a, lay);
     return hipGetLastError();
 }
 

@@ -161,7 +161,8 @@ def test_indexer_small_integers_bit_exact(sm, H, D):
 
 
 # ----------------------------------------------------------------- top-k --
-@pytest.mark.parametrize("kind", ["all_equal", "relu_zeros", "small_int", "signed_zero", "normal"])
+@pytest.mark.parametrize("kind", ["all_equal", "relu_zeros", "small_int", "signed_zero", "normal",
+                                  "coarse"])
 def test_topk_ties_bit_exact(sm, kind):
     g = torch.Generator().manual_seed(3)
     n, L, k = 24, 70000, 2048
@@ -176,6 +177,8 @@ def test_topk_ties_bit_exact(sm, kind):
     elif kind == "signed_zero":
         s = torch.where(torch.rand(n, L, generator=g) < 0.5, -0.0, 0.0)
         s[:, ::97] = 1.0
+    elif kind == "coarse":                 # many exact ties inside the threshold bin
+        s = torch.round(torch.randn(n, L, generator=g) * 4) * 2.5
     else:
         s = torch.randn(n, L, generator=g) * 100
     batch = sm.Batch([0, n], [0, L], pos, "cuda")
