@@ -46,7 +46,8 @@ constexpr int kThreads = 256;              // 4 waves: (head group, dim half)
 constexpr int kBlk = 32;                    // keys per block
 constexpr int kQK = 576, kV = 512;
 constexpr int kQKHalf = kQK / 2, kVHalf = kV / 2;
-constexpr float kLazyRescale = 8.0f;        // log2 headroom before the running max moves
+constexpr float kHeadroom = 64.0f;          // log2 headroom of the reference max (see below)
+constexpr float kClampLog2 = 100.0f;        // exponent clamp for a pass that will be redone
 constexpr int O_LD = kVHalf + 8;            // epilogue staging pitch (bf16)
 
 typedef int v2i32 __attribute__((ext_vector_type(2)));
@@ -106,7 +107,7 @@ template <bool FP8> constexpr size_t lds_bytes() {          // dynamic part: rin
 }
 template <bool FP8> constexpr size_t lds_static_bytes() {   // entry table
     using C = Cfg<FP8>;
-    return (size_t)C::kIdx * 4 + (FP8 ? C::kIdx : 4) * 4;
+    return (size_t)C::kIdx * 4 + (FP8 ? C::kIdx : 4) * 4 + 16;   // + restart votes
 }
 
 template <bool FP8>
@@ -160,17 +161,41 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         for (int t = 0; t < kQKHalf / 16; ++t) asm volatile("" ::"v"(qf[t]));
     }
 
-    float m_run = -INFINITY, l_run = 0.f;       // head `col`, this lane's keys
-    f32x16 o[kVHalf / 32];
+    // per-lane DMA slot constants (same for every block)
+    constexpr int kDmaIns = (kDma + 3) / 4;
+    int dma_r[kDmaIns], dma_lc[kDmaIns];
 #pragma unroll
-    for (int nb = 0; nb < kVHalf / 32; ++nb) o[nb] = zero16();
+    for (int u = 0; u < kDmaIns; ++u) {
+        const int sidx = (wv + 4 * u) * 64 + lane;
+        dma_r[u] = sidx / C::kChunks;
+        dma_lc[u] = 16 * ((sidx % C::kChunks) ^ swz<FP8>(dma_r[u]));
+    }
+
+    // Online softmax in base 2 against a reference max m_run per head. m_run is
+    // set by the first block with a valid key and only ever raised by a restart:
+    // probabilities exp2(t - m_run) may exceed 1 by up to 2^kHeadroom, which
+    // bf16 P and the fp32 sums hold exactly enough, so the 128 fp32 accumulators
+    // per lane are never rescaled inside the loop. A block overshooting by more
+    // makes the workgroup redo the query with the larger reference (the vote
+    // travels through s_redo, double-buffered by block parity).
+    __shared__ int s_redo[2];
+    float m_run = -INFINITY, l_run = 0.f;       // head `col`, this lane's keys
+    float m_seen = -INFINITY;                   // largest block max of head `col` seen
+    f32x16 o[kVHalf / 32];
     const float inv_c = 1.0f / a.scale_log2;
     // row this lane feeds into the QK A operand: accumulator row m = col
     const int qk_row = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
     const int qk_swz = swz<FP8>(qk_row);
     int parity = 0;
+    int nblk_seen = 0;                           // blocks processed, for the vote parity
+    if (tid < 2) s_redo[tid] = 0;
 
-    for (int c0 = 0; c0 < n_keys; c0 += chunk_len) {
+    for (;;) {                                   // attempts: one unless a block overshoots
+#pragma unroll
+    for (int nb = 0; nb < kVHalf / 32; ++nb) o[nb] = zero16();
+    l_run = 0.f;
+    bool redo = false;
+    for (int c0 = 0; c0 < n_keys && !redo; c0 += chunk_len) {
         const int cn = min(chunk_len, n_keys - c0);               // entries in this chunk
         const int n_blk = (cn + kBlk - 1) / kBlk;
         if (table) {
@@ -191,19 +216,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             if (table) return s_row[e];
             return e < cn ? c0 + e : -1;
         };
-        // DMA one block into ring slot `slot`: this wave issues instructions wv, wv+4, ...
+        // DMA one block into ring slot `slot`: this wave issues instructions
+        // wv, wv+4, ... (16-byte slot sidx = ins*64 + lane holds logical chunk
+        // dma_lc[u] of block row dma_r[u]); row offsets stay 32-bit.
         auto issue = [&](int blk, int slot) {
             uint8_t *dst = ring + slot * kBlockBytes;
 #pragma unroll
-            for (int u = 0; u < (kDma + 3) / 4; ++u) {
-                const int ins = wv + 4 * u;
-                if (ins < kDma) {
-                    const int sidx = ins * 64 + lane;             // 16-byte slot in the block
-                    const int r = sidx / C::kChunks, pc = sidx % C::kChunks;
-                    const int lc = pc ^ swz<FP8>(r);              // logical chunk stored at pc
-                    const int j = row_of(blk * kBlk + r);
-                    const uint8_t *src = kvq + (int64_t)(j >= 0 ? j : 0) * a.kv_stride + 16 * lc;
-                    dma16(src, dst + ins * 1024);
+            for (int u = 0; u < kDmaIns; ++u) {
+                if (wv + 4 * u < kDma) {
+                    const int j = max(row_of(blk * kBlk + dma_r[u]), 0);
+                    const uint32_t off = (uint32_t)j * (uint32_t)a.kv_stride + (uint32_t)dma_lc[u];
+                    dma16(kvq + off, dst + (wv + 4 * u) * 1024);
                 }
             }
         };
@@ -213,19 +236,35 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             const int slot = blk % C::kRing;
             wait_vm_blocks<kDma / 4>(min(C::kRing - 2, n_blk - 1 - blk));
             lds_barrier();                               // block blk landed; slot of blk-1 free
+            const int vp = nblk_seen & 1;                // this block votes into s_redo[vp]
+            if (nblk_seen > 0 && s_redo[vp ^ 1]) {       // uniform: last block's vote
+                redo = true;
+                break;
+            }
+            ++nblk_seen;
             if (blk + C::kRing - 1 < n_blk) issue(blk + C::kRing - 1, (blk + C::kRing - 1) % C::kRing);
             const uint8_t *kb = ring + slot * kBlockBytes;
 
-            // ---- partial S^T = K Q^T over this wave's 288 dims
+            // ---- partial S^T = K Q^T over this wave's 288 dims. The XOR swizzle
+            // only touches the low chunk bits, so (L + 4m) ^ sw == (L ^ sw) + 4m
+            // (FP8; 8m for bf16): a few per-lane bases plus immediate offsets
+            // address every k-step. All K reads are issued before the MFMAs, and
+            // even / odd k-steps accumulate in two independent chains.
             f32x16 s = zero16();
             {
                 const uint8_t *krow = kb + qk_row * C::kRowBytes;
                 if (FP8) {
+                    const uint8_t *ke = krow + 16 * ((18 * dh + g) ^ qk_swz);
+                    const uint8_t *ko = krow + 16 * ((18 * dh + g + 2) ^ qk_swz);
+                    // reads run two k-steps ahead of their use
+                    u32x4 r0 = *(const u32x4 *)ke, r1 = *(const u32x4 *)ko;
 #pragma unroll
                     for (int t = 0; t < kQKHalf / 32; ++t) {
-                        if (t % 3 == 0) __builtin_amdgcn_sched_barrier(0);
-                        const int lc = 18 * dh + 2 * t + g;
-                        const u32x4 raw = *(const u32x4 *)(krow + 16 * (lc ^ qk_swz));
+                        const u32x4 raw = (t & 1) ? r1 : r0;
+                        if (t + 2 < kQKHalf / 32) {
+                            const u32x4 nx = *(const u32x4 *)((((t + 2) & 1) ? ko : ke) + 64 * ((t + 2) >> 1));
+                            if (t & 1) r1 = nx; else r0 = nx;
+                        }
                         bf16x8 k0, k1;
                         fp8x4_to_bf16(raw[0], k0, 0);
                         fp8x4_to_bf16(raw[1], k0, 4);
@@ -235,12 +274,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                         s = mfma32x32x16(k1, qf[2 * t + 1], s);
                     }
                 } else {
+                    const int L0 = 36 * dh + 2 * g;
+                    const uint8_t *e0 = krow + 16 * (L0 ^ qk_swz), *e1 = krow + 16 * ((L0 + 1) ^ qk_swz);
+                    const uint8_t *o0 = krow + 16 * ((L0 + 4) ^ qk_swz), *o1 = krow + 16 * ((L0 + 5) ^ qk_swz);
 #pragma unroll
                     for (int t = 0; t < kQKHalf / 32; ++t) {
-                        if (t % 3 == 0) __builtin_amdgcn_sched_barrier(0);
-                        const int lc = 36 * dh + 2 * (2 * t + g);
-                        const bf16x8 k0 = *(const bf16x8 *)(krow + 16 * (lc ^ qk_swz));
-                        const bf16x8 k1 = *(const bf16x8 *)(krow + 16 * ((lc + 1) ^ qk_swz));
+                        const bf16x8 k0 = *(const bf16x8 *)(((t & 1) ? o0 : e0) + 128 * (t >> 1));
+                        const bf16x8 k1 = *(const bf16x8 *)(((t & 1) ? o1 : e1) + 128 * (t >> 1));
                         s = mfma32x32x16(k0, qf[2 * t], s);
                         s = mfma32x32x16(k1, qf[2 * t + 1], s);
                     }
@@ -254,6 +294,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 for (int q4 = 0; q4 < 4; ++q4)
                     mine[q4 * 64 + lane] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
                 lds_barrier();
+                if (tid == 0) s_redo[vp ^ 1] = 0;            // every wave has read it
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const f32x4 v = other[q4 * 64 + lane];
@@ -293,67 +334,95 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 }
             }
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const bool grow = mx > m_run + kLazyRescale;
-            if (__any(grow)) {                                   // rare: move the running max
-                const float m_new = grow ? mx : m_run;
-                const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-                m_run = m_new;
-                // O rows are heads 8i + 4g + j; their alphas live in lanes 0..31
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float ar = __shfl(alpha, 8 * i + 4 * g + j);
-#pragma unroll
-                        for (int nb = 0; nb < kVHalf / 32; ++nb) o[nb][4 * i + j] *= ar;
-                    }
-            }
+            m_seen = fmaxf(m_seen, mx);
+            if (m_run == -INFINITY) m_run = mx;          // first valid keys: nothing to rescale
+            if (__any(mx > m_run + kHeadroom) && lane == 0) s_redo[vp] = 1;
             const float msub = m_run == -INFINITY ? 0.f : m_run;
             bf16x8 pa[2];
             float psum = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(s[e] - msub);
+                const float p = __builtin_amdgcn_exp2f(fminf(s[e] - msub, kClampLog2));
                 psum += p;
                 pa[e >> 3][e & 7] = (__bf16)(FP8 ? p * __int_as_float(rw[e]) : p);
             }
             l_run += psum;
 
-            // ---- O[:, 256*dh ..] += P V; k-step t = LDS rows 16g + 8t .. +7
+            // ---- O[:, 256*dh ..] += P V; k-step t = LDS rows 16g + 8t .. +7. The
+            // chunk swizzle of the rows a lane addresses does not depend on t or
+            // on the N-block, so per-lane bases plus immediates address them all.
             {
                 const int gi = lane & 15, hh = (lane >> 4) & 1;
+                if (FP8) {
+                    // lane supplies row 16g + 8t + (gi >> 1), bytes 8*(gi & 1).. of
+                    // logical chunk 16*dh + 2*nb + hh
+                    const int sw = ((gi >> 3) & 1) | (g << 1);
+                    const int L1 = 16 * dh + hh;
+                    const uint8_t *rb = kb + (16 * g + (gi >> 1)) * C::kRowBytes + 8 * (gi & 1);
+                    const uint8_t *ve = rb + 16 * (L1 ^ sw), *vo = rb + 16 * ((L1 + 2) ^ sw);
+                    v2i32 w8[kVHalf / 32][2];
 #pragma unroll
-                for (int nb = 0; nb < kVHalf / 32; ++nb) {
-                    if (nb % 2 == 0) __builtin_amdgcn_sched_barrier(0);
+                    for (int nb = 0; nb < kVHalf / 32; ++nb)
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int R0 = 16 * g + 8 * t;
-                        bf16x8 vb;
-                        if (FP8) {
-                            const int r = R0 + (gi >> 1);
-                            const int lc = 16 * dh + 2 * nb + hh;
-                            const uint8_t *src = kb + r * C::kRowBytes + 16 * (lc ^ swz<FP8>(r)) + 8 * (gi & 1);
-                            const v2i32 w8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_ptr)src);
-                            fp8x4_to_bf16((uint32_t)w8[0], vb, 0);
-                            fp8x4_to_bf16((uint32_t)w8[1], vb, 4);
-                        } else {
+                        for (int t = 0; t < 2; ++t)
+                            w8[nb][t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                (lds_v2i32_ptr)(((nb & 1) ? vo : ve) + 64 * (nb >> 1) + 8 * C::kRowBytes * t));
 #pragma unroll
-                            for (int v = 0; v < 2; ++v) {
-                                const int r = R0 + 4 * v + (gi >> 2);
-                                const int lc = 32 * dh + 4 * nb + 2 * hh + ((gi & 3) >> 1);
-                                const uint8_t *src = kb + r * C::kRowBytes + 16 * (lc ^ swz<FP8>(r)) + 8 * (gi & 1);
-                                const bf16x4 w16 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)src);
+                    for (int nb = 0; nb < kVHalf / 32; ++nb)
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) vb[4 * v + e] = w16[e];
-                            }
+                        for (int t = 0; t < 2; ++t) {
+                            bf16x8 vb;
+                            fp8x4_to_bf16((uint32_t)w8[nb][t][0], vb, 0);
+                            fp8x4_to_bf16((uint32_t)w8[nb][t][1], vb, 4);
+                            o[nb] = mfma32x32x16(pa[t], vb, o[nb]);
                         }
-                        o[nb] = mfma32x32x16(pa[t], vb, o[nb]);
+                } else {
+                    // lane supplies row 16g + 8t + 4v + (gi >> 2), dims 4*(gi & 3).. of
+                    // the N-block's 16-dim group; logical chunk 32*dh + 4*nb + 2*hh + ((gi&3)>>1)
+                    const int L2 = 32 * dh + 2 * hh + ((gi & 3) >> 1);
+                    const uint8_t *vb0[2][2];
+#pragma unroll
+                    for (int v = 0; v < 2; ++v) {
+                        const int sw = (2 * v + (gi >> 3)) | (g << 2);
+                        const uint8_t *rb = kb + (16 * g + 4 * v + (gi >> 2)) * C::kRowBytes + 8 * (gi & 1);
+                        vb0[v][0] = rb + 16 * (L2 ^ sw);
+                        vb0[v][1] = rb + 16 * ((L2 + 4) ^ sw);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < kVHalf / 32; ++nb) {
+                        bf16x4 w16[2][2];
+#pragma unroll
+                        for (int t = 0; t < 2; ++t)
+#pragma unroll
+                            for (int v = 0; v < 2; ++v)
+                                w16[t][v] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                    (lds_bf16x4_ptr)(vb0[v][nb & 1] + 128 * (nb >> 1) + 8 * C::kRowBytes * t));
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            bf16x8 vb;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                vb[e] = w16[t][0][e];
+                                vb[4 + e] = w16[t][1][e];
+                            }
+                            o[nb] = mfma32x32x16(pa[t], vb, o[nb]);
+                        }
                     }
                 }
             }
         }
+        if (redo) break;
         lds_barrier();        // every wave is done with the ring and the entry table
+    }
+    if (!redo && nblk_seen > 0) redo = s_redo[(nblk_seen & 1) ^ 1] != 0;   // last block's vote
+    if (!redo) break;
+    // redo the query with a larger reference max: drain the ring, clear the votes
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (tid < 2) s_redo[tid] = 0;
+    m_run = fmaxf(m_run, m_seen);
+    nblk_seen = 0;
+    lds_barrier();
     }
 
     // ---- epilogue: l over both lane halves; LSE; O / l staged through LDS as bf16

@@ -139,6 +139,32 @@ def test_dense_equals_sparse_with_full_lists(sm):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("kv_dtype,listed", [("bf16", False), ("bf16", True), ("fp8", False),
+                                             ("fp8", True)])
+def test_wide_logit_range(sm, kv_dtype, listed):
+    """Logits spread over hundreds of units (q scaled by 40): block maxima
+    climb far above the first block's, across several chunks of the entry
+    table, with the keys listed in a shuffled order."""
+    L = 2600
+    wl = mla_inputs.Workload("wide", (L,), (((L - 12, L),),), n_heads=64, idx_heads=4,
+                             idx_dim=64, topk=L, kv_dtype=kv_dtype, dense=not listed, seed=25)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu"))
+    inp["q"] = (inp["q"].float() * 40).to(torch.bfloat16)
+    batch = sm.Batch.from_inputs(inp)
+    idx = None
+    if listed:
+        g = torch.Generator().manual_seed(5)
+        idx = torch.stack([torch.randperm(L, generator=g) for _ in range(wl.total_q)]).int().cuda()
+        idx = torch.where(idx <= inp["q_pos"][:, None], idx, torch.full_like(idx, -1))
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.total_q)
+    r_out, r_lse = oracle.attention_rows(inp, rows, None if idx is None else idx.cpu().numpy())
+    tol = TOL[kv_dtype]
+    assert_close("wide out", out.float().cpu().numpy(), r_out, tol, tol)
+    assert_close("wide lse", lse.cpu().numpy(), r_lse, tol, tol)
+
+
 # --------------------------------------------------------------- indexer --
 @pytest.mark.parametrize("H,D", [(64, 128), (4, 64), (33, 128)])
 def test_indexer_small_integers_bit_exact(sm, H, D):
