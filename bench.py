@@ -12,6 +12,8 @@ Default workload: 32,768-token sparse prefill, 64 heads, indexer 64 x 128
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -80,6 +82,81 @@ def kernel_bytes(wl, kv_dtype: str) -> dict:
     return out
 
 
+# ---------------------------------------------------------------- traffic --
+# Measured HBM traffic per launch comes from two rocprofv3 counter passes over
+# this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
+# what the same counter reads for a device-to-device copy of known size run
+# in the same process (--copy-calibration-mib). The figures are stored with a
+# hash of the kernel's sources and reported only while the sources match.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {"attention": "attention.hip", "indexer": "indexer.hip", "topk": "topk.hip"}
+KERNEL_SYMBOLS = {"attention": "attn_kernel", "indexer": "indexer_kernel", "topk": "topk_kernel"}
+COPY_SYMBOL = "copyBuffer"
+
+
+def kernel_source_hash(name: str) -> str:
+    csrc = os.path.join(ROOT, "sparse_mla_long_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[name], "common.h", "kernels.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_rows(path: str, counter: str) -> list:
+    with open(path, newline="") as fh:
+        return [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str,
+                    kv_dtype: str, command: str) -> dict:
+    """Turn the two counter passes into bytes per launch and store them."""
+    n = calib_mib << 20
+    rec = {"workload": workload, "kv_dtype": kv_dtype, "calibration_bytes": n,
+           "command": command, "kernels": {}}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _counter_rows(path, counter)
+        copies = [float(r["Counter_Value"]) for r in rows if COPY_SYMBOL in r["Kernel_Name"]]
+        if not copies:
+            raise SystemExit("no %s dispatch in %s" % (COPY_SYMBOL, path))
+        kib = max(copies)                      # the calibration copy is by far the largest
+        factor = n / (kib * 1024.0)
+        rec[key + "_factor"] = factor
+        rec[key + "_copy_kib"] = kib
+        for name, sym in KERNEL_SYMBOLS.items():
+            vals = [float(r["Counter_Value"]) for r in rows if sym in r["Kernel_Name"]]
+            if vals:
+                d = rec["kernels"].setdefault(name, {"source_hash": kernel_source_hash(name)})
+                d[key + "_kib_avg"] = float(np.mean(vals))
+                d[key + "_bytes"] = float(np.mean(vals)) * 1024.0 * factor
+                d[key + "_dispatches"] = len(vals)
+    for d in rec["kernels"].values():
+        d["bytes"] = d.get("fetch_bytes", 0.0) + d.get("write_bytes", 0.0)
+    table = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            table = json.load(fh)
+    table["%s/%s" % (workload, kv_dtype)] = rec
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return rec
+
+
+def measured_traffic(workload: str, kv_dtype: str, name: str):
+    """HBM bytes per launch of kernel `name` from the stored counter passes,
+    or None when there are none or the kernel's sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        rec = json.load(fh).get("%s/%s" % (workload, kv_dtype))
+    d = rec and rec["kernels"].get(name)
+    if not d or d["source_hash"] != kernel_source_hash(name) or "fetch_bytes" not in d \
+            or "write_bytes" not in d:
+        return None
+    return d["bytes"]
+
+
 # ------------------------------------------------------------------ bench --
 def cpu_baseline(inp, wl, budget_s: float = 12.0, seed: int = 7) -> dict:
     """The fp64 oracle (indexer -> top-k -> attention) timed on the host cores
@@ -129,7 +206,23 @@ def main():
     ap.add_argument("--kv-dtype", default=None, help="override the workload's KV dtype (bf16/fp8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this size before the steps (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="store per-launch traffic from two rocprofv3 counter CSVs and exit")
+    ap.add_argument("--command", default="", help="with --ingest-counters: the profiling command")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        import mla_inputs
+        wl = mla_inputs.WORKLOADS[args.workload]
+        if args.copy_calibration_mib <= 0:
+            raise SystemExit("--ingest-counters needs the --copy-calibration-mib of the runs")
+        rec = ingest_counters(args.ingest_counters[0], args.ingest_counters[1],
+                              args.copy_calibration_mib, wl.name, args.kv_dtype or wl.kv_dtype,
+                              args.command)
+        print(json.dumps(rec, indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
@@ -175,6 +268,12 @@ def main():
                           out=out, lse=lse)
         mark(3)
 
+    if args.copy_calibration_mib > 0:
+        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -203,6 +302,7 @@ def main():
         if n in byts:
             d["algo_bytes"] = byts[n]
             d["gbs"] = byts[n] / t / 1e9
+        d["traffic"] = measured_traffic(wl.name, kv_dtype, n)
         kern[n] = d
     kern["topk"] = kern.get("topk", {})
     if "topk" in per_kernel_ms:
@@ -214,10 +314,11 @@ def main():
     dk = kern[dominant]
     if dk.get("bound") == "mfma":
         roof = {"bound": "mfma", "kernel": dominant, "achieved": dk["tflops"],
-                "peak": dk["peak_tflops"], "unit": "TFLOP/s", "frac": dk["frac"], "traffic": None}
+                "peak": dk["peak_tflops"], "unit": "TFLOP/s", "frac": dk["frac"],
+                "traffic": dk["traffic"]}
     else:
         roof = {"bound": "hbm", "kernel": dominant, "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": dk["frac"], "traffic": None}
+                "unit": "GB/s", "frac": dk["frac"], "traffic": dk["traffic"]}
 
     ms_step = elapsed / args.steps * 1e3
     t_kernels = sum(per_kernel_ms.values()) * 1e-3

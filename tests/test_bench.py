@@ -1,0 +1,84 @@
+"""Host-side checks of the benchmark's accounting and its traffic bookkeeping."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import mla_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_attention_flop_per_pair_matches_the_footnote():
+    # spke.com article, footnote 1: 2 * (576 + 512) = 2,176 FLOP per row and head
+    assert bench.attn_flop_per_pair(1) == 2176
+    assert bench.attn_flop_per_pair(64) == 64 * 2176
+
+
+def test_pair_counts_by_brute_force():
+    wl = mla_inputs.Workload("pc", (50, 7), (((0, 20), (40, 50)), ((3, 7),)), n_heads=8,
+                             idx_heads=4, idx_dim=64, topk=16, kv_dtype="bf16", seed=0)
+    causal = selected = 0
+    for p in wl.q_pos():
+        keys = list(range(p + 1))
+        causal += len(keys)
+        selected += min(len(keys), 16)
+    pc = bench.pair_counts(wl)
+    assert pc == {"causal": causal, "selected": selected}
+    f = bench.workload_flops(wl)
+    assert f["attention"] == selected * 8 * 2176
+    assert f["indexer"] == causal * 2 * 4 * 64
+
+
+def test_sparse32k_totals():
+    wl = mla_inputs.WORKLOADS["sparse32k"]
+    pc = bench.pair_counts(wl)
+    n = 32768
+    assert pc["causal"] == n * (n + 1) // 2
+    assert pc["selected"] == sum(min(p + 1, 2048) for p in range(n))
+
+
+def _write_csv(path, rows):
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=cols)
+        w.writeheader()
+        for i, (k, c, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_counter_ingestion_scales_by_the_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    f_csv, w_csv = tmp_path / "f.csv", tmp_path / "w.csv"
+    # the 64 MiB copy reads 2x its size by this counter, writes 1x; a small copy is ignored
+    _write_csv(f_csv, [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 64.0),
+                       ("__amd_rocclr_copyBuffer", "FETCH_SIZE", 2 * 65536.0),
+                       ("mla::attn_kernel<true>", "FETCH_SIZE", 1000.0),
+                       ("mla::attn_kernel<true>", "FETCH_SIZE", 3000.0)])
+    _write_csv(w_csv, [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 65536.0),
+                       ("mla::attn_kernel<true>", "WRITE_SIZE", 10.0),
+                       ("mla::attn_kernel<true>", "WRITE_SIZE", 30.0)])
+    rec = bench.ingest_counters(str(f_csv), str(w_csv), 64, "sparse32k", "fp8", "cmd")
+    a = rec["kernels"]["attention"]
+    assert rec["fetch_factor"] == pytest.approx(0.5)
+    assert a["fetch_bytes"] == pytest.approx(2000 * 1024 * 0.5)
+    assert a["write_bytes"] == pytest.approx(20 * 1024)
+    assert bench.measured_traffic("sparse32k", "fp8", "attention") == pytest.approx(a["bytes"])
+    assert bench.measured_traffic("sparse32k", "bf16", "attention") is None
+    assert bench.measured_traffic("sparse32k", "fp8", "indexer") is None
+    # a changed kernel source invalidates the stored figure
+    table = json.load(open(bench.TRAFFIC_FILE))
+    table["sparse32k/fp8"]["kernels"]["attention"]["source_hash"] = "stale"
+    json.dump(table, open(bench.TRAFFIC_FILE, "w"))
+    assert bench.measured_traffic("sparse32k", "fp8", "attention") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "one GPU" in r.stderr
