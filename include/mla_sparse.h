@@ -132,9 +132,11 @@ mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int6
  *   kv_scale device fp32, scale of row r at byte offset r * kv_scale_stride (a
  *            multiple of 4); required for MLA_KV_FP8_E4M3, ignored for bf16
  *   indices  device [total_q, k] int32 local key indices, or NULL (dense causal)
- *   out      device [total_q, n_heads, 512] bf16 (round to nearest even)
+ *   out      device [total_q, n_heads, 512] bf16 (round to nearest even), 16-byte aligned
  *   lse      device [total_q, n_heads] fp32, natural log (sm_scale included)
- * Supported: n_heads in {8, 16, 32, 64}; 1 <= k <= 65536 when indices != NULL. */
+ * Supported: n_heads in {8, 16, 32, 64}; 1 <= k <= 65536 when indices != NULL;
+ * max_kv_len * kv_row_stride < 4 GiB (the rows of one sequence are addressed
+ * with 32-bit offsets); MLA_ERR_UNSUPPORTED otherwise. */
 mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const void *kv,
                                 const float *kv_scale, mla_kv_dtype_t kv_dtype,
                                 int64_t kv_row_stride, int64_t kv_scale_stride,

@@ -160,12 +160,15 @@ mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const v
     if (n_heads != 8 && n_heads != 16 && n_heads != 32 && n_heads != 64)
         return fail(MLA_ERR_UNSUPPORTED, "n_heads %d not in {8, 16, 32, 64}", n_heads);
     if (indices && k > 65536) return fail(MLA_ERR_UNSUPPORTED, "k %d > 65536", k);
+    if ((int64_t)batch->max_kv_len * kv_row_stride > (int64_t)UINT32_MAX)
+        return fail(MLA_ERR_UNSUPPORTED, "a sequence's KV rows span %lld bytes (>= 4 GiB)",
+                    (long long)batch->max_kv_len * kv_row_stride);
     if (batch->total_q == 0) return ok();
     if (!q || !kv || !out || !lse || (fp8 && !kv_scale))
         return fail(MLA_ERR_INVALID_ARG, "q / kv / out / lse%s is NULL", fp8 ? " / kv_scale" : "");
     if (!aligned(q, 16) || !aligned(kv, 16))
         return fail(MLA_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");
-    if (!aligned(out, 2) || !aligned(lse, 4) || (fp8 && !aligned(kv_scale, 4)) ||
+    if (!aligned(out, 16) || !aligned(lse, 4) || (fp8 && !aligned(kv_scale, 4)) ||
         (indices && !aligned(indices, 4)))
         return fail(MLA_ERR_INVALID_ARG, "out / lse / kv_scale / indices misaligned");
     a.q = (const __bf16 *)q;

@@ -41,7 +41,8 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+// wave index as a scalar (uniform in the wave), so conditions on it branch on SCC
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

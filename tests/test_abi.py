@@ -139,6 +139,10 @@ def test_attention_argument_checks(lib):
     assert attn_call(lib, b, k=70000) == UNSUPPORTED
     assert attn_call(lib, b, q=FAKE + 4) == INVALID
     assert attn_call(lib, b, lse=None) == INVALID
+    assert attn_call(lib, b, out=FAKE + 2) == INVALID        # 16-byte output stores
+    big, keep2 = make_batch(cu_q=(0, 4), cu_kv=(0, 8_000_000))
+    assert attn_call(lib, big) == UNSUPPORTED                  # 8M rows x 576 B >= 4 GiB
+    assert attn_call(lib, big, stride=512 + 64) == UNSUPPORTED
 
 
 def test_empty_batch_enqueues_nothing(lib):
