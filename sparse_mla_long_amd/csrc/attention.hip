@@ -140,7 +140,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     __shared__ __attribute__((aligned(16))) int32_t s_row[kTab];             // row, or -1
     __shared__ __attribute__((aligned(16))) float s_bias[kTab];              // 0, or -inf if masked
     __shared__ __attribute__((aligned(16))) float s_mul[FP8 ? C::kIdx : 4];  // sigma_j*scale*log2e
-    __shared__ __attribute__((aligned(16))) int s_vote[2][4];                // restart votes [block & 1][wave]
+    __shared__ __attribute__((aligned(16))) int s_vote[4];                   // restart votes per wave
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
     const int hg = wv >> 1, dh = wv & 1;                             // head group, dim half
@@ -192,9 +192,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     // bf16 P and the fp32 sums hold exactly enough, so the 128 fp32
     // accumulators per lane are never rescaled inside the loop. A block that
     // overshoots by more makes the workgroup redo the query with the larger
-    // reference: every wave writes its vote on block n to s_vote[n & 1][wave]
-    // (no branch, no clearing) and all waves read the four votes behind the
-    // next barrier.
+    // reference. Each wave ORs its votes in a register and posts them to
+    // s_vote at the end of a chunk of the index list; until then exponents
+    // are clamped to 2^kClampLog2, which keeps every sum finite.
     float m_run = -INFINITY, l_run = 0.f;       // head `col`, this lane's keys
     float m_seen = -INFINITY;                   // largest block max of head `col` seen
     f32x16 o[kVHalf / 32];
@@ -205,8 +205,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const int qk_swz = swz<FP8>(qk_row);
     int parity = 0;
     int nblk_seen = 0;                           // blocks processed in this attempt
-    auto voted = [&](int n) {                    // any wave's vote on block n
-        const int4 v = *(const int4 *)&s_vote[n & 1][0];
+    auto voted = [&]() {                         // any wave's posted vote
+        const int4 v = *(const int4 *)&s_vote[0];
         return (v.x | v.y | v.z | v.w) != 0;
     };
 
@@ -326,6 +326,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     for (int nb = 0; nb < kVHalf / 32; ++nb) o[nb] = zero16();
     l_run = 0.f;
     bool redo = false;
+    bool my_vote = false;                        // wave-uniform
     for (int c0 = 0; c0 < n_keys && !redo; c0 += chunk_len) {
         const int cn = min(chunk_len, n_keys - c0);               // entries in this chunk
         const int n_blk = (cn + kBlk - 1) / kBlk;
@@ -358,6 +359,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         // DMA one block into ring slot `slot`: this wave issues instructions
         // wv, wv+4, ... (16-byte slot sidx = ins*64 + lane holds logical chunk
         // dma_lc[u] of block row dma_r[u]); row offsets stay 32-bit.
+        // The rows of all of this wave's instructions are looked up first (one
+        // LDS wait); only the last instruction may be skipped, on SCC.
         auto issue = [&](int blk, int slot) {
             uint8_t *dst = ring + slot * kBlockBytes;
             int j[kDmaIns];
@@ -365,7 +368,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             for (int u = 0; u < kDmaIns; ++u) j[u] = max(row_of(blk * kBlk + dma_r[u]), 0);
 #pragma unroll
             for (int u = 0; u < kDmaIns; ++u) {
-                if (4 * u + 3 < kDma || wv + 4 * u < kDma) {             // compile-time true but for the last
+                if (4 * u + 3 < kDma || wv + 4 * u < kDma) {      // compile-time true but for the last
                     const uint32_t off = (uint32_t)j[u] * (uint32_t)a.kv_stride + (uint32_t)dma_lc[u];
                     dma16(kvq + off, dst + (wv + 4 * u) * 1024);
                 }
@@ -384,11 +387,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             // R-1 blocks were issued ahead; block blk+1 must have landed
             wait_vm_blocks<kDma / 4>(R - 3);
             lds_barrier();               // blk+1 landed everywhere; partials of blk written
-            if (nblk_seen > 0 && voted(nblk_seen - 1)) {            // uniform
-                redo = true;
-                break;
-            }
-            const int vp = nblk_seen & 1;
             issue(blk + R - 1, (blk + R - 1) % R);        // into the slot of block blk-1
             f32x16 s = s_own;
             add_partial(s, parity);
@@ -427,7 +425,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             mx = fmaxf(mx, xor32(mx));
             m_seen = fmaxf(m_seen, mx);
             if (m_run == -INFINITY) m_run = mx;          // first valid keys: nothing to rescale
-            s_vote[vp][wv] = __any(mx > m_run + kHeadroom) ? 1 : 0;   // same value from every lane
+            my_vote |= __any(mx > m_run + kHeadroom);
             const float msub = m_run == -INFINITY ? 0.f : m_run;
             bf16x8 pa[2];
             float psum = 0.f;
@@ -446,10 +444,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         }
         // the tail DMA must land before the ring is reused
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (redo) break;
-        lds_barrier();        // every wave is done with the ring, the table and the votes
+        s_vote[wv] = my_vote ? 1 : 0;                 // same value from every lane
+        lds_barrier();        // every wave is done with the ring and the table; votes posted
+        redo = voted();
+        lds_barrier();        // votes read before the next chunk posts again
     }
-    if (!redo && nblk_seen > 0) redo = voted(nblk_seen - 1);           // last block's vote
     if (!redo) break;
     // redo the query with a larger reference max
     lds_barrier();
