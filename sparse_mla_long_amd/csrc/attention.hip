@@ -38,23 +38,18 @@
 //    the fp32 output accumulators are never rescaled inside the loop.
 //  * FP8 scales sigma_j multiply the logit and the probability, not the row.
 // Entries of the index list outside 0..p_i are masked (probability 0).
+#include "attn_common.h"
 #include "common.h"
 #include "kernels.h"
 
 namespace mla {
 namespace {
 
-constexpr int kThreads = 256;              // 4 waves: (head group, dim half)
-constexpr int kBlk = 32;                    // keys per block
-constexpr int kQK = 576, kV = 512;
-constexpr int kQKHalf = kQK / 2, kVHalf = kV / 2;
-constexpr float kHeadroom = 64.0f;          // log2 headroom of the reference max (see below)
-constexpr float kClampLog2 = 100.0f;        // exponent clamp for a pass that will be redone
-constexpr int O_LD = kVHalf + 8;            // epilogue staging pitch (bf16)
+using namespace attn;
 
-typedef int v2i32 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) bf16x4 *lds_bf16x4_ptr;
-typedef __attribute__((address_space(3))) v2i32 *lds_v2i32_ptr;
+constexpr int kThreads = 256;              // 4 waves: (head group, dim half)
+constexpr int kQKHalf = kQK / 2, kVHalf = kV / 2;
+constexpr int O_LD = kVHalf + 8;            // epilogue staging pitch (bf16)
 
 template <bool FP8> struct Cfg;
 template <> struct Cfg<true> {              // E4M3 rows: 576 B = 36 chunks of 16 dims
@@ -64,50 +59,6 @@ template <> struct Cfg<false> {             // bf16 rows: 1152 B = 72 chunks of 
     static constexpr int kRowBytes = 1152, kChunks = 72, kRing = 3, kIdx = 2048;
 };
 constexpr int kXchgBytes = 2 * 4 * 64 * 16 * 4;   // [parity][wave][4][64 lanes] x f32x4
-
-// Chunk swizzle of LDS row r (XOR on the low chunk bits); rows 0..31 of a block.
-template <bool FP8> __device__ __forceinline__ int swz(int r) {
-    if (FP8) return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
-    return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
-}
-
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-// Wait until at most n*D of this wave's vector-memory operations are in flight
-// (D = the fewest DMA instructions any wave issues per block; waves issuing
-// more wait slightly longer, which is safe).
-template <int D> __device__ __forceinline__ void wait_vm_blocks(int n) {
-    switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * D) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory"); break;
-    }
-}
-
-typedef __attribute__((address_space(3))) void *lds_void_ptr;
-
-// 16 bytes per lane, global -> LDS at (wave-uniform) dst + 16 * lane; completion
-// is tracked with explicit vmcnt waits.
-__device__ __forceinline__ void dma16(const void *src, uint8_t *dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
-}
-
-__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x8 &d, int at) {
-    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-    d[at] = lo[0];
-    d[at + 1] = lo[1];
-    d[at + 2] = hi[0];
-    d[at + 3] = hi[1];
-}
-
-// v of lane l ^ 32, through v_permlane32_swap (no LDS round trip)
-__device__ __forceinline__ float xor32(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
-}
 
 template <bool FP8> constexpr size_t lds_bytes() {          // dynamic part: ring + exchange
     using C = Cfg<FP8>;
@@ -507,7 +458,7 @@ template <bool FP8, bool DENSE> hipError_t launch_t(const AttnArgs &a, hipStream
 hipError_t launch_attention(const AttnArgs &a, bool fp8, hipStream_t s) {
     if (a.batch.total_q <= 0) return hipSuccess;
     const bool dense = a.indices == nullptr;
-    if (fp8) return dense ? launch_t<true, true>(a, s) : launch_t<true, false>(a, s);
+    if (fp8) return launch_attention_fp8_w8(a, s);
     return dense ? launch_t<false, true>(a, s) : launch_t<false, false>(a, s);
 }
 

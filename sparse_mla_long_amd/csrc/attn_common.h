@@ -1,0 +1,65 @@
+// Device helpers shared by the attention kernels: gfx950 LDS DMA, barriers
+// with explicit counter waits, the row swizzle of gathered latent rows, and
+// E4M3 decoding.
+#pragma once
+#include "common.h"
+
+namespace mla {
+namespace attn {
+
+constexpr int kBlk = 32;                    // keys per block
+constexpr int kQK = 576, kV = 512;          // latent row: QK over 576 dims, PV over 512
+constexpr float kHeadroom = 64.0f;          // log2 headroom of the softmax reference max
+constexpr float kClampLog2 = 100.0f;        // exponent clamp for a pass that will be redone
+
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 *lds_bf16x4_ptr;
+typedef __attribute__((address_space(3))) v2i32 *lds_v2i32_ptr;
+
+// Chunk swizzle of LDS row r (XOR on the low chunk bits); rows 0..31 of a block.
+template <bool FP8> __device__ __forceinline__ int swz(int r) {
+    if (FP8) return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+    return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Wait until at most n*D of this wave's vector-memory operations are in flight
+// (D = the fewest DMA instructions any wave issues per block; waves issuing
+// more wait slightly longer, which is safe).
+template <int D> __device__ __forceinline__ void wait_vm_blocks(int n) {
+    switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * D) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory"); break;
+    }
+}
+
+typedef __attribute__((address_space(3))) void *lds_void_ptr;
+
+// 16 bytes per lane, global -> LDS at (wave-uniform) dst + 16 * lane; completion
+// is tracked with explicit vmcnt waits.
+__device__ __forceinline__ void dma16(const void *src, uint8_t *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x8 &d, int at) {
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    d[at] = lo[0];
+    d[at + 1] = lo[1];
+    d[at + 2] = hi[0];
+    d[at + 3] = hi[1];
+}
+
+// v of lane l ^ 32, through v_permlane32_swap (no LDS round trip)
+__device__ __forceinline__ float xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
+}
+
+
+}  // namespace attn
+}  // namespace mla
