@@ -21,6 +21,8 @@
 //    from the same rows with ds_read_b64_tr_b8 (8 rows of one column per lane).
 //  * Per block: phase A runs the softmax of block b and QK of block b+1,
 //    phase B posts the partials of b+1 and runs PV of b; a barrier ends each.
+//    Phase B also loads the raw K fragments of block b+2, so QK starts on
+//    data already in registers.
 //  * Softmax in base 2 against a reference max per head fixed for the whole
 //    query (the first block's max, shared by the head group's waves). Blocks
 //    whose max exceeds it by more than 2^kHeadroom vote for a redo with a
@@ -88,21 +90,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const int32_t *idx_row = DENSE ? nullptr : a.indices + (int64_t)qi * a.k;
     const uint8_t *kvq = a.kv + kv0 * a.kv_stride;                   // row 0 of this sequence
 
-    // Q^T fragments (B operand): k-step s, lane half g = dims 144dq + 16s + 8g .. +7
+    // Q^T fragments (B operand) over the wave's dims 144dq .. +143 = logical
+    // chunks 9dq .. 9dq+8. k-steps 2p, 2p+1 (p < 4): lane half g takes chunk
+    // 9dq + 2p + g, dims 0..7 then 8..15 of it, so a lane reads whole 16-byte
+    // chunks (conflict-free); k-step 8: chunk 9dq + 8, lane half g its dims 8g ...
     const int head = 32 * hg + col;
     bf16x8 qf[kSteps];
     {
         const bool hv = head < H;
-        const __bf16 *qrow = a.q + ((int64_t)qi * H + (hv ? head : 0)) * kQK + kQKQ * dq + 8 * g;
+        const __bf16 *qrow = a.q + ((int64_t)qi * H + (hv ? head : 0)) * kQK + kQKQ * dq;
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
-            const bf16x8 v = *(const bf16x8 *)(qrow + 16 * s);
+            const int d0 = s < 8 ? 16 * (2 * (s >> 1) + g) + 8 * (s & 1) : 128 + 8 * g;
+            const bf16x8 v = *(const bf16x8 *)(qrow + d0);
             qf[s] = hv ? v : zero_bf16x8();
         }
-        // settle the loads before the loop, whose waits also count the ring DMA
+    }
+    // the Q loads stay in flight through the first chunk's table build; they
+    // are settled before the block loop, whose waits also count the ring DMA
+    auto settle_q = [&]() {
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) asm volatile("" ::"v"(qf[s]));
-    }
+    };
 
     // per-lane DMA slot constants: instruction wv + 8u, 16-byte slot ins*64 + lane
     int dma_r[kDmaIns], dma_lc[kDmaIns];
@@ -123,23 +132,42 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     f32x16 o[kVQ / 32];
     const float inv_c = 1.0f / a.scale_log2;     // table multiplier -> sigma_j
 
-    auto qk = [&](const uint8_t *kb) -> f32x16 {
-        f32x16 s = zero16();
-        const uint8_t *krow = kb + qk_row * kRowBytes + 8 * g;
+    // K fragments of QK are loaded raw (E4M3) one phase ahead of their MFMAs.
+    struct KRaw {
+        u32x4 c[4];
+        uint2 last;
+    };
+    struct VRaw {
+        v2i32 w[kVQ / 32][2];
+    };
+    // QK of one ring slot over the wave's dims (k-steps 2p, 2p+1: chunk
+    // 9dq + 2p + g; k-step 8: chunk 9dq + 8, bytes 8g ..)
+    auto k_load = [&](const uint8_t *kb, KRaw &kr) {
+        const uint8_t *krow = kb + qk_row * kRowBytes;
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
-            const int c = 9 * dq + st;                               // logical chunk
-            const uint2 raw = *(const uint2 *)(krow + 16 * (c ^ qk_sw));
-            bf16x8 k8;
-            fp8x4_to_bf16(raw.x, k8, 0);
-            fp8x4_to_bf16(raw.y, k8, 4);
-            s = mfma32x32x16(k8, qf[st], s);
+        for (int p = 0; p < 4; ++p) kr.c[p] = *(const u32x4 *)(krow + 16 * ((9 * dq + 2 * p + g) ^ qk_sw));
+        kr.last = *(const uint2 *)(krow + 16 * ((9 * dq + 8) ^ qk_sw) + 8 * g);
+    };
+    auto k_mma = [&](const KRaw &kr) -> f32x16 {
+        f32x16 s = zero16();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            bf16x8 k0, k1;
+            fp8x4_to_bf16(kr.c[p][0], k0, 0);
+            fp8x4_to_bf16(kr.c[p][1], k0, 4);
+            fp8x4_to_bf16(kr.c[p][2], k1, 0);
+            fp8x4_to_bf16(kr.c[p][3], k1, 4);
+            s = mfma32x32x16(k0, qf[2 * p], s);
+            s = mfma32x32x16(k1, qf[2 * p + 1], s);
         }
-        return s;
+        bf16x8 k8;
+        fp8x4_to_bf16(kr.last.x, k8, 0);
+        fp8x4_to_bf16(kr.last.y, k8, 4);
+        return mfma32x32x16(k8, qf[8], s);
     };
     // O[:, 128dq ..] += P V; k-step t = LDS rows 16g + 8t .. +7. A lane supplies
     // row 16g + 8t + (gi >> 1), bytes 8 (gi & 1).. of logical chunk 8dq + 2nb + hh.
-    auto pv = [&](const uint8_t *kb, const bf16x8 *pa) {
+    auto v_load = [&](const uint8_t *kb, VRaw &vr) {
         const int gi = lane & 15, hh = (lane >> 4) & 1;
         const int sw = ((gi >> 3) & 1) | (g << 1);
         const int L1 = 8 * dq + hh;
@@ -148,12 +176,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 #pragma unroll
         for (int nb = 0; nb < kVQ / 32; ++nb)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const v2i32 w8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            for (int t = 0; t < 2; ++t)
+                vr.w[nb][t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                     (lds_v2i32_ptr)(((nb & 1) ? vo : ve) + 64 * (nb >> 1) + 8 * kRowBytes * t));
+    };
+    auto v_mma = [&](const VRaw &vr, const bf16x8 *pa) {
+#pragma unroll
+        for (int nb = 0; nb < kVQ / 32; ++nb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
                 bf16x8 vb;
-                fp8x4_to_bf16((uint32_t)w8[0], vb, 0);
-                fp8x4_to_bf16((uint32_t)w8[1], vb, 4);
+                fp8x4_to_bf16((uint32_t)vr.w[nb][t][0], vb, 0);
+                fp8x4_to_bf16((uint32_t)vr.w[nb][t][1], vb, 4);
                 o[nb] = mfma32x32x16(pa[t], vb, o[nb]);
             }
     };
@@ -214,6 +248,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             s_mul[e] = v ? *(const float *)(a.kv_scale + (kv0 + j) * a.scale_stride) * a.scale_log2 : 0.f;
         }
         __syncthreads();
+        settle_q();
         // entries past the chunk (the pipeline's tail) read row 0, which is
         // always present and whose result is unused
         auto issue = [&](int blk, int slot) {
@@ -234,13 +269,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             }
         };
 
-        // prologue: blocks 0..kRing-2 in flight; partial logits of block 0
+        // prologue: blocks 0..kRing-2 in flight; partial logits of block 0;
+        // K fragments of block 1
 #pragma unroll
         for (int p = 0; p < kRing - 1; ++p) issue(p, p);
-        wait_vm_blocks<kDma / kWaves>(kRing - 2);
+        wait_vm_blocks<kDma / kWaves>(kRing - 2);            // block 0 landed
         lds_barrier();
-        put_partial(qk(ring));
+        KRaw kr;
+        k_load(ring, kr);
+        put_partial(k_mma(kr));
+        wait_vm_blocks<kDma / kWaves>(kRing - 3);            // block 1 landed
         lds_barrier();
+        k_load(ring + kBlockBytes, kr);
         if (need_init) {
             // reference max: the first block's max over the head group's lanes
             float t[4], sg[4];
@@ -253,7 +293,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         }
 
         for (int blk = 0; blk < n_blk; ++blk) {
-            wait_vm_blocks<kDma / kWaves>(kRing - 3);   // block blk+1 landed
             lds_barrier();           // partials of blk posted; PV of blk-1 done everywhere
             issue(blk + kRing - 1, (blk + kRing - 1) % kRing);     // into the slot of blk-1
 
@@ -273,15 +312,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 pw[j] = (__bf16)(p * sg[j]);
             }
             *(bf16x4 *)p_out = pw;
-            const f32x16 s_next = qk(ring + ((blk + 1) % kRing) * kBlockBytes);
+            const f32x16 s_next = k_mma(kr);
+            wait_vm_blocks<kDma / kWaves>(kRing - 3);   // block blk+2 landed
             lds_barrier();           // probabilities of blk posted; partials of blk read
 
-            // ---- phase B: post the partials of blk+1, PV of blk
+            // ---- phase B: post the partials of blk+1, K of blk+2, PV of blk
             put_partial(s_next);
+            k_load(ring + ((blk + 2) % kRing) * kBlockBytes, kr);
             bf16x8 pa[2];
             pa[0] = *(const bf16x8 *)p_in;
             pa[1] = *(const bf16x8 *)(p_in + 2 * 32 * 8);
-            pv(ring + (blk % kRing) * kBlockBytes, pa);
+            VRaw vr;
+            v_load(ring + (blk % kRing) * kBlockBytes, vr);
+            v_mma(vr, pa);
         }
         // the tail DMA must land before the ring is reused
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
