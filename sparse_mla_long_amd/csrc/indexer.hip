@@ -9,9 +9,11 @@
 // with the 64 indexer heads as two 32-row MFMA blocks held in registers for
 // the whole sweep. In the 32x32 accumulator layout a lane owns one key column
 // and 16 head rows, so ReLU, the w-weighting and most of the head reduction
-// stay in the lane; one cross-lane add finishes it. Keys stream through a
-// double-buffered 64-key LDS tile shared by the eight waves; tiles wholly
-// above a query's position are skipped, not masked.
+// stay in the lane; one cross-lane add finishes it. Keys stream HBM -> LDS by
+// direct DMA through a ring of 64-key tiles shared by the eight waves, three
+// tiles ahead, 16-byte chunks XOR-swizzled by key row so the B-operand reads
+// are bank-conflict-free; one barrier per tile.
+#include "attn_common.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -19,16 +21,19 @@ namespace mla {
 namespace {
 
 constexpr int kIdxThreads = kIdxQueriesPerBlock * kWave;  // one wave per query
+constexpr int kIdxWaves = kIdxQueriesPerBlock;
 constexpr int kKeyTile = 64;
+constexpr int kTileRing = 4;
 
 template <int KS, int MB>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     constexpr int DI = KS * 16;          // indexer head dim
-    constexpr int LDK = DI + 8;          // LDS row pitch in bf16 (+16 B avoids bank aliasing)
     constexpr int CPR = DI / 8;          // 16-byte chunks per key row
-    constexpr int PER_T = kKeyTile * CPR / kIdxThreads;
-    static_assert(PER_T >= 1 && kKeyTile * CPR % kIdxThreads == 0, "tile split");
-    __shared__ __attribute__((aligned(16))) __bf16 ktile[2][kKeyTile * LDK];
+    constexpr int kTileBytes = kKeyTile * DI * 2;
+    constexpr int kDma = kTileBytes / 1024;                 // DMA instructions per tile
+    constexpr int kDmaPerWave = kDma / kIdxWaves;
+    static_assert(kDmaPerWave >= 1 && kDma % kIdxWaves == 0, "tile split");
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[kTileRing][kTileBytes];
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
 
@@ -76,65 +81,75 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         }
     }
 
-    u32x4 stage[PER_T];
-    auto load_tile = [&](int t0) {
+    // DMA slots: instruction wv + 8u of a tile; 16-byte slot sidx = ins*64 + lane
+    // holds logical chunk (sidx % CPR) ^ (row & (CPR-1)) of tile row sidx / CPR
+    int dma_r[kDmaPerWave], dma_c[kDmaPerWave];
 #pragma unroll
-        for (int c = 0; c < PER_T; ++c) {
-            const int id = threadIdx.x + c * kIdxThreads;
-            const int r = id / CPR, cc = id % CPR;
-            const int j = t0 + r;
-            if (j <= pmax) {
-                stage[c] = *(const u32x4 *)(a.k_idx + (kv0 + j) * DI + cc * 8);
-            } else {
-                stage[c] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
+    for (int u = 0; u < kDmaPerWave; ++u) {
+        const int sidx = (wv + kIdxWaves * u) * 64 + lane;
+        dma_r[u] = sidx / CPR;
+        dma_c[u] = (sidx % CPR) ^ (dma_r[u] & (CPR - 1));
+    }
+    // rows past the block's last position read that row instead (results unused)
+    auto issue = [&](int t, int slot) {
 #pragma unroll
-        for (int c = 0; c < PER_T; ++c) {
-            const int id = threadIdx.x + c * kIdxThreads;
-            const int r = id / CPR, cc = id % CPR;
-            *(u32x4 *)(&ktile[buf][r * LDK + cc * 8]) = stage[c];
+        for (int u = 0; u < kDmaPerWave; ++u) {
+            const int j = min(t * kKeyTile + dma_r[u], pmax);
+            attn::dma16(a.k_idx + (kv0 + j) * DI + 8 * dma_c[u], &ktile[slot][(wv + kIdxWaves * u) * 1024]);
         }
     };
 
     const int n_tiles = pmax / kKeyTile + 1;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
     float *srow = a.scores + (int64_t)qi * a.ld;
+    // Software pipeline over 32-key sub-tiles: the MFMAs of sub-tile u run in
+    // the same straight-line block as the epilogue (ReLU, w, head sum) of
+    // sub-tile u-1. Sub-tiles past this query's position compute on later or
+    // repeated keys and are not stored.
+    f32x16 prev[MB];
+    int prev_j0 = -1;                                   // first key of the pending sub-tile
+    auto epilogue = [&](const f32x16 *acc, int j0) {
+        // four independent partial sums (a single chain would serialise
+        // 32 dependent FMAs), then the other lane half's rows
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ps[e & 3] += wr[mb][e] * fmaxf(acc[mb][e], 0.f);
+        float sc = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
+        sc += __uint_as_float(g ? r[0] : r[1]);
+        const int j = j0 + col;
+        if (g == 0 && j <= pos) srow[j] = sc;
+    };
+#pragma unroll
+    for (int p = 0; p < kTileRing - 1; ++p) issue(p, p);
     for (int t = 0; t < n_tiles; ++t) {
         const int t0 = t * kKeyTile;
-        if (t + 1 < n_tiles) load_tile(t0 + kKeyTile);
-        const __bf16 *kt = ktile[t & 1];
+        attn::wait_vm_blocks<kDmaPerWave>(kTileRing - 2);   // tile t landed (this wave's part)
+        attn::lds_barrier();                                 // ... everywhere; tile t-1 done
+        issue(t + kTileRing - 1, (t + kTileRing - 1) % kTileRing);
+        const uint8_t *kt = ktile[t % kTileRing];
 #pragma unroll
         for (int s = 0; s < kKeyTile / 32; ++s) {
-            const int j0 = t0 + 32 * s;
-            if (j0 <= pos) {                           // wave-uniform causal skip
-                f32x16 acc[MB];
+            f32x16 acc[MB];
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
-                const __bf16 *krow = kt + (32 * s + col) * LDK + 8 * g;
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
+            const int row = 32 * s + col;
+            const uint8_t *krow = kt + row * (DI * 2);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 bk = *(const bf16x8 *)(krow + 16 * ks);
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 bk = *(const bf16x8 *)(krow + 16 * ((2 * ks + g) ^ (row & (CPR - 1))));
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(qf[mb][ks], bk, acc[mb]);
-                }
-                float sc = 0.f;
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) sc += wr[mb][e] * fmaxf(acc[mb][e], 0.f);
-                sc += __shfl_xor(sc, 32);
-                const int j = j0 + col;
-                if (g == 0 && j <= pos) srow[j] = sc;
+                for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(qf[mb][ks], bk, acc[mb]);
             }
+            if (prev_j0 >= 0) epilogue(prev, prev_j0);   // false only for the very first sub-tile
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) prev[mb] = acc[mb];
+            prev_j0 = t0 + 32 * s;
         }
-        if (t + 1 < n_tiles) store_tile((t + 1) & 1);
-        __syncthreads();
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail DMA lands before the LDS is freed
+    epilogue(prev, prev_j0);
 }
 
 template <int KS, int MB>
