@@ -294,7 +294,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 
         for (int blk = 0; blk < n_blk; ++blk) {
             lds_barrier();           // partials of blk posted; PV of blk-1 done everywhere
-            issue(blk + kRing - 1, (blk + kRing - 1) % kRing);     // into the slot of blk-1
 
             // ---- phase A: softmax of block blk (this lane's 4 keys), QK of blk+1
             float t[4], sg[4];
@@ -312,6 +311,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 pw[j] = (__bf16)(p * sg[j]);
             }
             *(bf16x4 *)p_out = pw;
+            // the gather of block blk+kRing-1 into the slot of blk-1 (free since
+            // the barrier) is issued here, after the softmax, where its issue
+            // stalls overlap the other wave's work
+            issue(blk + kRing - 1, (blk + kRing - 1) % kRing);
             const f32x16 s_next = k_mma(kr);
             wait_vm_blocks<kDma / kWaves>(kRing - 3);   // block blk+2 landed
             lds_barrier();           // probabilities of blk posted; partials of blk read
