@@ -89,15 +89,17 @@ def kernel_bytes(wl, kv_dtype: str) -> dict:
 # in the same process (--copy-calibration-mib). The figures are stored with a
 # hash of the kernel's sources and reported only while the sources match.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {"attention": "attention.hip", "indexer": "indexer.hip", "topk": "topk.hip"}
-KERNEL_SYMBOLS = {"attention": "attn_kernel", "indexer": "indexer_kernel", "topk": "topk_kernel"}
+KERNEL_SOURCES = {"attention": ("attention.hip", "attention_w8.hip", "attn_common.h"),
+                  "indexer": ("indexer.hip", "attn_common.h"), "topk": ("topk.hip",)}
+KERNEL_SYMBOLS = {"attention": ("attn_kernel", "attn_w8_kernel"), "indexer": ("indexer_kernel",),
+                  "topk": ("topk_kernel",)}
 COPY_SYMBOL = "copyBuffer"
 
 
 def kernel_source_hash(name: str) -> str:
     csrc = os.path.join(ROOT, "sparse_mla_long_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[name], "common.h", "kernels.h"):
+    for f in (*KERNEL_SOURCES[name], "common.h", "kernels.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -123,8 +125,9 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: st
         factor = n / (kib * 1024.0)
         rec[key + "_factor"] = factor
         rec[key + "_copy_kib"] = kib
-        for name, sym in KERNEL_SYMBOLS.items():
-            vals = [float(r["Counter_Value"]) for r in rows if sym in r["Kernel_Name"]]
+        for name, syms in KERNEL_SYMBOLS.items():
+            vals = [float(r["Counter_Value"]) for r in rows
+                    if any(sym + "<" in r["Kernel_Name"] or sym + "(" in r["Kernel_Name"] for sym in syms)]
             if vals:
                 d = rec["kernels"].setdefault(name, {"source_hash": kernel_source_hash(name)})
                 d[key + "_kib_avg"] = float(np.mean(vals))
@@ -182,11 +185,15 @@ def cpu_baseline(inp, wl, budget_s: float = 12.0, seed: int = 7) -> dict:
         return dt, float(((p + 1) * fl_pair_i + sel * fl_pair_a).sum())
 
     oracle.lib()
-    rows = np.sort(rng.choice(wl.total_q, 8, replace=False))
-    dt, fl = run(rows)                                 # calibration sample
-    n = int(min(wl.total_q, max(8, 8 * budget_s / max(dt, 1e-3))))
-    rows = np.sort(rng.choice(wl.total_q, n, replace=False))
-    dt, fl = run(rows)
+    # grow the sample until it takes about budget_s (small samples are
+    # dominated by fixed costs, so one calibration step undershoots)
+    n = 8
+    while True:
+        rows = np.sort(rng.choice(wl.total_q, n, replace=False))
+        dt, fl = run(rows)
+        if dt >= 0.6 * budget_s or n >= wl.total_q:
+            break
+        n = int(min(wl.total_q, max(2 * n, n * budget_s / max(dt, 1e-3))))
     total_fl = sum(workload_flops(wl)[k] for k in ("indexer", "attention"))
     t_full = dt * total_fl / fl
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))

@@ -1,4 +1,5 @@
-// Absorbed (MQA-form) MLA attention over selected latent rows.
+// Absorbed (MQA-form) MLA attention over bf16 latent rows (FP8 rows use the
+// eight-wave kernel of attention_w8.hip).
 //
 // Every token has one latent row of 576 values (512 latent + 64 rope) shared
 // by all heads; a query's heads attend with QK over all 576 dims and PV over
@@ -14,29 +15,27 @@
 // order, so both hold identical logits and run the same softmax.
 //
 //  * Gather: rows move HBM -> LDS with global_load_lds_dwordx4 (each lane's
-//    16 bytes land at LDS base + 16*lane) through a ring of 5 (FP8) or 3
-//    (bf16) blocks. No registers hold rows in flight; completion is tracked
-//    with explicit vmcnt waits. Key indices, FP8 multipliers and mask biases
-//    are copied to LDS per chunk of the index list before its blocks.
-//  * Rows keep their storage type in LDS (E4M3 codes or bf16), 16-byte chunks
-//    XOR-swizzled per row so both read patterns below are bank-conflict-free.
+//    16 bytes land at LDS base + 16*lane) through a ring of 3 blocks. No
+//    registers hold rows in flight; completion is tracked with explicit vmcnt
+//    waits. Key indices and mask biases of a listed query are copied to LDS
+//    per chunk of the index list before its blocks.
+//  * 16-byte chunks are XOR-swizzled per row so both read patterns below are
+//    bank-conflict-free.
 //  * QK: S^T[key x head] = K[key x dims] . Q^T[dims x head] on 32x32x16 bf16
 //    MFMA; the wave's Q^T fragments stay in registers for the whole query.
-//    FP8 K is decoded to bf16 on the fly (exact: E4M3 values are bf16
-//    representable). Accumulator row m reads LDS row 16*((m>>2)&1) +
-//    4*(m>>3) + (m&3), so lane half g of the 32x32 accumulator holds LDS rows
-//    16g..16g+15 of the block, in order.
+//    Accumulator row m reads LDS row 16*((m>>2)&1) + 4*(m>>3) + (m&3), so
+//    lane half g of the 32x32 accumulator holds LDS rows 16g..16g+15 of the
+//    block, in order.
 //  * PV: O[head x dim] += P[head x key] . V[key x dim]: the accumulator above
 //    already is P in the A-operand layout (k-step t = LDS rows 16g+8t..+7), so
 //    P never leaves registers. V is read key-major from the same LDS rows with
-//    the gfx950 transpose reads: ds_read_b64_tr_b8 for E4M3 (a lane receives 8
-//    rows of one column) and ds_read_b64_tr_b16 for bf16 (4 rows).
+//    the gfx950 transpose read ds_read_b64_tr_b16 (a lane receives 4 rows of
+//    one column).
 //  * Software pipeline, one barrier per block: iteration b computes the
 //    partial logits of block b+1 while it runs the softmax and PV of block b;
 //    the partial logits cross to the partner wave behind the next barrier.
 //  * Softmax in base 2 against a fixed reference max per head (see below), so
 //    the fp32 output accumulators are never rescaled inside the loop.
-//  * FP8 scales sigma_j multiply the logit and the probability, not the row.
 // Entries of the index list outside 0..p_i are masked (probability 0).
 #include "attn_common.h"
 #include "common.h"
@@ -51,34 +50,21 @@ constexpr int kThreads = 256;              // 4 waves: (head group, dim half)
 constexpr int kQKHalf = kQK / 2, kVHalf = kV / 2;
 constexpr int O_LD = kVHalf + 8;            // epilogue staging pitch (bf16)
 
-template <bool FP8> struct Cfg;
-template <> struct Cfg<true> {              // E4M3 rows: 576 B = 36 chunks of 16 dims
-    static constexpr int kRowBytes = 576, kChunks = 36, kRing = 5, kIdx = 2048;
-};
-template <> struct Cfg<false> {             // bf16 rows: 1152 B = 72 chunks of 8 dims
-    static constexpr int kRowBytes = 1152, kChunks = 72, kRing = 3, kIdx = 2048;
-};
+constexpr int kRowBytes = 1152, kChunks = 72;   // bf16 rows: 72 chunks of 8 dims
+constexpr int kRing = 3, kIdx = 2048;
 constexpr int kXchgBytes = 2 * 4 * 64 * 16 * 4;   // [parity][wave][4][64 lanes] x f32x4
 
-template <bool FP8> constexpr size_t lds_bytes() {          // dynamic part: ring + exchange
-    using C = Cfg<FP8>;
-    return (size_t)C::kRing * kBlk * C::kRowBytes + kXchgBytes;
-}
-template <bool FP8> constexpr size_t lds_static_bytes() {   // entry table + votes
-    using C = Cfg<FP8>;
-    return (size_t)C::kIdx * (FP8 ? 12 : 8) + 16;
-}
+constexpr size_t kLdsBytes = (size_t)kRing * kBlk * kRowBytes + kXchgBytes;  // ring + exchange
+constexpr size_t kStaticBytes = (size_t)kIdx * 8 + 16;                        // entry table + votes
 
-// DENSE: no index list (keys 0..p_i). TABLE: an entry table is built per chunk
-// (always for FP8, whose per-row multipliers it holds; for bf16 only when an
-// index list is given).
-template <bool FP8, bool DENSE>
+// DENSE: no index list (keys 0..p_i); otherwise an entry table (row and mask
+// bias) is built per chunk of the list.
+template <bool DENSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void attn_kernel(AttnArgs a) {
-    using C = Cfg<FP8>;
-    constexpr bool TABLE = FP8 || !DENSE;
-    constexpr int R = C::kRing;
-    constexpr int kBlockBytes = kBlk * C::kRowBytes;
+    constexpr bool TABLE = !DENSE;
+    constexpr int R = kRing;
+    constexpr int kBlockBytes = kBlk * kRowBytes;
     constexpr int kDma = kBlockBytes / 1024;                    // 16 B x 64 lanes per DMA
     static_assert(kDma * 1024 == kBlockBytes && kDma >= 16, "DMA split");
     static_assert(R >= 3, "the pipeline needs three ring slots");
@@ -87,10 +73,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     f32x4 *xchg = (f32x4 *)(smem + R * kBlockBytes);                 // partial S^T exchange
     // entry table in its own LDS objects, so LDS reads of it are not ordered
     // behind the in-flight ring DMA
-    constexpr int kTab = TABLE ? C::kIdx : 4;
+    constexpr int kTab = TABLE ? kIdx : 4;
     __shared__ __attribute__((aligned(16))) int32_t s_row[kTab];             // row, or -1
     __shared__ __attribute__((aligned(16))) float s_bias[kTab];              // 0, or -inf if masked
-    __shared__ __attribute__((aligned(16))) float s_mul[FP8 ? C::kIdx : 4];  // sigma_j*scale*log2e
     __shared__ __attribute__((aligned(16))) int s_vote[4];                   // restart votes per wave
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
@@ -105,7 +90,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const int n_keys = DENSE ? pos + 1 : a.k;
     const int32_t *idx_row = DENSE ? nullptr : a.indices + (int64_t)qi * a.k;
     const uint8_t *kvq = a.kv + kv0 * a.kv_stride;                   // row 0 of this sequence
-    const int chunk_len = TABLE ? C::kIdx : n_keys;
+    const int chunk_len = TABLE ? kIdx : n_keys;
 
     // Q^T fragments (B operand) of head 32*hg + col over this wave's 288 dims.
     // k-step 2t+u uses dims 288*dh + 16*(2t+g) + 8u .. +7.
@@ -133,8 +118,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 #pragma unroll
     for (int u = 0; u < kDmaIns; ++u) {
         const int sidx = (wv + 4 * u) * 64 + lane;
-        dma_r[u] = sidx / C::kChunks;
-        dma_lc[u] = 16 * ((sidx % C::kChunks) ^ swz<FP8>(dma_r[u]));
+        dma_r[u] = sidx / kChunks;
+        dma_lc[u] = 16 * ((sidx % kChunks) ^ swz<false>(dma_r[u]));
     }
 
     // Softmax in base 2 against a reference max m_run per head. m_run is set
@@ -149,54 +134,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     float m_run = -INFINITY, l_run = 0.f;       // head `col`, this lane's keys
     float m_seen = -INFINITY;                   // largest block max of head `col` seen
     f32x16 o[kVHalf / 32];
-    const float mul_scale = a.scale_log2;
-    const float inv_c = 1.0f / mul_scale;        // table multiplier -> sigma_j
     // row this lane feeds into the QK A operand: accumulator row m = col
     const int qk_row = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
-    const int qk_swz = swz<FP8>(qk_row);
+    const int qk_swz = swz<false>(qk_row);
     int parity = 0;
-    int nblk_seen = 0;                           // blocks processed in this attempt
     auto voted = [&]() {                         // any wave's posted vote
         const int4 v = *(const int4 *)&s_vote[0];
         return (v.x | v.y | v.z | v.w) != 0;
     };
 
     // ---- partial S^T = K Q^T of one ring slot over this wave's 288 dims. The
-    // XOR swizzle only touches the low chunk bits, so (L + 4m) ^ sw ==
-    // (L ^ sw) + 4m (FP8; 8m for bf16): a few per-lane bases plus immediate
-    // offsets address every k-step.
-    // ---- partial S^T = K Q^T of one ring slot over this wave's 288 dims. The
-    // XOR swizzle only touches the low chunk bits, so (L + 4m) ^ sw ==
-    // (L ^ sw) + 4m (FP8; 8m for bf16): a few per-lane bases plus immediate
-    // offsets address every k-step.
+    // XOR swizzle only touches the low chunk bits, so (L + 8m) ^ sw ==
+    // (L ^ sw) + 8m: four per-lane bases plus immediate offsets address every
+    // k-step.
     auto qk = [&](const uint8_t *kb) -> f32x16 {
         f32x16 s = zero16();
-        const uint8_t *krow = kb + qk_row * C::kRowBytes;
-        if (FP8) {
-            const uint8_t *ke = krow + 16 * ((18 * dh + g) ^ qk_swz);
-            const uint8_t *ko = krow + 16 * ((18 * dh + g + 2) ^ qk_swz);
+        const uint8_t *krow = kb + qk_row * kRowBytes;
+        const int L0 = 36 * dh + 2 * g;
+        const uint8_t *e0 = krow + 16 * (L0 ^ qk_swz), *e1 = krow + 16 * ((L0 + 1) ^ qk_swz);
+        const uint8_t *o0 = krow + 16 * ((L0 + 4) ^ qk_swz), *o1 = krow + 16 * ((L0 + 5) ^ qk_swz);
 #pragma unroll
-            for (int t = 0; t < kQKHalf / 32; ++t) {
-                const u32x4 raw = *(const u32x4 *)(((t & 1) ? ko : ke) + 64 * (t >> 1));
-                bf16x8 k0, k1;
-                fp8x4_to_bf16(raw[0], k0, 0);
-                fp8x4_to_bf16(raw[1], k0, 4);
-                fp8x4_to_bf16(raw[2], k1, 0);
-                fp8x4_to_bf16(raw[3], k1, 4);
-                s = mfma32x32x16(k0, qf[2 * t], s);
-                s = mfma32x32x16(k1, qf[2 * t + 1], s);
-            }
-        } else {
-            const int L0 = 36 * dh + 2 * g;
-            const uint8_t *e0 = krow + 16 * (L0 ^ qk_swz), *e1 = krow + 16 * ((L0 + 1) ^ qk_swz);
-            const uint8_t *o0 = krow + 16 * ((L0 + 4) ^ qk_swz), *o1 = krow + 16 * ((L0 + 5) ^ qk_swz);
-#pragma unroll
-            for (int t = 0; t < kQKHalf / 32; ++t) {
-                const bf16x8 k0 = *(const bf16x8 *)(((t & 1) ? o0 : e0) + 128 * (t >> 1));
-                const bf16x8 k1 = *(const bf16x8 *)(((t & 1) ? o1 : e1) + 128 * (t >> 1));
-                s = mfma32x32x16(k0, qf[2 * t], s);
-                s = mfma32x32x16(k1, qf[2 * t + 1], s);
-            }
+        for (int t = 0; t < kQKHalf / 32; ++t) {
+            const bf16x8 k0 = *(const bf16x8 *)(((t & 1) ? o0 : e0) + 128 * (t >> 1));
+            const bf16x8 k1 = *(const bf16x8 *)(((t & 1) ? o1 : e1) + 128 * (t >> 1));
+            s = mfma32x32x16(k0, qf[2 * t], s);
+            s = mfma32x32x16(k1, qf[2 * t + 1], s);
         }
         return s;
     };
@@ -205,54 +167,34 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     // t or on the N-block, so per-lane bases plus immediates address them all.
     auto pv = [&](const uint8_t *kb, const bf16x8 *pa) {
         const int gi = lane & 15, hh = (lane >> 4) & 1;
-        if (FP8) {
-            // lane supplies row 16g + 8t + (gi >> 1), bytes 8*(gi & 1).. of
-            // logical chunk 16*dh + 2*nb + hh
-            const int sw = ((gi >> 3) & 1) | (g << 1);
-            const int L1 = 16 * dh + hh;
-            const uint8_t *rb = kb + (16 * g + (gi >> 1)) * C::kRowBytes + 8 * (gi & 1);
-            const uint8_t *ve = rb + 16 * (L1 ^ sw), *vo = rb + 16 * ((L1 + 2) ^ sw);
+        // lane supplies row 16g + 8t + 4v + (gi >> 2), dims 4*(gi & 3).. of the
+        // N-block's 16-dim group; logical chunk 32*dh + 4*nb + 2*hh + ((gi&3)>>1)
+        const int L2 = 32 * dh + 2 * hh + ((gi & 3) >> 1);
+        const uint8_t *vb0[2][2];
 #pragma unroll
-            for (int nb = 0; nb < kVHalf / 32; ++nb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const v2i32 w8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (lds_v2i32_ptr)(((nb & 1) ? vo : ve) + 64 * (nb >> 1) + 8 * C::kRowBytes * t));
-                    bf16x8 vb;
-                    fp8x4_to_bf16((uint32_t)w8[0], vb, 0);
-                    fp8x4_to_bf16((uint32_t)w8[1], vb, 4);
-                    o[nb] = mfma32x32x16(pa[t], vb, o[nb]);
-                }
-        } else {
-            // lane supplies row 16g + 8t + 4v + (gi >> 2), dims 4*(gi & 3).. of
-            // the N-block's 16-dim group; logical chunk 32*dh + 4*nb + 2*hh + ((gi&3)>>1)
-            const int L2 = 32 * dh + 2 * hh + ((gi & 3) >> 1);
-            const uint8_t *vb0[2][2];
-#pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                const int sw = (2 * v + (gi >> 3)) | (g << 2);
-                const uint8_t *rb = kb + (16 * g + 4 * v + (gi >> 2)) * C::kRowBytes + 8 * (gi & 1);
-                vb0[v][0] = rb + 16 * (L2 ^ sw);
-                vb0[v][1] = rb + 16 * ((L2 + 4) ^ sw);
-            }
-#pragma unroll
-            for (int nb = 0; nb < kVHalf / 32; ++nb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    bf16x4 w16[2];
-#pragma unroll
-                    for (int v = 0; v < 2; ++v)
-                        w16[v] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                            (lds_bf16x4_ptr)(vb0[v][nb & 1] + 128 * (nb >> 1) + 8 * C::kRowBytes * t));
-                    bf16x8 vb;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        vb[e] = w16[0][e];
-                        vb[4 + e] = w16[1][e];
-                    }
-                    o[nb] = mfma32x32x16(pa[t], vb, o[nb]);
-                }
+        for (int v = 0; v < 2; ++v) {
+            const int sw = (2 * v + (gi >> 3)) | (g << 2);
+            const uint8_t *rb = kb + (16 * g + 4 * v + (gi >> 2)) * kRowBytes + 8 * (gi & 1);
+            vb0[v][0] = rb + 16 * (L2 ^ sw);
+            vb0[v][1] = rb + 16 * ((L2 + 4) ^ sw);
         }
+#pragma unroll
+        for (int nb = 0; nb < kVHalf / 32; ++nb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                bf16x4 w16[2];
+#pragma unroll
+                for (int v = 0; v < 2; ++v)
+                    w16[v] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_bf16x4_ptr)(vb0[v][nb & 1] + 128 * (nb >> 1) + 8 * kRowBytes * t));
+                bf16x8 vb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vb[e] = w16[0][e];
+                    vb[4 + e] = w16[1][e];
+                }
+                o[nb] = mfma32x32x16(pa[t], vb, o[nb]);
+            }
     };
     f32x4 *xmine = xchg + (wv * 4) * 64 + lane;           // + parity * 16 * 64
     const f32x4 *xother = xchg + ((wv ^ 1) * 4) * 64 + lane;
@@ -283,8 +225,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         const int n_blk = (cn + kBlk - 1) / kBlk;
         const int n_ent = n_blk * kBlk;
         if (TABLE) {
-            // entry table of the chunk: row (or -1 when masked), mask bias and
-            // FP8 multiplier
+            // entry table of the chunk: row (or -1 when masked) and mask bias
             for (int e = tid; e < n_ent; e += kThreads) {
                 const int ge = c0 + e;
                 int j = -1;
@@ -292,9 +233,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 const bool v = j >= 0 && j <= pos;
                 s_row[e] = v ? j : -1;
                 s_bias[e] = v ? 0.f : -INFINITY;
-                if (FP8)
-                    s_mul[e] = v ? *(const float *)(a.kv_scale + (kv0 + j) * a.scale_stride) * mul_scale
-                                 : 0.f;
             }
             __syncthreads();
         }
@@ -349,28 +287,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             // LDS row 16g + e
             const int e0 = blk * kBlk + 16 * g;
             float mx = -INFINITY;
-            float sg[16];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                float mu[4], bi[4];
+                float bi[4];
                 if (TABLE) {
                     *(f32x4 *)bi = *(const f32x4 *)&s_bias[e0 + 4 * q4];
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) bi[j] = e0 + 4 * q4 + j < cn ? 0.f : -INFINITY;
                 }
-                if (FP8) {
-                    *(f32x4 *)mu = *(const f32x4 *)&s_mul[e0 + 4 * q4];
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) mu[j] = a.scale_log2;
-                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int e = 4 * q4 + j;
-                    s[e] = fmaf(s[e], mu[j], bi[j]);
+                    s[e] = fmaf(s[e], a.scale_log2, bi[j]);
                     mx = fmaxf(mx, s[e]);
-                    if (FP8) sg[e] = mu[j] * inv_c;
                 }
             }
             mx = fmaxf(mx, xor32(mx));
@@ -384,14 +314,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             for (int e = 0; e < 16; ++e) {
                 const float p = __builtin_amdgcn_exp2f(fminf(s[e] - msub, kClampLog2));
                 psum += p;
-                pa[e >> 3][e & 7] = (__bf16)(FP8 ? p * sg[e] : p);
+                pa[e >> 3][e & 7] = (__bf16)p;
             }
             l_run += psum;
 
             pv(ring + (blk % R) * kBlockBytes, pa);
             parity ^= 1;
             put_partial(s_own, parity);
-            ++nblk_seen;
         }
         // the tail DMA must land before the ring is reused
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -404,7 +333,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     // redo the query with a larger reference max
     lds_barrier();
     m_run = fmaxf(m_run, m_seen);
-    nblk_seen = 0;
     parity = 0;
     lds_barrier();
     }
@@ -438,18 +366,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     }
 }
 
-static_assert(lds_bytes<true>() >= 4 * 32 * O_LD * 2 && lds_bytes<false>() >= 4 * 32 * O_LD * 2,
-              "epilogue staging must fit");
-static_assert(lds_bytes<true>() + lds_static_bytes<true>() <= 160 * 1024 &&
-                  lds_bytes<false>() + lds_static_bytes<false>() <= 160 * 1024,
-              "LDS budget");
+static_assert(kLdsBytes >= 4 * 32 * O_LD * 2, "epilogue staging must fit");
+static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
 
-template <bool FP8, bool DENSE> hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
-    const size_t lds = lds_bytes<FP8>();
-    hipError_t e = hipFuncSetAttribute((const void *)attn_kernel<FP8, DENSE>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+template <bool DENSE> hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
+    hipError_t e = hipFuncSetAttribute((const void *)attn_kernel<DENSE>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_kernel<FP8, DENSE>), dim3(a.batch.total_q), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((attn_kernel<DENSE>), dim3(a.batch.total_q), dim3(kThreads), kLdsBytes, s, a);
     return hipGetLastError();
 }
 
@@ -457,9 +381,8 @@ template <bool FP8, bool DENSE> hipError_t launch_t(const AttnArgs &a, hipStream
 
 hipError_t launch_attention(const AttnArgs &a, bool fp8, hipStream_t s) {
     if (a.batch.total_q <= 0) return hipSuccess;
-    const bool dense = a.indices == nullptr;
     if (fp8) return launch_attention_fp8_w8(a, s);
-    return dense ? launch_t<false, true>(a, s) : launch_t<false, false>(a, s);
+    return a.indices == nullptr ? launch_t<true>(a, s) : launch_t<false>(a, s);
 }
 
 }  // namespace mla
