@@ -89,9 +89,9 @@ def kernel_bytes(wl, kv_dtype: str) -> dict:
 # in the same process (--copy-calibration-mib). The figures are stored with a
 # hash of the kernel's sources and reported only while the sources match.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {"attention": ("attention.hip", "attention_w8.hip", "attn_common.h"),
+KERNEL_SOURCES = {"attention": ("attention.hip", "attention_f8.hip", "attn_common.h"),
                   "indexer": ("indexer.hip", "attn_common.h"), "topk": ("topk.hip",)}
-KERNEL_SYMBOLS = {"attention": ("attn_kernel", "attn_w8_kernel"), "indexer": ("indexer_kernel",),
+KERNEL_SYMBOLS = {"attention": ("attn_kernel", "attn_f8_kernel"), "indexer": ("indexer_kernel",),
                   "topk": ("topk_kernel",)}
 COPY_SYMBOL = "copyBuffer"
 

@@ -1,5 +1,5 @@
 // Absorbed (MQA-form) MLA attention over bf16 latent rows (FP8 rows use the
-// eight-wave kernel of attention_w8.hip).
+// kernel of attention_f8.hip).
 //
 // Every token has one latent row of 576 values (512 latent + 64 rope) shared
 // by all heads; a query's heads attend with QK over all 576 dims and PV over
@@ -381,7 +381,7 @@ template <bool DENSE> hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 
 hipError_t launch_attention(const AttnArgs &a, bool fp8, hipStream_t s) {
     if (a.batch.total_q <= 0) return hipSuccess;
-    if (fp8) return launch_attention_fp8_w8(a, s);
+    if (fp8) return launch_attention_fp8_f8(a, s);
     return a.indices == nullptr ? launch_t<true>(a, s) : launch_t<false>(a, s);
 }
 

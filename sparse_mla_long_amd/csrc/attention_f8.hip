@@ -1,0 +1,473 @@
+// Absorbed (MQA-form) MLA attention over FP8 (E4M3) latent rows: four waves
+// per query, each computing whole 576-dim logits for its own key blocks.
+//
+// Every token has one latent row of 576 values (512 latent + 64 rope) shared
+// by all heads; a query's heads attend with QK over all 576 dims and PV over
+// the first 512 (spke.com GLM-5.3 PCP/DCP article, footnote 1), so one
+// gathered row serves every head (section "PCP"). Blocks of 32 gathered rows
+// land in LDS once and feed QK and PV of all 64 heads.
+//
+// Work split: one query per 256-thread workgroup, one wave per SIMD. Wave w
+// owns head group hg = w & 1 (32 heads) and half = w >> 1. A step moves two
+// blocks (2s, 2s+1): the wave computes logits and softmax of block 2s + half,
+// and PV of both blocks over output dims 256 half .. +255, with the partner
+// wave's probabilities (wave w ^ 2, same heads) taken from LDS.
+//  * QK: S^T[key x head] = K Q^T over all 576 dims on 32x32x64 FP8 MFMA,
+//    K straight from LDS, Q^T as an exact hi + lo pair of E4M3 operands (two
+//    MFMAs per 64 dims); the wave's Q^T operands (144 VGPRs) stay in
+//    registers, so a block's logits need no cross-wave reduction.
+//  * Softmax in registers: accumulator element (i, j) of lane half g is LDS
+//    row 16g + 4i + j of the block (the QK A operand reads rows in that
+//    order), which is the k order PV's A operand wants, so the probabilities
+//    (times the FP8 row scale sigma_j) go straight from the softmax into PV.
+//  * PV: O[head x dim] += P[head x key] V[key x dim] over the wave's 256
+//    dims; V is read key-major with ds_read_b64_tr_b8 (8 rows of one column
+//    per lane). O (32 heads x 256 dims, f32) lives in accumulation registers.
+//    The own block's PV runs before the mid-step barrier that publishes the
+//    probabilities, the partner block's after it.
+//  * Reference max per head shared by both waves of a head group (the max of
+//    the first step's two blocks), so their probabilities and row sums share
+//    one scale; blocks exceeding it by more than 2^kHeadroom vote for a redo
+//    of the query with a larger reference.
+//  * LDS block layout: dims 0..511 of row r at r * 512, 16-byte chunk c at
+//    chunk c ^ sm(r); dims 512..575 at 16384 + r * 64, chunk c ^ st(r). The
+//    swizzles make the QK reads (16 rows, one chunk) and the transposed V
+//    reads (8 rows, two chunks) bank-conflict free, and keep the gather's
+//    per-lane offsets independent of the instruction but for a scalar term.
+//  * The barrier opening a step retires the step before (its ring slots take
+//    the gather of step s+2) and publishes step s, which every wave waited
+//    for on its own DMA counter.
+// Entries of the index list outside 0..p_i are masked (probability 0).
+#include "attn_common.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+namespace {
+
+using namespace attn;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;                   // 256
+constexpr int kRowBytes = 576;                             // E4M3 row
+constexpr int kMainPitch = 512;                            // LDS: dims 0..511 of a row
+constexpr int kTailPitch = 64;                             // LDS: dims 512..575 of a row
+constexpr int kTailBase = kBlk * kMainPitch;               // 16,384
+constexpr int kBlockBytes = kBlk * kRowBytes;              // 18,432
+constexpr int kStepBlocks = 2;                             // one block per wave of a head group
+constexpr int kStepBytes = kStepBlocks * kBlockBytes;
+constexpr int kDmaStep = kStepBytes / 1024 / kWaves;       // 9 DMA instructions per wave and step
+constexpr int kRingSteps = 3;                              // steps resident in LDS
+constexpr int kIdx = 2048;                                 // index-list entries per chunk
+constexpr int kPad = 2 * 64;                               // row-table entries the pipeline tail reads
+constexpr int kPairs = kQK / 32;                           // 16-byte K chunks per lane half
+constexpr int kKB = kQK / 64;                              // QK k-blocks of the FP8 MFMA
+constexpr int kOwn = kV / 64;                              // output tiles (32 dims) per wave
+constexpr int O_LD = 32 * kOwn + 8;                        // epilogue staging pitch (bf16)
+
+constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
+constexpr size_t kStaticBytes = (size_t)kIdx * 12 + kPad * 4 + kWaves * 2 * 64 * 16 + 2 * 2 * 32 * 4 + kWaves * 4;
+static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
+static_assert(kDmaStep * kWaves * 1024 == kStepBytes, "DMA split");
+static_assert(kTailBase + kBlk * kTailPitch == kBlockBytes, "block layout");
+static_assert((size_t)kWaves * 32 * O_LD * 2 <= kLdsBytes, "staging fits the ring");
+
+template <int N> using IC = std::integral_constant<int, N>;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// v_mfma_scale_f32_32x32x64_f8f6f4, both operands E4M3, unit scales. Operand
+// layout (lane l, g = l / 32): A row (l % 32), B column (l % 32), byte p of the
+// 32 holds k = 32g + p; C as the 32x32x16 bf16 MFMA.
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// chunk swizzles of block row r: main part (32 chunks), tail part (4 chunks)
+__device__ __forceinline__ int sm_of(int r) { return ((r & 7) << 1) | ((r >> 4) & 1); }
+__device__ __forceinline__ int st_of(int r) { return ((r >> 2) & 1) | (((r >> 4) & 1) << 1); }
+
+template <bool DENSE>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(1, 1))) void attn_f8_kernel(AttnArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t *ring = smem;
+    // entry table in its own LDS objects, so LDS reads of it are not ordered
+    // behind the in-flight ring DMA
+    __shared__ __attribute__((aligned(16))) int32_t s_row[kIdx + kPad];   // row, or -1
+    __shared__ __attribute__((aligned(16))) float s_bias[kIdx];     // 0, or -inf if masked
+    __shared__ __attribute__((aligned(16))) float s_mul[kIdx];      // sigma_j * scale * log2e
+    __shared__ bf16x8 s_p[kWaves][2][64];                           // probabilities, A-operand order
+    __shared__ float s_x[2][2][32];                                 // [hg][half][head] exchange
+    __shared__ int s_vote[kWaves];
+
+    const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
+    const int hg = wv & 1, half = wv >> 1;
+    const int tid = threadIdx.x;
+    const int qi = a.batch.total_q - 1 - (int)blockIdx.x;
+    const int b = seq_of_row(a.batch.cu_q, a.batch.num_seqs, qi);
+    const int64_t kv0 = a.batch.cu_kv[b];
+    const int L = a.batch.cu_kv[b + 1] - (int)kv0;
+    const int pos = min(a.batch.q_pos[qi], L - 1);
+    const int H = a.n_heads;
+    const int n_keys = DENSE ? pos + 1 : a.k;
+    const int32_t *idx_row = DENSE ? nullptr : a.indices + (int64_t)qi * a.k;
+    const uint8_t *kvq = a.kv + kv0 * a.kv_stride;                   // row 0 of this sequence
+
+    // Q^T fragments (B operand): k-steps 2p, 2p+1 take chunk 2p + g (lane half
+    // g), dims 0..7 then 8..15 of it, matching the K reads below
+    const int head = 32 * hg + col;
+    const bool hv = head < H;
+    // Q^T as two E4M3 operands (B of the 32x32x64 FP8 MFMA): per head, Q is
+    // scaled by 2^sq (its largest |q| lands in [128, 256)) and split into
+    // hi = e4m3(q 2^sq) and lo = e4m3(q 2^sq - hi). A bf16 value has 8
+    // significant bits and the residual is a multiple of its last bit no larger
+    // than half a step of hi, so hi + lo is exact unless lo falls below the
+    // E4M3 subnormal range (elements 2^10 below the head's largest, off by at
+    // most 2^-18 of it). K-block kb (dims of chunks 4kb + g and 4kb + 2 + g for
+    // lane half g) is operand kb; byte order follows the K rows in LDS.
+    i32x8 qh[kKB], ql[kKB];
+    float qinv;                                  // 2^-sq of head `col`
+    {
+        const __bf16 *qrow = a.q + ((int64_t)qi * H + (hv ? head : 0)) * kQK;
+        bf16x8 raw[kPairs][2];
+        float qmax = 0.f;
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const bf16x8 v = *(const bf16x8 *)(qrow + 16 * (2 * p + g) + 8 * e);
+                raw[p][e] = hv ? v : zero_bf16x8();
+#pragma unroll
+                for (int k = 0; k < 8; ++k) qmax = fmaxf(qmax, fabsf((float)raw[p][e][k]));
+            }
+        qmax = fmaxf(qmax, xor32(qmax));
+        const int sq = 8 - __builtin_amdgcn_frexp_expf(qmax);
+        const float qs = __builtin_ldexpf(1.f, sq);
+        qinv = __builtin_ldexpf(1.f, -sq);
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {               // dword d of the pair: dims 4d .. 4d+3
+                float x[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) x[k] = (float)raw[p][d >> 1][4 * (d & 1) + k] * qs;
+                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hi, true);
+                const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+                const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - b0[0], x[1] - b0[1], 0, false);
+                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b1[0], x[3] - b1[1], lo, true);
+                qh[p >> 1][4 * (p & 1) + d] = hi;
+                ql[p >> 1][4 * (p & 1) + d] = lo;
+            }
+    }
+
+    // DMA lane constants. Main instruction k of a block (k < 16) moves rows
+    // 2k + (lane >> 5), physical chunk lane & 31; tail instruction t moves
+    // rows 16t + (lane >> 2), physical tail chunk lane & 3. The logical chunk
+    // each lane fetches is its constant XOR a term of the instruction.
+    const int dma_main = (lane & 31) ^ ((lane >> 5) << 1);
+    const int dma_tail = (lane & 3) ^ ((lane >> 4) & 1);
+
+    // accumulator row m = col of the QK A operand reads LDS row qk_row, so lane
+    // half g of the tile holds LDS rows 16g + 0..15 in element order
+    const int qk_row = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
+    // logical chunk 2p + g of the main part sits at chunk 2p ^ qk_x
+    const int qk_x = g ^ sm_of(qk_row);
+    const int qk_xt = g ^ st_of(qk_row);
+
+    float m_run = -INFINITY, l_run = 0.f;        // head `col`, this lane's keys
+    float m_seen = -INFINITY;
+    f32x16 o[kOwn];
+    const float inv_c = 1.0f / a.scale_log2;     // table multiplier -> sigma_j
+
+    // S^T of one block over all 576 dims, software-pipelined: the K chunk of
+    // pair p + 2 is read while pair p is decoded and multiplied; hook(p) runs
+    // inside pair p (the step's DMA issue is spread over the first pairs)
+    auto qk = [&](const uint8_t *kb, bool mma, auto &&hook) -> f32x16 {
+        if (!mma) {                                  // uniform: hooks only
+#pragma unroll
+            for (int p = 0; p < kPairs; ++p) {
+                hook(p);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return zero16();
+        }
+        const uint8_t *krow = kb + qk_row * kMainPitch;
+        const uint8_t *ktail = kb + kTailBase + qk_row * kTailPitch;
+        auto ld = [&](int p) {
+            if (2 * p < 32)
+                return *(const u32x4 *)(krow + 16 * ((2 * p) & 16) + 16 * (((2 * p) & 15) ^ qk_x));
+            return *(const u32x4 *)(ktail + 16 * ((2 * p - 32) ^ qk_xt));
+        };
+        // k-block kb: pairs 2kb, 2kb+1; its K reads are issued one block ahead
+        u32x4 c0 = ld(0), c1 = ld(1);
+        f32x16 s = zero16();
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) {
+            u32x4 n0 = c0, n1 = c1;
+            if (kb + 1 < kKB) {
+                n0 = ld(2 * kb + 2);
+                n1 = ld(2 * kb + 3);
+            }
+            hook(2 * kb);
+            hook(2 * kb + 1);
+            const i32x8 kf = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3],
+                              (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+            s = mfma_f8(kf, qh[kb], s);
+            s = mfma_f8(kf, ql[kb], s);
+            c0 = n0;
+            c1 = n1;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return s;
+    };
+    // O += P V over the wave's dims; k-step t = LDS rows 16g + 8t .. +7. A lane
+    // supplies row 16g + 8t + (gi >> 1), bytes 8 (gi & 1).. of chunk 2nb + hh
+    // (nb: tile of the wave's dims). Fragment x = 2nb + t of the own block
+    // (x < 16), then of the partner block; the read of x + kVPre overlaps the
+    // MFMA of x.
+    constexpr int kVPre = 4;
+    constexpr int kVX = 2 * kOwn;                                   // fragments per block
+    const int gi = lane & 15;
+    // the lane's rows 16g + 8t + (gi >> 1) share sm = 2 (gi >> 1) + g; logical
+    // chunk 2nb + hh sits at chunk 2nb ^ v_x (within the wave's 256 dims)
+    const int v_x = ((lane >> 4) & 1) ^ (2 * (gi >> 1) + g);
+    auto v_ld = [&](const uint8_t *kb, int x) -> v2i32 {
+        const int nb = (x % kVX) >> 1, t = x & 1;
+        const uint8_t *rb = kb + (x < kVX ? half : 1 - half) * kBlockBytes + 256 * half +
+                            (16 * g + (gi >> 1)) * kMainPitch + 8 * (gi & 1) + 8 * kMainPitch * t;
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_ptr)(rb + 16 * ((2 * nb) ^ v_x)));
+    };
+    // pa: own probabilities; after the own block, `mid` runs (barrier) and
+    // returns the partner's
+    auto pv = [&](const uint8_t *kb, const bf16x8 *pa, v2i32 *w, auto &&mid) {
+        bf16x8 pp[2] = {pa[0], pa[1]};
+#pragma unroll
+        for (int x = 0; x < 2 * kVX; ++x) {
+            if (x == kVX) mid(pp);
+            const v2i32 cur = w[x % kVPre];
+            if (x + kVPre < 2 * kVX) w[x % kVPre] = v_ld(kb, x + kVPre);
+            bf16x8 vb;
+            fp8x4_to_bf16((uint32_t)cur[0], vb, 0);
+            fp8x4_to_bf16((uint32_t)cur[1], vb, 4);
+            const int nb = (x % kVX) >> 1;
+            o[nb] = mfma32x32x16(pp[x & 1], vb, o[nb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // largest value of a head over both waves of the head group (lanes g = 0)
+    auto group_max = [&](float v) -> float {
+        v = fmaxf(v, xor32(v));
+        if (g == 0) s_x[hg][half][col] = v;
+        lds_barrier();
+        const float r = fmaxf(s_x[hg][0][col], s_x[hg][1][col]);
+        lds_barrier();
+        return r;
+    };
+
+    // every row-table entry the gather may read holds -1 or a row of this
+    // sequence before the first chunk's table lands
+    for (int e = tid; e < kIdx + kPad; e += kThreads) s_row[e] = -1;
+
+    bool need_init = true;                        // reference max not yet set (uniform)
+    for (;;) {                                    // attempts: one unless a block overshoots
+#pragma unroll
+    for (int nb = 0; nb < kOwn; ++nb) o[nb] = zero16();
+    l_run = 0.f;
+    bool redo = false;
+    bool my_vote = false;                         // wave-uniform
+    for (int c0 = 0; c0 < n_keys && !redo; c0 += kIdx) {
+        const int cn = min(kIdx, n_keys - c0);
+        const int n_steps = (cn + kStepBlocks * kBlk - 1) / (kStepBlocks * kBlk);
+        const int n_ent = n_steps * kStepBlocks * kBlk;
+        for (int e = tid; e < n_ent; e += kThreads) {
+            const int ge = c0 + e;
+            int j = -1;
+            if (e < cn) j = DENSE ? ge : idx_row[ge];
+            const bool v = j >= 0 && j <= pos;
+            s_row[e] = v ? j : -1;
+            s_bias[e] = v ? 0.f : -INFINITY;
+            s_mul[e] = v ? *(const float *)(a.kv_scale + (kv0 + j) * a.scale_stride) * a.scale_log2 : 0.f;
+        }
+        __syncthreads();
+        // a wait the compiler sees: the Q fragments (loaded before the first
+        // table, already landed here) need no wait of its own inside the steps,
+        // where the gather's counter is managed by hand
+        __builtin_amdgcn_s_waitcnt(0x0f70);              // vmcnt(0)
+        // DMA instructions of this wave in a step: u < 8 are main instructions
+        // ins = wv + 4u (block ins >> 4, main instruction ins & 15 of it); u = 8
+        // is tail instruction wv & 1 of block wv >> 1. Entries past the chunk
+        // (the pipeline's tail) hold -1 or a row of an earlier chunk of this
+        // query, both fetched harmlessly (row 0 for -1) and never used.
+        // (lane terms pass through an empty asm at each use, so they are
+        // recomputed rather than hoisted into registers for every instruction)
+        auto dma_row = [&](int s, int u) -> int {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            int e;
+            if (u < 8) {
+                const int ins = wv + kWaves * u;
+                e = kStepBlocks * kBlk * s + kBlk * (ins >> 4) + 2 * (ins & 15) + (ln >> 5);
+            } else {
+                e = kStepBlocks * kBlk * s + kBlk * (wv >> 1) + 16 * (wv & 1) + (ln >> 2);
+            }
+            return max(s_row[e], 0);
+        };
+        auto dma_go = [&](int s, int u, int j) {
+            int dm = dma_main, dt = dma_tail;
+            asm volatile("" : "+v"(dm), "+v"(dt));
+            uint32_t coff;
+            uint8_t *dst = ring + (s % kRingSteps) * kStepBytes;
+            if (u < 8) {
+                const int ins = wv + kWaves * u, k = ins & 15;
+                coff = 16u * (uint32_t)(dm ^ ((((2 * k) & 7) << 1) | ((k >> 3) & 1)));
+                dst += (ins >> 4) * kBlockBytes + k * 1024;
+            } else {
+                const int t = wv & 1;
+                coff = (uint32_t)kMainPitch + 16u * (uint32_t)(dt ^ (t << 1));
+                dst += (wv >> 1) * kBlockBytes + kTailBase + t * 1024;
+            }
+            dma16_opaque(kvq, (uint32_t)j * (uint32_t)a.kv_stride + coff, dst);
+        };
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int u = 0; u < kDmaStep; ++u) dma_go(s, u, dma_row(s, u));
+
+        // prologue: logits of block `half` of step 0 (and the reference max)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaStep) : "memory");       // step 0 landed
+        lds_barrier();
+        f32x16 s_cur = qk(ring + half * kBlockBytes, true, [](int) {});
+        if (need_init) {             // uniform: the first chunk of the first attempt
+            const int e0 = half * kBlk + 16 * g;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 mu = *(const f32x4 *)&s_mul[e0 + 4 * i];
+                const f32x4 bi = *(const f32x4 *)&s_bias[e0 + 4 * i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaf(s_cur[4 * i + j], mu[j] * qinv, bi[j]));
+            }
+            m_run = group_max(mx);
+            need_init = false;
+        }
+        const float msub = m_run == -INFINITY ? 0.f : m_run;
+
+        // step s: logits of step s + 1 (QK MFMAs) interleaved with the softmax
+        // of step s and the issue of the gather of step s + 2; then PV of step s
+        for (int s = 0; s < n_steps; ++s) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // step s + 1 landed
+            lds_barrier();           // step s + 1 everywhere; PV of step s - 1 done
+
+            const int e0 = (kStepBlocks * s + half) * kBlk + 16 * g;      // entry of LDS row 16g
+            const uint8_t *kstep = ring + (s % kRingSteps) * kStepBytes;
+            const uint8_t *knext = ring + ((s + 1) % kRingSteps) * kStepBytes + half * kBlockBytes;
+            // gather of step s + 2 into the slots of step s - 1: row of
+            // instruction u read in QK pair 2u, the DMA issued in pair 2u + 1
+            int jn = 0;
+            // softmax of step s: group i of the scales read in pair 4i, key k
+            // finished in pair k + 2
+            f32x4 mu[4], bi[4];
+            float mx = -INFINITY;
+            bf16x8 pa[2];
+            auto hook = [&](int p) {
+                if ((p & 1) == 1 && (p >> 1) < kDmaStep) dma_go(s + 2, p >> 1, jn);
+                if ((p & 1) == 0 && (p >> 1) < kDmaStep) jn = dma_row(s + 2, p >> 1);
+                if ((p & 3) == 0 && (p >> 2) < 4) {
+                    mu[p >> 2] = *(const f32x4 *)&s_mul[e0 + p];
+                    bi[p >> 2] = *(const f32x4 *)&s_bias[e0 + p];
+                }
+                if (p >= 2) {
+                    const int k = p - 2, i = k >> 2, j = k & 3;
+                    const float t = fmaf(s_cur[k], mu[i][j] * qinv, bi[i][j]);
+                    mx = fmaxf(mx, t);
+                    const float pr = __builtin_amdgcn_exp2f(fminf(t - msub, kClampLog2));
+                    l_run += pr;
+                    pa[k >> 3][k & 7] = (__bf16)(pr * (mu[i][j] * inv_c));
+                }
+            };
+            static_assert(kPairs == 16 + 2 && 2 * kDmaStep <= kPairs, "hook schedule");
+            const f32x16 s_next = qk(knext, s + 1 < n_steps, hook);
+            m_seen = fmaxf(m_seen, mx);
+            // also catches valid keys while the reference is unset (-inf)
+            my_vote |= __any(mx > m_run + kHeadroom);
+
+            v2i32 w[kVPre];
+#pragma unroll
+            for (int x = 0; x < kVPre; ++x) w[x] = v_ld(kstep, x);
+            s_p[wv][0][lane] = pa[0];
+            s_p[wv][1][lane] = pa[1];
+            pv(kstep, pa, w, [&](bf16x8 *pp) {
+                lds_barrier();       // probabilities of both blocks posted
+                pp[0] = s_p[wv ^ 2][0][lane];
+                pp[1] = s_p[wv ^ 2][1][lane];
+            });
+            s_cur = s_next;
+        }
+        // the tail DMA must land before the ring is reused
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        s_vote[wv] = my_vote ? 1 : 0;                // same value from every lane
+        lds_barrier();        // votes posted; every wave is done with the ring and the table
+        {
+            const int4 v = *(const int4 *)&s_vote[0];
+            redo = (v.x | v.y | v.z | v.w) != 0;
+        }
+        lds_barrier();        // votes read before the next chunk posts again
+    }
+    if (!redo) break;
+    // redo the query with a larger reference: the head group's largest block max
+    m_run = fmaxf(m_run, group_max(m_seen));
+    }
+
+    // ---- epilogue: l over both waves of the head group; LSE
+    {
+        const float lh = l_run + xor32(l_run);
+        if (g == 0) s_x[hg][half][col] = lh;
+    }
+    lds_barrier();
+    const float lt = s_x[hg][0][col] + s_x[hg][1][col];
+    if (half == 0 && g == 0 && hv)
+        a.lse[(int64_t)qi * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+
+    __bf16 *stage = (__bf16 *)smem + wv * 32 * O_LD;          // 32 heads x 256 bf16 per wave
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int hr = 8 * i + 4 * g + j;
+            const float ir = __shfl(inv, hr);
+#pragma unroll
+            for (int nb = 0; nb < kOwn; ++nb)
+                stage[hr * O_LD + 32 * nb + col] = (__bf16)(o[nb][4 * i + j] * ir);
+        }
+    lds_barrier();
+    // 32 rows x 512 B per wave: two rows per pass, 16 B per lane
+#pragma unroll
+    for (int pr = 0; pr < 16; ++pr) {
+        const int hr = 2 * pr + g;
+        const int h = 32 * hg + hr;
+        if (h < H) {
+            const u32x4 v = *(const u32x4 *)(stage + hr * O_LD + 8 * col);
+            *(u32x4 *)(a.out + ((int64_t)qi * H + h) * kV + 32 * kOwn * half + 8 * col) = v;
+        }
+    }
+}
+
+template <bool DENSE> hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
+    hipError_t e = hipFuncSetAttribute((const void *)attn_f8_kernel<DENSE>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_f8_kernel<DENSE>), dim3(a.batch.total_q), dim3(kThreads), kLdsBytes, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_fp8_f8(const AttnArgs &a, hipStream_t s) {
+    if (a.batch.total_q <= 0) return hipSuccess;
+    return a.indices == nullptr ? launch_t<true>(a, s) : launch_t<false>(a, s);
+}
+
+}  // namespace mla

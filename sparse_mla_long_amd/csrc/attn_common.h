@@ -44,6 +44,18 @@ typedef __attribute__((address_space(3))) void *lds_void_ptr;
 __device__ __forceinline__ void dma16(const void *src, uint8_t *dst) {
     __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
 }
+// The same transfer from inline asm: 16 bytes per lane from base + off (base
+// uniform, off per lane) to LDS at (wave-uniform) dst + 16 * lane. The compiler
+// does not see it as a write of LDS, so it adds no counter wait of its own
+// before later LDS reads (it cannot tell ring slots apart and would wait for
+// every transfer in flight); the caller's explicit vmcnt waits and barriers
+// must cover every read of the destination. M0 carries the LDS base; one wait
+// state follows its write, as the LDS DMA requires.
+__device__ __forceinline__ void dma16_opaque(const void *base, uint32_t off, uint8_t *dst) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)dst);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
 
 __device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x8 &d, int at) {
     const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);

@@ -58,11 +58,11 @@ def test_counter_ingestion_scales_by_the_copy(tmp_path, monkeypatch):
     # the 64 MiB copy reads 2x its size by this counter, writes 1x; a small copy is ignored
     _write_csv(f_csv, [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 64.0),
                        ("__amd_rocclr_copyBuffer", "FETCH_SIZE", 2 * 65536.0),
-                       ("mla::attn_w8_kernel<false>", "FETCH_SIZE", 1000.0),
-                       ("mla::attn_w8_kernel<false>", "FETCH_SIZE", 3000.0)])
+                       ("mla::attn_f8_kernel<false>", "FETCH_SIZE", 1000.0),
+                       ("mla::attn_f8_kernel<false>", "FETCH_SIZE", 3000.0)])
     _write_csv(w_csv, [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 65536.0),
-                       ("mla::attn_w8_kernel<false>", "WRITE_SIZE", 10.0),
-                       ("mla::attn_w8_kernel<false>", "WRITE_SIZE", 30.0)])
+                       ("mla::attn_f8_kernel<false>", "WRITE_SIZE", 10.0),
+                       ("mla::attn_f8_kernel<false>", "WRITE_SIZE", 30.0)])
     rec = bench.ingest_counters(str(f_csv), str(w_csv), 64, "sparse32k", "fp8", "cmd")
     a = rec["kernels"]["attention"]
     assert rec["fetch_factor"] == pytest.approx(0.5)
