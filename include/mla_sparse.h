@@ -135,8 +135,9 @@ mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int6
  *   out      device [total_q, n_heads, 512] bf16 (round to nearest even), 16-byte aligned
  *   lse      device [total_q, n_heads] fp32, natural log (sm_scale included)
  * Supported: n_heads in {8, 16, 32, 64}; 1 <= k <= 65536 when indices != NULL;
- * max_kv_len * kv_row_stride < 4 GiB (the rows of one sequence are addressed
- * with 32-bit offsets); MLA_ERR_UNSUPPORTED otherwise. */
+ * max_kv_len * kv_row_stride < 4 GiB and, for FP8, max_kv_len * kv_scale_stride
+ * < 4 GiB (the rows and scales of one sequence are addressed with 32-bit
+ * offsets); MLA_ERR_UNSUPPORTED otherwise. */
 mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const void *kv,
                                 const float *kv_scale, mla_kv_dtype_t kv_dtype,
                                 int64_t kv_row_stride, int64_t kv_scale_stride,

@@ -163,6 +163,9 @@ mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const v
     if ((int64_t)batch->max_kv_len * kv_row_stride > (int64_t)UINT32_MAX)
         return fail(MLA_ERR_UNSUPPORTED, "a sequence's KV rows span %lld bytes (>= 4 GiB)",
                     (long long)batch->max_kv_len * kv_row_stride);
+    if (fp8 && (int64_t)batch->max_kv_len * kv_scale_stride > (int64_t)UINT32_MAX)
+        return fail(MLA_ERR_UNSUPPORTED, "a sequence's KV scales span %lld bytes (>= 4 GiB)",
+                    (long long)batch->max_kv_len * kv_scale_stride);
     if (batch->total_q == 0) return ok();
     if (!q || !kv || !out || !lse || (fp8 && !kv_scale))
         return fail(MLA_ERR_INVALID_ARG, "q / kv / out / lse%s is NULL", fp8 ? " / kv_scale" : "");

@@ -60,16 +60,18 @@ constexpr int kDmaStep = kStepBytes / 1024 / kWaves;       // 9 DMA instructions
 constexpr int kRingSteps = 3;                              // steps resident in LDS
 constexpr int kIdx = 2048;                                 // index-list entries per chunk
 constexpr int kPad = 2 * 64;                               // row-table entries the pipeline tail reads
+constexpr int kEnt = kIdx / 256;                           // table entries per thread
 constexpr int kPairs = kQK / 32;                           // 16-byte K chunks per lane half
 constexpr int kKB = kQK / 64;                              // QK k-blocks of the FP8 MFMA
 constexpr int kOwn = kV / 64;                              // output tiles (32 dims) per wave
 constexpr int O_LD = 32 * kOwn + 8;                        // epilogue staging pitch (bf16)
 
 constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
-constexpr size_t kStaticBytes = (size_t)kIdx * 12 + kPad * 4 + kWaves * 2 * 64 * 16 + 2 * 2 * 32 * 4 + kWaves * 4;
+constexpr size_t kStaticBytes = (size_t)kIdx * 16 + kPad * 4 + kWaves * 2 * 64 * 16 + 2 * 2 * 32 * 4 + kWaves * 4;
 static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
 static_assert(kDmaStep * kWaves * 1024 == kStepBytes, "DMA split");
 static_assert(kTailBase + kBlk * kTailPitch == kBlockBytes, "block layout");
+static_assert(kEnt * kThreads == kIdx, "table split");
 static_assert((size_t)kWaves * 32 * O_LD * 2 <= kLdsBytes, "staging fits the ring");
 
 template <int N> using IC = std::integral_constant<int, N>;
@@ -94,8 +96,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     // entry table in its own LDS objects, so LDS reads of it are not ordered
     // behind the in-flight ring DMA
     __shared__ __attribute__((aligned(16))) int32_t s_row[kIdx + kPad];   // row, or -1
+    __shared__ __attribute__((aligned(16))) float s_sig[kIdx];      // sigma_j (row scale)
+    __shared__ __attribute__((aligned(16))) float s_mul[kIdx];      // sigma_j * scale * log2e, or 0
     __shared__ __attribute__((aligned(16))) float s_bias[kIdx];     // 0, or -inf if masked
-    __shared__ __attribute__((aligned(16))) float s_mul[kIdx];      // sigma_j * scale * log2e
     __shared__ bf16x8 s_p[kWaves][2][64];                           // probabilities, A-operand order
     __shared__ float s_x[2][2][32];                                 // [hg][half][head] exchange
     __shared__ int s_vote[kWaves];
@@ -126,20 +129,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     // most 2^-18 of it). K-block kb (dims of chunks 4kb + g and 4kb + 2 + g for
     // lane half g) is operand kb; byte order follows the K rows in LDS.
     i32x8 qh[kKB], ql[kKB];
-    float qinv;                                  // 2^-sq of head `col`
+    bf16x8 qraw[kPairs][2];                      // Q as loaded
     {
         const __bf16 *qrow = a.q + ((int64_t)qi * H + (hv ? head : 0)) * kQK;
-        bf16x8 raw[kPairs][2];
-        float qmax = 0.f;
 #pragma unroll
         for (int p = 0; p < kPairs; ++p)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const bf16x8 v = *(const bf16x8 *)(qrow + 16 * (2 * p + g) + 8 * e);
-                raw[p][e] = hv ? v : zero_bf16x8();
-#pragma unroll
-                for (int k = 0; k < 8; ++k) qmax = fmaxf(qmax, fabsf((float)raw[p][e][k]));
+                qraw[p][e] = hv ? v : zero_bf16x8();
             }
+    }
+    float qinv = 1.f;                            // 2^-sq of head `col`
+    auto split_q = [&]() {
+        float qmax = 0.f;
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) qmax = fmaxf(qmax, fabsf((float)qraw[p][e][k]));
         qmax = fmaxf(qmax, xor32(qmax));
         const int sq = 8 - __builtin_amdgcn_frexp_expf(qmax);
         const float qs = __builtin_ldexpf(1.f, sq);
@@ -150,7 +159,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             for (int d = 0; d < 4; ++d) {               // dword d of the pair: dims 4d .. 4d+3
                 float x[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) x[k] = (float)raw[p][d >> 1][4 * (d & 1) + k] * qs;
+                for (int k = 0; k < 4; ++k) x[k] = (float)qraw[p][d >> 1][4 * (d & 1) + k] * qs;
                 int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
                 hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hi, true);
                 const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
@@ -160,7 +169,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 qh[p >> 1][4 * (p & 1) + d] = hi;
                 ql[p >> 1][4 * (p & 1) + d] = lo;
             }
+    };
+    // index entries of the first chunk, loaded alongside Q
+    int j0[kEnt];
+#pragma unroll
+    for (int i = 0; i < kEnt; ++i) {
+        const int e = tid + kThreads * i, cn0 = min(kIdx, n_keys);
+        j0[i] = DENSE ? e : idx_row[min(e, cn0 - 1)];                   // unconditional load
     }
+    split_q();
 
     // DMA lane constants. Main instruction k of a block (k < 16) moves rows
     // 2k + (lane >> 5), physical chunk lane & 31; tail instruction t moves
@@ -179,7 +196,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     float m_run = -INFINITY, l_run = 0.f;        // head `col`, this lane's keys
     float m_seen = -INFINITY;
     f32x16 o[kOwn];
-    const float inv_c = 1.0f / a.scale_log2;     // table multiplier -> sigma_j
 
     // S^T of one block over all 576 dims, software-pipelined: the K chunk of
     // pair p + 2 is read while pair p is decoded and multiplied; hook(p) runs
@@ -281,20 +297,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         const int cn = min(kIdx, n_keys - c0);
         const int n_steps = (cn + kStepBlocks * kBlk - 1) / (kStepBlocks * kBlk);
         const int n_ent = n_steps * kStepBlocks * kBlk;
-        for (int e = tid; e < n_ent; e += kThreads) {
-            const int ge = c0 + e;
-            int j = -1;
-            if (e < cn) j = DENSE ? ge : idx_row[ge];
-            const bool v = j >= 0 && j <= pos;
-            s_row[e] = v ? j : -1;
-            s_bias[e] = v ? 0.f : -INFINITY;
-            s_mul[e] = v ? *(const float *)(a.kv_scale + (kv0 + j) * a.scale_stride) * a.scale_log2 : 0.f;
+        // entry table: rows posted, then the row scales gathered into LDS by
+        // DMA (one 4-byte lane per entry) together with the first two steps
+        int jv[kEnt];
+        if (c0 == 0) {               // uniform
+#pragma unroll
+            for (int i = 0; i < kEnt; ++i) jv[i] = j0[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kEnt; ++i) {
+                const int e = tid + kThreads * i;
+                jv[i] = DENSE ? c0 + e : idx_row[c0 + min(e, cn - 1)];   // unconditional loads
+            }
         }
-        __syncthreads();
-        // a wait the compiler sees: the Q fragments (loaded before the first
-        // table, already landed here) need no wait of its own inside the steps,
-        // where the gather's counter is managed by hand
-        __builtin_amdgcn_s_waitcnt(0x0f70);              // vmcnt(0)
+#pragma unroll
+        for (int i = 0; i < kEnt; ++i) {
+            const int e = tid + kThreads * i;
+            jv[i] = e < cn && jv[i] >= 0 && jv[i] <= pos ? jv[i] : -1;
+            s_row[e] = jv[i];
+        }
+        lds_barrier();                                   // rows posted
         // DMA instructions of this wave in a step: u < 8 are main instructions
         // ins = wv + 4u (block ins >> 4, main instruction ins & 15 of it); u = 8
         // is tail instruction wv & 1 of block wv >> 1. Entries past the chunk
@@ -334,10 +356,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int u = 0; u < kDmaStep; ++u) dma_go(s, u, dma_row(s, u));
+        {
+            const uint8_t *scale0 = a.kv_scale + kv0 * a.scale_stride;   // scale of row 0
+#pragma unroll
+            for (int i = 0; i < kEnt; ++i)                   // masked entries fetch row 0's
+                dma4_opaque(scale0, (uint32_t)max(jv[i], 0) * (uint32_t)a.scale_stride,
+                            &s_sig[kThreads * i + kWave * wv]);
+        }
+        // a wait the compiler sees (it cannot count the gathers): nothing it
+        // issued stays in flight into the steps, whose counter is kept by hand
+        __builtin_amdgcn_s_waitcnt(0x0f70);              // vmcnt(0): also steps 0 and 1 landed
+        lds_barrier();               // scales and steps 0, 1 everywhere
+#pragma unroll
+        for (int i = 0; i < kEnt; ++i) {                 // this thread's entries
+            const int e = tid + kThreads * i;
+            const bool v = jv[i] >= 0;
+            s_mul[e] = v ? s_sig[e] * a.scale_log2 : 0.f;
+            s_bias[e] = v ? 0.f : -INFINITY;
+        }
+        lds_barrier();               // table complete
 
         // prologue: logits of block `half` of step 0 (and the reference max)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaStep) : "memory");       // step 0 landed
-        lds_barrier();
         f32x16 s_cur = qk(ring + half * kBlockBytes, true, [](int) {});
         if (need_init) {             // uniform: the first chunk of the first attempt
             const int e0 = half * kBlk + 16 * g;
@@ -368,7 +407,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             int jn = 0;
             // softmax of step s: group i of the scales read in pair 4i, key k
             // finished in pair k + 2
-            f32x4 mu[4], bi[4];
+            f32x4 mu[4], bi[4], sg[4];
             float mx = -INFINITY;
             bf16x8 pa[2];
             auto hook = [&](int p) {
@@ -377,6 +416,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 if ((p & 3) == 0 && (p >> 2) < 4) {
                     mu[p >> 2] = *(const f32x4 *)&s_mul[e0 + p];
                     bi[p >> 2] = *(const f32x4 *)&s_bias[e0 + p];
+                    sg[p >> 2] = *(const f32x4 *)&s_sig[e0 + p];
                 }
                 if (p >= 2) {
                     const int k = p - 2, i = k >> 2, j = k & 3;
@@ -384,7 +424,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                     mx = fmaxf(mx, t);
                     const float pr = __builtin_amdgcn_exp2f(fminf(t - msub, kClampLog2));
                     l_run += pr;
-                    pa[k >> 3][k & 7] = (__bf16)(pr * (mu[i][j] * inv_c));
+                    pa[k >> 3][k & 7] = (__bf16)(pr * sg[i][j]);
                 }
             };
             static_assert(kPairs == 16 + 2 && 2 * kDmaStep <= kPairs, "hook schedule");

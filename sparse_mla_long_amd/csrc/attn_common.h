@@ -57,6 +57,13 @@ __device__ __forceinline__ void dma16_opaque(const void *base, uint32_t off, uin
                  ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
+// 4 bytes per lane, the same way (dst + 4 * lane).
+__device__ __forceinline__ void dma4_opaque(const void *base, uint32_t off, void *dst) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)dst);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
+
 __device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x8 &d, int at) {
     const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
     const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
