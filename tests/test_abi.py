@@ -143,6 +143,8 @@ def test_attention_argument_checks(lib):
     big, keep2 = make_batch(cu_q=(0, 4), cu_kv=(0, 8_000_000))
     assert attn_call(lib, big) == UNSUPPORTED                  # 8M rows x 576 B >= 4 GiB
     assert attn_call(lib, big, stride=512 + 64) == UNSUPPORTED
+    mid, keep3 = make_batch(cu_q=(0, 4), cu_kv=(0, 5_000_000))   # rows: 2.9 GB, fits
+    assert attn_call(lib, mid, sstride=1024) == UNSUPPORTED       # scales: 5.1 GB >= 4 GiB
 
 
 def test_empty_batch_enqueues_nothing(lib):
