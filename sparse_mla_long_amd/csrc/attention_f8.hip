@@ -67,7 +67,8 @@ constexpr int kOwn = kV / 64;                              // output tiles (32 d
 constexpr int O_LD = 32 * kOwn + 8;                        // epilogue staging pitch (bf16)
 
 constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
-constexpr size_t kStaticBytes = (size_t)kIdx * 16 + kPad * 4 + kWaves * 2 * 64 * 16 + 2 * 2 * 32 * 4 + kWaves * 4;
+constexpr size_t kStaticBytes = (size_t)kIdx * 16 + kPad * 4 + kWaves * 2 * 2 * 32 * 16 + kWaves * 32 * 4 +
+                                 2 * 2 * 32 * 4 + kWaves * 4;
 static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
 static_assert(kDmaStep * kWaves * 1024 == kStepBytes, "DMA split");
 static_assert(kTailBase + kBlk * kTailPitch == kBlockBytes, "block layout");
@@ -99,7 +100,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     __shared__ __attribute__((aligned(16))) float s_sig[kIdx];      // sigma_j (row scale)
     __shared__ __attribute__((aligned(16))) float s_mul[kIdx];      // sigma_j * scale * log2e, or 0
     __shared__ __attribute__((aligned(16))) float s_bias[kIdx];     // 0, or -inf if masked
-    __shared__ bf16x8 s_p[kWaves][2][64];                           // probabilities, A-operand order
+    __shared__ u32x4 s_ph[kWaves][2][32];                           // PV weights, E4M3 hi: [wave][g][head]
+    __shared__ u32x4 s_pl[kWaves][2][32];                           // E4M3 lo
+    __shared__ int s_pe[kWaves][32];                                // E8M0 block scale per head
     __shared__ float s_x[2][2][32];                                 // [hg][half][head] exchange
     __shared__ int s_vote[kWaves];
 
@@ -238,37 +241,41 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         }
         return s;
     };
-    // O += P V over the wave's dims; k-step t = LDS rows 16g + 8t .. +7. A lane
-    // supplies row 16g + 8t + (gi >> 1), bytes 8 (gi & 1).. of chunk 2nb + hh
-    // (nb: tile of the wave's dims). Fragment x = 2nb + t of the own block
-    // (x < 16), then of the partner block; the read of x + kVPre overlaps the
-    // MFMA of x.
-    constexpr int kVPre = 4;
-    constexpr int kVX = 2 * kOwn;                                   // fragments per block
+    // O += P V over the wave's dims on the FP8 MFMA, both blocks of a step in
+    // one 64-deep contraction. Operand bytes 0..15 of lane half g are k 16g ..
+    // 16g+15, bytes 16..31 are k 32 + 16g .. ; the E8M0 scale of lane half g
+    // covers k 32g .. 32g+31. So k 0..31 are the own block's keys (LDS rows;
+    // lane half g brings rows 16g .. 16g+15, the ones its softmax produced) and
+    // k 32..63 the partner block's, each under its own per-head scale. A is P
+    // as an E4M3 hi + lo pair (two MFMAs on the same V). B lane (dim col, g)
+    // reads rows 16g + 8t + (gi >> 1), bytes 8 (gi & 1).. of chunk 2nb + hh of
+    // the wave's 256 dims; ds_read_b64_tr_b8 hands it rows 16g + 8t .. +7 of
+    // column col.
     const int gi = lane & 15;
-    // the lane's rows 16g + 8t + (gi >> 1) share sm = 2 (gi >> 1) + g; logical
-    // chunk 2nb + hh sits at chunk 2nb ^ v_x (within the wave's 256 dims)
+    // those rows share sm = 2 (gi >> 1) + g: logical chunk 2nb + hh sits at
+    // chunk 2nb ^ v_x
     const int v_x = ((lane >> 4) & 1) ^ (2 * (gi >> 1) + g);
-    auto v_ld = [&](const uint8_t *kb, int x) -> v2i32 {
-        const int nb = (x % kVX) >> 1, t = x & 1;
-        const uint8_t *rb = kb + (x < kVX ? half : 1 - half) * kBlockBytes + 256 * half +
-                            (16 * g + (gi >> 1)) * kMainPitch + 8 * (gi & 1) + 8 * kMainPitch * t;
-        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_ptr)(rb + 16 * ((2 * nb) ^ v_x)));
-    };
-    // pa: own probabilities; after the own block, `mid` runs (barrier) and
-    // returns the partner's
-    auto pv = [&](const uint8_t *kb, const bf16x8 *pa, v2i32 *w, auto &&mid) {
-        bf16x8 pp[2] = {pa[0], pa[1]};
+    auto v_ld = [&](const uint8_t *kstep, int nb) -> i32x8 {
+        const uint8_t *rb = kstep + 256 * half + (16 * g + (gi >> 1)) * kMainPitch + 8 * (gi & 1) +
+                            16 * ((2 * nb) ^ v_x);
+        i32x8 v;
 #pragma unroll
-        for (int x = 0; x < 2 * kVX; ++x) {
-            if (x == kVX) mid(pp);
-            const v2i32 cur = w[x % kVPre];
-            if (x + kVPre < 2 * kVX) w[x % kVPre] = v_ld(kb, x + kVPre);
-            bf16x8 vb;
-            fp8x4_to_bf16((uint32_t)cur[0], vb, 0);
-            fp8x4_to_bf16((uint32_t)cur[1], vb, 4);
-            const int nb = (x % kVX) >> 1;
-            o[nb] = mfma32x32x16(pp[x & 1], vb, o[nb]);
+        for (int t = 0; t < 4; ++t) {            // own block rows (t < 2), then the partner's
+            const int blk = t < 2 ? half : 1 - half;
+            const v2i32 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_v2i32_ptr)(rb + blk * kBlockBytes + 8 * kMainPitch * (t & 1)));
+            v[2 * t] = w[0];
+            v[2 * t + 1] = w[1];
+        }
+        return v;
+    };
+    auto pv = [&](const uint8_t *kstep, const i32x8 &ah, const i32x8 &al, int sa, i32x8 vn) {
+#pragma unroll
+        for (int nb = 0; nb < kOwn; ++nb) {
+            const i32x8 vb = vn;
+            if (nb + 1 < kOwn) vn = v_ld(kstep, nb + 1);
+            o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ah, vb, o[nb], 0, 0, 0, sa, 0, 127);
+            o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(al, vb, o[nb], 0, 0, 0, sa, 0, 127);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -409,7 +416,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             // finished in pair k + 2
             f32x4 mu[4], bi[4], sg[4];
             float mx = -INFINITY;
-            bf16x8 pa[2];
+            float pw[16];            // probability times sigma_j: the PV weight
             auto hook = [&](int p) {
                 if ((p & 1) == 1 && (p >> 1) < kDmaStep) dma_go(s + 2, p >> 1, jn);
                 if ((p & 1) == 0 && (p >> 1) < kDmaStep) jn = dma_row(s + 2, p >> 1);
@@ -424,7 +431,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                     mx = fmaxf(mx, t);
                     const float pr = __builtin_amdgcn_exp2f(fminf(t - msub, kClampLog2));
                     l_run += pr;
-                    pa[k >> 3][k & 7] = (__bf16)(pr * sg[i][j]);
+                    pw[k] = pr * sg[i][j];
                 }
             };
             static_assert(kPairs == 16 + 2 && 2 * kDmaStep <= kPairs, "hook schedule");
@@ -433,16 +440,44 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             // also catches valid keys while the reference is unset (-inf)
             my_vote |= __any(mx > m_run + kHeadroom);
 
-            v2i32 w[kVPre];
+            // PV weights of the own block as E4M3 hi + lo under a per-head E8M0
+            // scale 2^pe (the block's largest weight lands in [128, 256)); the
+            // lane's 16 keys are LDS rows 16g .. 16g+15, piece g of the 32
+            float pmax = 0.f;
 #pragma unroll
-            for (int x = 0; x < kVPre; ++x) w[x] = v_ld(kstep, x);
-            s_p[wv][0][lane] = pa[0];
-            s_p[wv][1][lane] = pa[1];
-            pv(kstep, pa, w, [&](bf16x8 *pp) {
-                lds_barrier();       // probabilities of both blocks posted
-                pp[0] = s_p[wv ^ 2][0][lane];
-                pp[1] = s_p[wv ^ 2][1][lane];
-            });
+            for (int k = 0; k < 16; ++k) pmax = fmaxf(pmax, pw[k]);
+            pmax = fmaxf(pmax, xor32(pmax));
+            const int pe = min(max(__builtin_amdgcn_frexp_expf(pmax) - 8, -127), 127);
+            u32x4 ph, pl;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                float x[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x[q] = __builtin_ldexpf(pw[4 * d + q], -pe);
+                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hi, true);
+                const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+                const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - b0[0], x[1] - b0[1], 0, false);
+                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b1[0], x[3] - b1[1], lo, true);
+                ph[d] = (uint32_t)hi;
+                pl[d] = (uint32_t)lo;
+            }
+            s_ph[wv][g][col] = ph;
+            s_pl[wv][g][col] = pl;
+            if (g == 0) s_pe[wv][col] = 127 + pe;
+            i32x8 vn = v_ld(kstep, 0);
+            lds_barrier();           // weights of both blocks posted
+            // A: own weights in bytes 0..15, the partner's (same heads, same
+            // rows of its block) in bytes 16..31; lane half 0 carries the own
+            // block's scale, half 1 the partner's
+            const u32x4 hp = s_ph[wv ^ 2][g][col], lp = s_pl[wv ^ 2][g][col];
+            const i32x8 ah = {(int)ph[0], (int)ph[1], (int)ph[2], (int)ph[3],
+                              (int)hp[0], (int)hp[1], (int)hp[2], (int)hp[3]};
+            const i32x8 al = {(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3],
+                              (int)lp[0], (int)lp[1], (int)lp[2], (int)lp[3]};
+            const int sa = g == 0 ? 127 + pe : s_pe[wv ^ 2][col];
+            pv(kstep, ah, al, sa, vn);
             s_cur = s_next;
         }
         // the tail DMA must land before the ring is reused
