@@ -108,7 +108,7 @@ mla_status_t mla_indexer_score(const mla_batch_t *batch, const void *q_idx, cons
  * padded with -1. Scores must not be NaN.
  *   scores  device [total_q, ld_scores] fp32 (row i read for j <= q_pos[i])
  *   indices device [total_q, k] int32
- * Supported: 1 <= k <= 4096. */
+ * Supported: 1 <= k <= 4096; max_kv_len <= 524288 (MLA_ERR_UNSUPPORTED otherwise). */
 mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int64_t ld_scores,
                              int32_t k, int32_t *indices, void *stream);
 

@@ -124,6 +124,9 @@ mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int6
     if (ld_scores < batch->max_kv_len)
         return fail(MLA_ERR_INVALID_ARG, "ld_scores %lld < max_kv_len %d", (long long)ld_scores,
                     batch->max_kv_len);
+    if (batch->max_kv_len > mla::kTopkMaxRow)
+        return fail(MLA_ERR_UNSUPPORTED, "max_kv_len %d > %d (top-k row bitmaps live in LDS)",
+                    batch->max_kv_len, mla::kTopkMaxRow);
     if (batch->total_q == 0) return ok();
     if (!scores || !indices) return fail(MLA_ERR_INVALID_ARG, "scores / indices is NULL");
     if (!aligned(scores, 4) || !aligned(indices, 4))

@@ -53,6 +53,7 @@ struct AttnArgs {
 
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+constexpr int32_t kTopkMaxRow = 1 << 19;   // longest score row top-k takes (its bitmaps sit in LDS)
 hipError_t launch_attention(const AttnArgs &a, bool fp8, hipStream_t s);
 // FP8 (E4M3) latent rows (launch_attention dispatches to it)
 hipError_t launch_attention_fp8_f8(const AttnArgs &a, hipStream_t s);

@@ -4,17 +4,22 @@
 // to). Ties go to the smaller key index; the kept indices come out ascending.
 //
 // One 512-thread workgroup per query row. Scores become order-preserving
-// 32-bit keys (-0 folded onto +0). The row is read once for its key range
-// [kmin, kmax] (and staged in LDS when it fits); the k-th largest key T is
-// then found by an MSD radix select on v = key - kmin whose first 11-bit
-// digit spans the row's actual range, so it already splits typical score
-// distributions finely. A classify pass marks every key whose first digit is
-// above T's in a bitmap and collects the keys of T's bin (usually a few
-// dozen) into an LDS candidate list; the remaining digits are resolved on
-// that list alone. Candidates above T join the bitmap, candidates equal to T
-// go to a tie bitmap, and the output is the selected bits in index order --
-// the first (k - #above) ties by index -- written with two block scans.
-// Long rows cost three global reads; rows in LDS read global memory once.
+// 32-bit keys (-0 folded onto +0). A first pass over the row finds its key
+// range [kmin, kmax]; the k-th largest key T is then found by an MSD radix
+// select on v = key - kmin whose first 11-bit digit spans the row's actual
+// range, so it already splits typical score distributions finely. A classify
+// pass marks every key whose first digit is above T's in a bitmap and
+// collects the keys of T's bin (usually a few dozen) into an LDS candidate
+// list; the remaining digits are resolved on that list alone. Candidates
+// above T join the bitmap, candidates equal to T go to a tie bitmap, and the
+// output is the selected bits in index order -- the first (k - #above) ties
+// by index -- written with two block scans.
+//
+// The row is read from global memory three times (range, first-digit
+// histogram, classify); the re-reads hit L2/MALL. Nothing but the bitmaps,
+// the histogram and the candidate list lives in LDS, and the kernel keeps to
+// 64 VGPRs, so several rows share a CU and hide each other's latency: the
+// kernel is bound by latency, not by its few instructions per key.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,8 +31,10 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kBins = 2048;                  // 11-bit digits
 constexpr int kDigit = 11;
 constexpr int kBatch = 8;                    // keys per thread per pass iteration
-constexpr int kVecBatch = 16;                // 16-byte loads per thread in the first pass
-constexpr size_t kLdsBudget = 160 * 1024 - 12 * 1024;   // minus static LDS and slack
+constexpr int kVecBatch = 4;                 // 16-byte loads per thread in the first pass
+constexpr int kCandCap = 1024;               // candidate list entries (a bin this size or more: one more pass)
+// longest rows: two bitmaps of kTopkMaxRow bits plus the candidate list beside the static LDS
+static_assert(2 * (kTopkMaxRow / 32) * 4 + kCandCap * 8 + 16 * 1024 <= 160 * 1024, "top-k LDS");
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -70,23 +77,18 @@ __device__ __forceinline__ int block_excl_scan(int x, int *s_w, int &total) {
     return woff + inc - x;
 }
 
-struct TopkLds {        // dynamic LDS carve-up, decided on the host
-    int32_t stage_cap;  // rows up to this length are staged as keys in LDS
-    int32_t words;      // bitmap words (max_row / 32, rounded up)
-    int32_t cand_cap;   // candidate list entries
-};
-
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a, TopkLds lay) {
+// 64 VGPRs: eight waves per SIMD, several workgroups per CU
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void topk_kernel(TopkArgs a, int words) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ uint32_t hist[kBins];
     __shared__ int s_w[kWaves];
     __shared__ uint32_t s_mm[2 * kWaves];
     __shared__ int s_sel[2];
     __shared__ int s_cand_n;
-    uint32_t *keys = dyn;                                        // [stage_cap]
-    uint32_t *bm_sel = dyn + lay.stage_cap;                      // [words]
-    uint32_t *bm_eq = bm_sel + lay.words;                        // [words]
-    uint2 *cand = (uint2 *)(bm_eq + lay.words);                  // [cand_cap] (key, index)
+    uint32_t *bm_sel = dyn;                                      // [words]
+    uint32_t *bm_eq = bm_sel + words;                            // [words]
+    uint2 *cand = (uint2 *)(bm_eq + words);                      // [kCandCap] (key, index)
 
     const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
     const int qi = a.batch.total_q - 1 - (int)blockIdx.x;
@@ -98,33 +100,23 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a, TopkLds lay)
         return;
     }
     const float *row = a.scores + (int64_t)qi * a.ld;
-    const bool staged = n <= lay.stage_cap;
     // kBatch keys per thread: element base + u*kThreads + tid (0 past the row end)
     auto load_keys = [&](int base, uint32_t (&kb)[kBatch]) {
-        if (staged) {
+        float f[kBatch];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int j = base + u * kThreads + tid;
-                kb[u] = j < n ? keys[j] : 0u;
-            }
-        } else {
-            float f[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int j = base + u * kThreads + tid;
-                f[u] = j < n ? row[j] : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) kb[u] = order_key(f[u]);
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = base + u * kThreads + tid;
+            f[u] = j < n ? row[j] : 0.f;
         }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) kb[u] = order_key(f[u]);
     };
     const int W = (n + 31) >> 5;
 
-    // ---- pass 1: key range (and staging); clear the bitmaps. Loads are
-    // batched kBatch deep per thread so a workgroup keeps ~16 KiB in flight.
+    // ---- pass 1: key range; clear the bitmaps
     uint32_t kmin = 0xffffffffu, kmax = 0u;
     const bool vec = (((uintptr_t)row) & 15) == 0;
-    // 16-byte loads, kVecBatch per thread: a 32k-key row is in flight at once
+    // 16-byte loads, kVecBatch per thread
     for (int base = 0; vec && base < n; base += kThreads * 4 * kVecBatch) {
         f32x4 f[kVecBatch];
 #pragma unroll
@@ -149,14 +141,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a, TopkLds lay)
                     kmax = max(kmax, kk[e]);
                 }
             }
-            if (staged) {
-                if (j + 3 < n) {
-                    *(u32x4 *)(keys + j) = u32x4{kk[0], kk[1], kk[2], kk[3]};
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) if (j + e < n) keys[j + e] = kk[e];
-                }
-            }
         }
     }
     for (int base = 0; !vec && base < n; base += kThreads * kBatch) {
@@ -171,7 +155,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a, TopkLds lay)
             const int j = base + u * kThreads + tid;
             if (j < n) {
                 const uint32_t key = order_key(f[u]);
-                if (staged) keys[j] = key;
                 kmin = min(kmin, key);
                 kmax = max(kmax, key);
             }
@@ -273,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a, TopkLds lay)
             __syncthreads();
             if (level == 0) {
                 // classify: above T's first digit -> selected; in its bin -> candidate
-                const bool fits = in_bin <= lay.cand_cap;
+                const bool fits = in_bin <= kCandCap;
                 for (int base = 0; base < n; base += kThreads * kBatch) {
                   uint32_t kb[kBatch];
                   load_keys(base, kb);
@@ -396,22 +379,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a, TopkLds lay)
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     if (a.batch.total_q <= 0) return hipSuccess;
-    TopkLds lay;
-    lay.words = (a.max_row + 31) / 32;
-    const size_t bitmaps = (size_t)2 * lay.words * 4;
-    const size_t min_cand = 512 * 8;
-    const size_t room = kLdsBudget > bitmaps + min_cand ? kLdsBudget - bitmaps - min_cand : 0;
-    int stage = (int)(room / 4);
-    if (stage > 32768) stage = 32768;
-    if (stage > a.max_row) stage = a.max_row;
-    lay.stage_cap = stage;
-    const size_t used = (size_t)stage * 4 + bitmaps;
-    lay.cand_cap = used < kLdsBudget ? (int)((kLdsBudget - used) / 8) : 0;
-    const size_t lds = used + (size_t)lay.cand_cap * 8;
+    const int words = (a.max_row + 31) / 32;
+    const size_t lds = (size_t)2 * words * 4 + (size_t)kCandCap * 8;
     const hipError_t e = hipFuncSetAttribute((const void *)topk_kernel,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_kernel, dim3(a.batch.total_q), dim3(kThreads), lds, s, a, lay);
+    hipLaunchKernelGGL(topk_kernel, dim3(a.batch.total_q), dim3(kThreads), lds, s, a, words);
     return hipGetLastError();
 }
 

@@ -121,6 +121,8 @@ def test_topk_argument_checks(lib):
     assert topk_call(lib, b, k=0) == INVALID
     assert topk_call(lib, b, k=4097) == UNSUPPORTED
     assert topk_call(lib, b, ld=5) == INVALID
+    long_rows, keep2 = make_batch(cu_q=(0, 4), cu_kv=(0, 524289))
+    assert topk_call(lib, long_rows) == UNSUPPORTED             # row bitmaps would overflow LDS
     assert topk_call(lib, b, out=None) == INVALID
 
 
