@@ -22,7 +22,7 @@ namespace {
 
 constexpr int kIdxThreads = kIdxQueriesPerBlock * kWave;  // one wave per query
 constexpr int kIdxWaves = kIdxQueriesPerBlock;
-constexpr int kKeyTile = 64;
+constexpr int kKeyTile = 128;
 constexpr int kTileRing = 4;
 
 template <int KS, int MB>
@@ -101,15 +101,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
 
     const int n_tiles = pmax / kKeyTile + 1;
     float *srow = a.scores + (int64_t)qi * a.ld;
-    // Software pipeline over 32-key sub-tiles: the MFMAs of sub-tile u run in
-    // the same straight-line block as the epilogue (ReLU, w, head sum) of
-    // sub-tile u-1. Sub-tiles past this query's position compute on later or
-    // repeated keys and are not stored.
     f32x16 prev[MB];
     int prev_j0 = -1;                                   // first key of the pending sub-tile
-    auto epilogue = [&](const f32x16 *acc, int j0) {
-        // four independent partial sums (a single chain would serialise
-        // 32 dependent FMAs), then the other lane half's rows
+    // score of key prev_j0 + col for this lane (lane half 0 stores it): ReLU,
+    // w and the head sum over four independent partial sums (a single chain
+    // would serialise 32 dependent FMAs), then the other lane half's rows
+    auto epilogue = [&](const f32x16 *acc) -> float {
         float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -117,7 +114,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
             for (int e = 0; e < 16; ++e) ps[e & 3] += wr[mb][e] * fmaxf(acc[mb][e], 0.f);
         float sc = (ps[0] + ps[1]) + (ps[2] + ps[3]);
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
-        sc += __uint_as_float(g ? r[0] : r[1]);
+        return sc + __uint_as_float(g ? r[0] : r[1]);
+    };
+    auto store = [&](float sc, int j0) {
         const int j = j0 + col;
         if (g == 0 && j <= pos) srow[j] = sc;
     };
@@ -129,6 +128,13 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         attn::lds_barrier();                                 // ... everywhere; tile t-1 done
         issue(t + kTileRing - 1, (t + kTileRing - 1) % kTileRing);
         const uint8_t *kt = ktile[t % kTileRing];
+        // Software pipeline over 32-key sub-tiles: the MFMAs of sub-tile u share
+        // a scheduling region (closed by a scheduling barrier) with the
+        // epilogue of sub-tile u-1; the scores are stored after the tile's
+        // MFMAs, so no branch splits that region. Sub-tiles past this query's
+        // position compute on later or repeated keys and are not stored.
+        float sc[kKeyTile / 32];
+        int sj[kKeyTile / 32];
 #pragma unroll
         for (int s = 0; s < kKeyTile / 32; ++s) {
             f32x16 acc[MB];
@@ -142,14 +148,19 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(qf[mb][ks], bk, acc[mb]);
             }
-            if (prev_j0 >= 0) epilogue(prev, prev_j0);   // false only for the very first sub-tile
+            sc[s] = epilogue(prev);                      // garbage before the first sub-tile: not stored
+            sj[s] = prev_j0;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) prev[mb] = acc[mb];
             prev_j0 = t0 + 32 * s;
+            __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int s = 0; s < kKeyTile / 32; ++s)
+            if (sj[s] >= 0) store(sc[s], sj[s]);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail DMA lands before the LDS is freed
-    epilogue(prev, prev_j0);
+    store(epilogue(prev), prev_j0);
 }
 
 template <int KS, int MB>
