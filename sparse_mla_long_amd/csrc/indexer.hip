@@ -25,6 +25,11 @@ constexpr int kIdxWaves = kIdxQueriesPerBlock;
 constexpr int kKeyTile = 128;
 constexpr int kTileRing = 4;
 
+// ReLU as a signed-integer max on the bit pattern: negative values and -0
+// become +0, everything else passes unchanged. One instruction, where fmaxf
+// also canonicalises its operand first.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 template <int KS, int MB>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     constexpr int DI = KS * 16;          // indexer head dim
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) ps[e & 3] += wr[mb][e] * fmaxf(acc[mb][e], 0.f);
+            for (int e = 0; e < 16; ++e) ps[e & 3] += wr[mb][e] * relu(acc[mb][e]);
         float sc = (ps[0] + ps[1]) + (ps[2] + ps[3]);
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
         return sc + __uint_as_float(g ? r[0] : r[1]);
