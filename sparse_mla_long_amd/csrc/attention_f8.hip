@@ -18,13 +18,13 @@
 //    registers, so a block's logits need no cross-wave reduction.
 //  * Softmax in registers: accumulator element (i, j) of lane half g is LDS
 //    row 16g + 4i + j of the block (the QK A operand reads rows in that
-//    order), which is the k order PV's A operand wants, so the probabilities
+//    order), which is the k order PV's P operand wants, so the probabilities
 //    (times the FP8 row scale sigma_j) go straight from the softmax into PV.
-//  * PV: O[head x dim] += P[head x key] V[key x dim] over the wave's 256
-//    dims; V is read key-major with ds_read_b64_tr_b8 (8 rows of one column
-//    per lane). O (32 heads x 256 dims, f32) lives in accumulation registers.
-//    The own block's PV runs before the mid-step barrier that publishes the
-//    probabilities, the partner block's after it.
+//  * PV: O^T[dim x head] += V^T[dim x key] P^T[key x head] over the wave's
+//    256 dims and the 64 keys of the step (the partner's probabilities come
+//    through LDS after a mid-step barrier); V is read key-major with
+//    ds_read_b64_tr_b8 (8 rows of one column per lane). O^T (256 dims x 32
+//    heads, f32) lives in accumulation registers, one head per lane column.
 //  * Reference max per head shared by both waves of a head group (the max of
 //    the first step's two blocks), so their probabilities and row sums share
 //    one scale; blocks exceeding it by more than 2^kHeadroom vote for a redo
@@ -68,7 +68,7 @@ constexpr int O_LD = 32 * kOwn + 8;                        // epilogue staging p
 
 constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
 constexpr size_t kStaticBytes = (size_t)kIdx * 16 + kPad * 4 + kWaves * 2 * 2 * 32 * 16 + kWaves * 32 * 4 +
-                                 2 * 2 * 32 * 4 + kWaves * 4;
+                                 2 * 2 * 32 * 4 + kWaves * 4 + 2 * kKB * 32;
 static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
 static_assert(kDmaStep * kWaves * 1024 == kStepBytes, "DMA split");
 static_assert(kTailBase + kBlk * kTailPitch == kBlockBytes, "block layout");
@@ -77,12 +77,21 @@ static_assert((size_t)kWaves * 32 * O_LD * 2 <= kLdsBytes, "staging fits the rin
 
 template <int N> using IC = std::integral_constant<int, N>;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// v_mfma_scale_f32_32x32x64_f8f6f4, both operands E4M3, unit scales. Operand
-// layout (lane l, g = l / 32): A row (l % 32), B column (l % 32), byte p of the
-// 32 holds k = 32g + p; C as the 32x32x16 bf16 MFMA.
-__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// v_mfma_scale_f32_32x32x64_f8f6f4, both operands E4M3, A unscaled, B scaled
+// by the E8M0 code in byte `sel` of sb. Operand layout (lane l, g = l / 32): A
+// row (l % 32), B column (l % 32); operand bytes 0..15 hold k = 16g .. 16g+15,
+// bytes 16..31 k = 32 + 16g ..; the scale of lane (r, g) covers row or column r
+// at k = 32g .. 32g+31. C as the 32x32x16 bf16 MFMA. (`sel` is a constant
+// after unrolling; the switch folds away.)
+__device__ __forceinline__ f32x16 mfma_f8_bs(i32x8 a, i32x8 b, f32x16 c, int sel, uint32_t sb) {
+    switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, (int)sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 1, (int)sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 2, (int)sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 3, (int)sb);
+    }
 }
 
 // chunk swizzles of block row r: main part (32 chunks), tail part (4 chunks)
@@ -105,6 +114,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     __shared__ int s_pe[kWaves][32];                                // E8M0 block scale per head
     __shared__ float s_x[2][2][32];                                 // [hg][half][head] exchange
     __shared__ int s_vote[kWaves];
+    __shared__ uint8_t s_qcode[2][kKB][32];                         // Q scale codes [hg][k-block][head]
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
     const int hg = wv & 1, half = wv >> 1;
@@ -119,68 +129,115 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const int32_t *idx_row = DENSE ? nullptr : a.indices + (int64_t)qi * a.k;
     const uint8_t *kvq = a.kv + kv0 * a.kv_stride;                   // row 0 of this sequence
 
-    // Q^T fragments (B operand): k-steps 2p, 2p+1 take chunk 2p + g (lane half
-    // g), dims 0..7 then 8..15 of it, matching the K reads below
     const int head = 32 * hg + col;
     const bool hv = head < H;
-    // Q^T as two E4M3 operands (B of the 32x32x64 FP8 MFMA): per head, Q is
-    // scaled by 2^sq (its largest |q| lands in [128, 256)) and split into
-    // hi = e4m3(q 2^sq) and lo = e4m3(q 2^sq - hi). A bf16 value has 8
-    // significant bits and the residual is a multiple of its last bit no larger
-    // than half a step of hi, so hi + lo is exact unless lo falls below the
-    // E4M3 subnormal range (elements 2^10 below the head's largest, off by at
-    // most 2^-18 of it). K-block kb (dims of chunks 4kb + g and 4kb + 2 + g for
-    // lane half g) is operand kb; byte order follows the K rows in LDS.
+    // Q^T as two E4M3 operands (B of the 32x32x64 FP8 MFMA). K-block kb (dims
+    // of chunks 4kb + g and 4kb + 2 + g for lane half g) is operand kb; byte
+    // order follows the K rows in LDS. Per head and k-block, Q is scaled by
+    // 2^sq (the block's largest |q| lands in [128, 256)) and split into
+    // hi = e4m3(q 2^sq) and lo = e4m3(q 2^sq - hi); the MFMA's E8M0 B scale
+    // 2^-sq (byte kb & 3 of qsc[kb >> 2]) undoes the scaling. A bf16 value has
+    // 8 significant bits and the residual is a multiple of its last bit no
+    // larger than half a step of hi, so hi + lo is exact unless lo falls below
+    // the E4M3 subnormal range (elements 2^10 below the block's largest, off by
+    // at most 2^-18 of it). The two waves of a head group split half of the
+    // k-blocks each (kKB0 and the rest) and trade the operands through LDS.
+    constexpr int kKB0 = 5;                      // k-blocks split by the half-0 wave (it takes 0 .. 4)
     i32x8 qh[kKB], ql[kKB];
-    bf16x8 qraw[kPairs][2];                      // Q as loaded
-    {
-        const __bf16 *qrow = a.q + ((int64_t)qi * H + (hv ? head : 0)) * kQK;
-#pragma unroll
-        for (int p = 0; p < kPairs; ++p)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const bf16x8 v = *(const bf16x8 *)(qrow + 16 * (2 * p + g) + 8 * e);
-                qraw[p][e] = hv ? v : zero_bf16x8();
-            }
-    }
-    float qinv = 1.f;                            // 2^-sq of head `col`
-    auto split_q = [&]() {
-        float qmax = 0.f;
-#pragma unroll
-        for (int p = 0; p < kPairs; ++p)
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) qmax = fmaxf(qmax, fabsf((float)qraw[p][e][k]));
-        qmax = fmaxf(qmax, xor32(qmax));
-        const int sq = 8 - __builtin_amdgcn_frexp_expf(qmax);
-        const float qs = __builtin_ldexpf(1.f, sq);
-        qinv = __builtin_ldexpf(1.f, -sq);
-#pragma unroll
-        for (int p = 0; p < kPairs; ++p)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {               // dword d of the pair: dims 4d .. 4d+3
-                float x[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) x[k] = (float)qraw[p][d >> 1][4 * (d & 1) + k] * qs;
-                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hi, true);
-                const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-                const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - b0[0], x[1] - b0[1], 0, false);
-                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b1[0], x[3] - b1[1], lo, true);
-                qh[p >> 1][4 * (p & 1) + d] = hi;
-                ql[p >> 1][4 * (p & 1) + d] = lo;
-            }
-    };
-    // index entries of the first chunk, loaded alongside Q
+    uint32_t qsc[(kKB + 3) / 4] = {};
+    // index entries of the first chunk, loaded ahead of Q so the row table
+    // does not wait for it
     int j0[kEnt];
 #pragma unroll
     for (int i = 0; i < kEnt; ++i) {
         const int e = tid + kThreads * i, cn0 = min(kIdx, n_keys);
         j0[i] = DENSE ? e : idx_row[min(e, cn0 - 1)];                   // unconditional load
     }
-    split_q();
+    // The wave's k-blocks kbase + kl (kl < kKB0; the half-1 wave's last one
+    // repeats block kKB - 1 and is not posted): dims 64 kb + 32 pp + 16 g ..
+    // +15 of pair pp. Lanes of heads past n_heads load head 0 and compute on
+    // it; nothing of theirs is stored. (Unconditional loads: no branch, all in
+    // flight at once.)
+    const int kbase = half == 0 ? 0 : kKB0;
+    bf16x8 qraw[kKB0][2][2];
+    {
+        const __bf16 *qrow = a.q + ((int64_t)qi * H + (hv ? head : 0)) * kQK + 16 * g;
+#pragma unroll
+        for (int kl = 0; kl < kKB0; ++kl)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    qraw[kl][pp][e] = *(const bf16x8 *)(qrow + 64 * min(kbase + kl, kKB - 1) + 32 * pp + 8 * e);
+    }
+    // The split, traded with the partner (wave w ^ 2, same heads and lanes)
+    // through ring slots 1 and 2, free until the first gathers of step 1:
+    // k-block kbase + kl of wave w at xq(w) + 4096 kl + 1024 u + 16 lane (u:
+    // hi dwords 0..3, 4..7, lo dwords 0..3, 4..7), its scale code in s_qcode.
+    // Every wave then reads all nine blocks back, so no register array is
+    // indexed by a wave-dependent value.
+    auto trade_q = [&]() {
+        auto xq = [&](int w) {
+            const int hf = w >> 1, hgw = w & 1;
+            return ring + kStepBytes + 4096 * (hf == 0 ? hgw * kKB0 : 2 * kKB0 + hgw * (kKB - kKB0));
+        };
+#pragma unroll
+        for (int kl = 0; kl < kKB0; ++kl) {
+            // largest |q| of the head over the block: bf16 magnitudes order as
+            // the integers in their low 15 bits (two per dword, packed u16 max)
+            u16x2 m2 = {0, 0};
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const u32x4 w = __builtin_bit_cast(u32x4, qraw[kl][pp][e]);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[d] & 0x7fff7fffu));
+                }
+            uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]) << 16;
+            m = max(m, __float_as_uint(xor32(__uint_as_float(m))));
+            const int ex = max(__builtin_amdgcn_frexp_expf(__uint_as_float(m)), -119);
+            const float qs = __builtin_ldexpf(1.f, 8 - ex);
+            int hw[8], lw[8];
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {           // dword d of the pair: dims 4d .. 4d+3
+                    float x[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) x[k] = (float)qraw[kl][pp][d >> 1][4 * (d & 1) + k] * qs;
+                    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hi, true);
+                    const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+                    const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - b0[0], x[1] - b0[1], 0, false);
+                    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b1[0], x[3] - b1[1], lo, true);
+                    hw[4 * pp + d] = hi;
+                    lw[4 * pp + d] = lo;
+                }
+            if (kl < kKB - kKB0 || half == 0) {  // uniform
+                uint8_t *x = xq(wv) + 4096 * kl + 16 * lane;
+                *(u32x4 *)(x) = u32x4{(uint32_t)hw[0], (uint32_t)hw[1], (uint32_t)hw[2], (uint32_t)hw[3]};
+                *(u32x4 *)(x + 1024) = u32x4{(uint32_t)hw[4], (uint32_t)hw[5], (uint32_t)hw[6], (uint32_t)hw[7]};
+                *(u32x4 *)(x + 2048) = u32x4{(uint32_t)lw[0], (uint32_t)lw[1], (uint32_t)lw[2], (uint32_t)lw[3]};
+                *(u32x4 *)(x + 3072) = u32x4{(uint32_t)lw[4], (uint32_t)lw[5], (uint32_t)lw[6], (uint32_t)lw[7]};
+                if (g == 0) s_qcode[hg][kbase + kl][col] = (uint8_t)(119 + ex);   // E8M0 of 2^(ex - 8)
+            }
+        }
+        lds_barrier();                           // both halves posted
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) {
+            const int oh = kb < kKB0 ? 0 : 1;        // the half that split it
+            const uint8_t *x = xq(hg + 2 * oh) + 4096 * (kb - kKB0 * oh) + 16 * lane;
+            const u32x4 h0 = *(const u32x4 *)(x), h1 = *(const u32x4 *)(x + 1024);
+            const u32x4 l0 = *(const u32x4 *)(x + 2048), l1 = *(const u32x4 *)(x + 3072);
+            qh[kb] = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+            ql[kb] = i32x8{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+            qsc[kb >> 2] |= (uint32_t)s_qcode[hg][kb][col] << (8 * (kb & 3));
+        }
+        lds_barrier();                           // traded: slot 1 may take its gather
+    };
 
     // DMA lane constants. Main instruction k of a block (k < 16) moves rows
     // 2k + (lane >> 5), physical chunk lane & 31; tail instruction t moves
@@ -233,24 +290,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             hook(2 * kb + 1);
             const i32x8 kf = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3],
                               (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
-            s = mfma_f8(kf, qh[kb], s);
-            s = mfma_f8(kf, ql[kb], s);
+            s = mfma_f8_bs(kf, qh[kb], s, kb & 3, qsc[kb >> 2]);
+            s = mfma_f8_bs(kf, ql[kb], s, kb & 3, qsc[kb >> 2]);
             c0 = n0;
             c1 = n1;
             __builtin_amdgcn_sched_barrier(0);
         }
         return s;
     };
-    // O += P V over the wave's dims on the FP8 MFMA, both blocks of a step in
-    // one 64-deep contraction. Operand bytes 0..15 of lane half g are k 16g ..
-    // 16g+15, bytes 16..31 are k 32 + 16g .. ; the E8M0 scale of lane half g
-    // covers k 32g .. 32g+31. So k 0..31 are the own block's keys (LDS rows;
-    // lane half g brings rows 16g .. 16g+15, the ones its softmax produced) and
-    // k 32..63 the partner block's, each under its own per-head scale. A is P
-    // as an E4M3 hi + lo pair (two MFMAs on the same V). B lane (dim col, g)
-    // reads rows 16g + 8t + (gi >> 1), bytes 8 (gi & 1).. of chunk 2nb + hh of
-    // the wave's 256 dims; ds_read_b64_tr_b8 hands it rows 16g + 8t .. +7 of
-    // column col.
+    // O^T += V^T P^T over the wave's dims on the FP8 MFMA, both blocks of a
+    // step in one 64-deep contraction; O^T puts one head in each lane column,
+    // so the epilogue needs no shuffle. Operand bytes 0..15 of lane half g are
+    // k 16g .. 16g+15, bytes 16..31 are k 32 + 16g .. ; the E8M0 scale of lane
+    // half g covers k 32g .. 32g+31. So k 0..31 are the own block's keys (LDS
+    // rows; lane half g brings rows 16g .. 16g+15, the ones its softmax
+    // produced) and k 32..63 the partner block's, each under its own per-head
+    // scale. B is P^T as an E4M3 hi + lo pair (two MFMAs on the same V). A lane
+    // (dim col, g) reads rows 16g + 8t + (gi >> 1), bytes 8 (gi & 1).. of chunk
+    // 2nb + hh of the wave's 256 dims; ds_read_b64_tr_b8 hands it rows
+    // 16g + 8t .. +7 of column col.
     const int gi = lane & 15;
     // those rows share sm = 2 (gi >> 1) + g: logical chunk 2nb + hh sits at
     // chunk 2nb ^ v_x
@@ -274,8 +332,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         for (int nb = 0; nb < kOwn; ++nb) {
             const i32x8 vb = vn;
             if (nb + 1 < kOwn) vn = v_ld(kstep, nb + 1);
-            o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ah, vb, o[nb], 0, 0, 0, sa, 0, 127);
-            o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(al, vb, o[nb], 0, 0, 0, sa, 0, 127);
+            o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, ah, o[nb], 0, 0, 0, 127, 0, sa);
+            o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, al, o[nb], 0, 0, 0, 127, 0, sa);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -289,9 +347,76 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         return r;
     };
 
+    // DMA instructions of this wave in a step: u < 8 are main instructions
+    // ins = wv + 4u (block ins >> 4, main instruction ins & 15 of it); u = 8 is
+    // tail instruction wv & 1 of block wv >> 1. Entries past the chunk (the
+    // pipeline's tail) hold -1 or a row of an earlier chunk of this query,
+    // both fetched harmlessly (row 0 for -1) and never used. (Lane terms pass
+    // through an empty asm at each use, so they are recomputed rather than
+    // hoisted into registers for every instruction.)
+    auto dma_row = [&](int s, int u) -> int {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        int e;
+        if (u < 8) {
+            const int ins = wv + kWaves * u;
+            e = kStepBlocks * kBlk * s + kBlk * (ins >> 4) + 2 * (ins & 15) + (ln >> 5);
+        } else {
+            e = kStepBlocks * kBlk * s + kBlk * (wv >> 1) + 16 * (wv & 1) + (ln >> 2);
+        }
+        return max(s_row[e], 0);
+    };
+    auto dma_go = [&](int s, int u, int j) {
+        int dm = dma_main, dt = dma_tail;
+        asm volatile("" : "+v"(dm), "+v"(dt));
+        uint32_t coff;
+        uint8_t *dst = ring + (s % kRingSteps) * kStepBytes;
+        if (u < 8) {
+            const int ins = wv + kWaves * u, k = ins & 15;
+            coff = 16u * (uint32_t)(dm ^ ((((2 * k) & 7) << 1) | ((k >> 3) & 1)));
+            dst += (ins >> 4) * kBlockBytes + k * 1024;
+        } else {
+            const int t = wv & 1;
+            coff = (uint32_t)kMainPitch + 16u * (uint32_t)(dt ^ (t << 1));
+            dst += (wv >> 1) * kBlockBytes + kTailBase + t * 1024;
+        }
+        dma16_opaque(kvq, (uint32_t)j * (uint32_t)a.kv_stride + coff, dst);
+    };
+    // Row table of the chunk starting at entry c0 (jv: its raw entries of this
+    // thread): rows posted (-1 where masked), then the gather of step 0 and the
+    // row scales into LDS by DMA (one 4-byte lane per entry).
+    auto post_rows = [&](int c0, int *jv) {
+        const int cn = min(kIdx, n_keys - c0);
+#pragma unroll
+        for (int i = 0; i < kEnt; ++i) {
+            const int e = tid + kThreads * i;
+            jv[i] = e < cn && jv[i] >= 0 && jv[i] <= pos ? jv[i] : -1;
+            s_row[e] = jv[i];
+        }
+        lds_barrier();                                   // rows posted
+#pragma unroll
+        for (int u = 0; u < kDmaStep; ++u) dma_go(0, u, dma_row(0, u));
+        const uint8_t *scale0 = a.kv_scale + kv0 * a.scale_stride;   // scale of row 0
+#pragma unroll
+        for (int i = 0; i < kEnt; ++i)                   // masked entries fetch row 0's
+            dma4_opaque(scale0, (uint32_t)max(jv[i], 0) * (uint32_t)a.scale_stride, &s_sig[kThreads * i + kWave * wv]);
+    };
+    auto gather_step1 = [&]() {
+#pragma unroll
+        for (int u = 0; u < kDmaStep; ++u) dma_go(1, u, dma_row(1, u));
+    };
+
     // every row-table entry the gather may read holds -1 or a row of this
     // sequence before the first chunk's table lands
     for (int e = tid; e < kIdx + kPad; e += kThreads) s_row[e] = -1;
+    // The first chunk is staged here, before the loops: the Q split and trade
+    // run while its step 0 and scales fly (the compiler's waits for the Q
+    // loads stay exact: loads complete in issue order and the gathers were
+    // issued after them), and the raw Q registers die before the step loop.
+    post_rows(0, j0);
+    trade_q();
+    gather_step1();
+    bool staged = true;                           // the next chunk's rows and first gathers are in flight
 
     bool need_init = true;                        // reference max not yet set (uniform)
     for (;;) {                                    // attempts: one unless a block overshoots
@@ -303,81 +428,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     for (int c0 = 0; c0 < n_keys && !redo; c0 += kIdx) {
         const int cn = min(kIdx, n_keys - c0);
         const int n_steps = (cn + kStepBlocks * kBlk - 1) / (kStepBlocks * kBlk);
-        const int n_ent = n_steps * kStepBlocks * kBlk;
-        // entry table: rows posted, then the row scales gathered into LDS by
-        // DMA (one 4-byte lane per entry) together with the first two steps
-        int jv[kEnt];
-        if (c0 == 0) {               // uniform
-#pragma unroll
-            for (int i = 0; i < kEnt; ++i) jv[i] = j0[i];
-        } else {
+        if (!staged) {               // uniform: later chunks and redo attempts
+            int jv[kEnt];
 #pragma unroll
             for (int i = 0; i < kEnt; ++i) {
                 const int e = tid + kThreads * i;
                 jv[i] = DENSE ? c0 + e : idx_row[c0 + min(e, cn - 1)];   // unconditional loads
             }
+            post_rows(c0, jv);
+            gather_step1();
         }
-#pragma unroll
-        for (int i = 0; i < kEnt; ++i) {
-            const int e = tid + kThreads * i;
-            jv[i] = e < cn && jv[i] >= 0 && jv[i] <= pos ? jv[i] : -1;
-            s_row[e] = jv[i];
-        }
-        lds_barrier();                                   // rows posted
-        // DMA instructions of this wave in a step: u < 8 are main instructions
-        // ins = wv + 4u (block ins >> 4, main instruction ins & 15 of it); u = 8
-        // is tail instruction wv & 1 of block wv >> 1. Entries past the chunk
-        // (the pipeline's tail) hold -1 or a row of an earlier chunk of this
-        // query, both fetched harmlessly (row 0 for -1) and never used.
-        // (lane terms pass through an empty asm at each use, so they are
-        // recomputed rather than hoisted into registers for every instruction)
-        auto dma_row = [&](int s, int u) -> int {
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            int e;
-            if (u < 8) {
-                const int ins = wv + kWaves * u;
-                e = kStepBlocks * kBlk * s + kBlk * (ins >> 4) + 2 * (ins & 15) + (ln >> 5);
-            } else {
-                e = kStepBlocks * kBlk * s + kBlk * (wv >> 1) + 16 * (wv & 1) + (ln >> 2);
-            }
-            return max(s_row[e], 0);
-        };
-        auto dma_go = [&](int s, int u, int j) {
-            int dm = dma_main, dt = dma_tail;
-            asm volatile("" : "+v"(dm), "+v"(dt));
-            uint32_t coff;
-            uint8_t *dst = ring + (s % kRingSteps) * kStepBytes;
-            if (u < 8) {
-                const int ins = wv + kWaves * u, k = ins & 15;
-                coff = 16u * (uint32_t)(dm ^ ((((2 * k) & 7) << 1) | ((k >> 3) & 1)));
-                dst += (ins >> 4) * kBlockBytes + k * 1024;
-            } else {
-                const int t = wv & 1;
-                coff = (uint32_t)kMainPitch + 16u * (uint32_t)(dt ^ (t << 1));
-                dst += (wv >> 1) * kBlockBytes + kTailBase + t * 1024;
-            }
-            dma16_opaque(kvq, (uint32_t)j * (uint32_t)a.kv_stride + coff, dst);
-        };
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int u = 0; u < kDmaStep; ++u) dma_go(s, u, dma_row(s, u));
-        {
-            const uint8_t *scale0 = a.kv_scale + kv0 * a.scale_stride;   // scale of row 0
-#pragma unroll
-            for (int i = 0; i < kEnt; ++i)                   // masked entries fetch row 0's
-                dma4_opaque(scale0, (uint32_t)max(jv[i], 0) * (uint32_t)a.scale_stride,
-                            &s_sig[kThreads * i + kWave * wv]);
-        }
-        // a wait the compiler sees (it cannot count the gathers): nothing it
-        // issued stays in flight into the steps, whose counter is kept by hand
-        __builtin_amdgcn_s_waitcnt(0x0f70);              // vmcnt(0): also steps 0 and 1 landed
-        lds_barrier();               // scales and steps 0, 1 everywhere
+        staged = false;
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaStep) : "memory");   // step 0 and the scales landed
+        lds_barrier();               // scales and step 0 everywhere
 #pragma unroll
         for (int i = 0; i < kEnt; ++i) {                 // this thread's entries
             const int e = tid + kThreads * i;
-            const bool v = jv[i] >= 0;
+            const bool v = s_row[e] >= 0;
             s_mul[e] = v ? s_sig[e] * a.scale_log2 : 0.f;
             s_bias[e] = v ? 0.f : -INFINITY;
         }
@@ -393,7 +460,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 const f32x4 mu = *(const f32x4 *)&s_mul[e0 + 4 * i];
                 const f32x4 bi = *(const f32x4 *)&s_bias[e0 + 4 * i];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaf(s_cur[4 * i + j], mu[j] * qinv, bi[j]));
+                for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaf(s_cur[4 * i + j], mu[j], bi[j]));
             }
             m_run = group_max(mx);
             need_init = false;
@@ -427,7 +494,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 }
                 if (p >= 2) {
                     const int k = p - 2, i = k >> 2, j = k & 3;
-                    const float t = fmaf(s_cur[k], mu[i][j] * qinv, bi[i][j]);
+                    const float t = fmaf(s_cur[k], mu[i][j], bi[i][j]);
                     mx = fmaxf(mx, t);
                     const float pr = __builtin_amdgcn_exp2f(fminf(t - msub, kClampLog2));
                     l_run += pr;
@@ -468,7 +535,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             if (g == 0) s_pe[wv][col] = 127 + pe;
             i32x8 vn = v_ld(kstep, 0);
             lds_barrier();           // weights of both blocks posted
-            // A: own weights in bytes 0..15, the partner's (same heads, same
+            // B: own weights in bytes 0..15, the partner's (same heads, same
             // rows of its block) in bytes 16..31; lane half 0 carries the own
             // block's scale, half 1 the partner's
             const u32x4 hp = s_ph[wv ^ 2][g][col], lp = s_pl[wv ^ 2][g][col];
@@ -506,16 +573,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         a.lse[(int64_t)qi * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
 
+    // lane (head col, g) holds dims 32 nb + 8 i + 4 g .. +3 of its head in
+    // accumulator elements 4 i .. 4 i + 3 of tile nb
     __bf16 *stage = (__bf16 *)smem + wv * 32 * O_LD;          // 32 heads x 256 bf16 per wave
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int nb = 0; nb < kOwn; ++nb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int hr = 8 * i + 4 * g + j;
-            const float ir = __shfl(inv, hr);
+        for (int i = 0; i < 4; ++i) {
+            bf16x4 v;
 #pragma unroll
-            for (int nb = 0; nb < kOwn; ++nb)
-                stage[hr * O_LD + 32 * nb + col] = (__bf16)(o[nb][4 * i + j] * ir);
+            for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[nb][4 * i + j] * inv);
+            *(bf16x4 *)(stage + col * O_LD + 32 * nb + 8 * i + 4 * g) = v;
         }
     lds_barrier();
     // 32 rows x 512 B per wave: two rows per pass, 16 B per lane
