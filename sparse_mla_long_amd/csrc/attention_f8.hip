@@ -64,16 +64,17 @@ constexpr int kEnt = kIdx / 256;                           // table entries per 
 constexpr int kPairs = kQK / 32;                           // 16-byte K chunks per lane half
 constexpr int kKB = kQK / 64;                              // QK k-blocks of the FP8 MFMA
 constexpr int kOwn = kV / 64;                              // output tiles (32 dims) per wave
-constexpr int O_LD = 32 * kOwn + 8;                        // epilogue staging pitch (bf16)
+constexpr int O_LD = 16 * kOwn + 8;                        // epilogue staging pitch (bf16): 128 dims a pass
 
 constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
-constexpr size_t kStaticBytes = (size_t)kIdx * 16 + kPad * 4 + kWaves * 2 * 2 * 32 * 16 + kWaves * 32 * 4 +
+constexpr size_t kStaticBytes = (size_t)kIdx * 20 + kPad * 4 + kWaves * 2 * 2 * 32 * 16 + kWaves * 32 * 4 +
                                  2 * 2 * 32 * 4 + kWaves * 4 + 2 * kKB * 32;
 static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
 static_assert(kDmaStep * kWaves * 1024 == kStepBytes, "DMA split");
 static_assert(kTailBase + kBlk * kTailPitch == kBlockBytes, "block layout");
 static_assert(kEnt * kThreads == kIdx, "table split");
-static_assert((size_t)kWaves * 32 * O_LD * 2 <= kLdsBytes, "staging fits the ring");
+static_assert((size_t)kWaves * 32 * O_LD * 2 <= kStepBytes, "staging fits a ring slot");
+static_assert(kKB * kWaves * 1024 == kStepBytes, "a head group's Q fills a ring slot");
 
 template <int N> using IC = std::integral_constant<int, N>;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -109,6 +110,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     __shared__ __attribute__((aligned(16))) float s_sig[kIdx];      // sigma_j (row scale)
     __shared__ __attribute__((aligned(16))) float s_mul[kIdx];      // sigma_j * scale * log2e, or 0
     __shared__ __attribute__((aligned(16))) float s_bias[kIdx];     // 0, or -inf if masked
+    __shared__ __attribute__((aligned(16))) int32_t s_next[kIdx];   // index list of the next query (raw)
     __shared__ u32x4 s_ph[kWaves][2][32];                           // PV weights, E4M3 hi: [wave][g][head]
     __shared__ u32x4 s_pl[kWaves][2][32];                           // E4M3 lo
     __shared__ int s_pe[kWaves][32];                                // E8M0 block scale per head
@@ -119,18 +121,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
     const int hg = wv & 1, half = wv >> 1;
     const int tid = threadIdx.x;
-    const int qi = a.batch.total_q - 1 - (int)blockIdx.x;
-    const int b = seq_of_row(a.batch.cu_q, a.batch.num_seqs, qi);
-    const int64_t kv0 = a.batch.cu_kv[b];
-    const int L = a.batch.cu_kv[b + 1] - (int)kv0;
-    const int pos = min(a.batch.q_pos[qi], L - 1);
     const int H = a.n_heads;
-    const int n_keys = DENSE ? pos + 1 : a.k;
-    const int32_t *idx_row = DENSE ? nullptr : a.indices + (int64_t)qi * a.k;
-    const uint8_t *kvq = a.kv + kv0 * a.kv_stride;                   // row 0 of this sequence
-
     const int head = 32 * hg + col;
     const bool hv = head < H;
+    const int total_q = a.batch.total_q;
+
+    // Persistent workgroup: its k-th query in snake order over the rows, last
+    // rows first (they have the most keys in causal batches), so the
+    // workgroups' totals stay even. -1 past the end.
+    auto query_of = [&](int k) -> int {
+        const int G = (int)gridDim.x, bx = (int)blockIdx.x;
+        const int r = k * G + ((k & 1) ? G - 1 - bx : bx);
+        return r < total_q ? total_q - 1 - r : -1;
+    };
+    // the current query and chunk (wave-uniform)
+    int qi = 0, qn = -1;                         // this query, the next one (or -1)
+    int pos = 0, n_keys = 0, n_steps = 1;
+    int64_t kv0 = 0;
+    const int32_t *idx_row = nullptr;
+    const uint8_t *kvq = a.kv;                   // row 0 of this query's sequence
+    int cb = 0;                                  // ring slot of the chunk's step 0
+    bool q_next = false;                         // the chunk is the query's last and qn >= 0
+
     // Q^T as two E4M3 operands (B of the 32x32x64 FP8 MFMA). K-block kb (dims
     // of chunks 4kb + g and 4kb + 2 + g for lane half g) is operand kb; byte
     // order follows the K rows in LDS. Per head and k-block, Q is scaled by
@@ -140,49 +152,33 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     // 8 significant bits and the residual is a multiple of its last bit no
     // larger than half a step of hi, so hi + lo is exact unless lo falls below
     // the E4M3 subnormal range (elements 2^10 below the block's largest, off by
-    // at most 2^-18 of it). The two waves of a head group split half of the
-    // k-blocks each (kKB0 and the rest) and trade the operands through LDS.
+    // at most 2^-18 of it).
+    //
+    // A query's Q lands in LDS by DMA ahead of it (during the previous query's
+    // last two steps): head group h in ring slot (cb + 1 + h) % 3, 16-byte
+    // chunk (kb, pp, e) of lane (head col, g) -- dims 64 kb + 32 pp + 16 g +
+    // 8 e .. +7 -- at 1024 (4 kb + 2 pp + e) + 16 lane, conflict-free for the
+    // split's reads. The two waves of a head group split half of the k-blocks
+    // each (kKB0 and the rest; the half-1 wave's fifth block repeats block
+    // kKB - 1 and is dropped) in place, hi over chunk e = 0 and lo over e = 1,
+    // then every wave reads all nine blocks back, so no register array is
+    // indexed by a wave-dependent value.
     constexpr int kKB0 = 5;                      // k-blocks split by the half-0 wave (it takes 0 .. 4)
     i32x8 qh[kKB], ql[kKB];
-    uint32_t qsc[(kKB + 3) / 4] = {};
-    // index entries of the first chunk, loaded ahead of Q so the row table
-    // does not wait for it
-    int j0[kEnt];
-#pragma unroll
-    for (int i = 0; i < kEnt; ++i) {
-        const int e = tid + kThreads * i, cn0 = min(kIdx, n_keys);
-        j0[i] = DENSE ? e : idx_row[min(e, cn0 - 1)];                   // unconditional load
-    }
-    // The wave's k-blocks kbase + kl (kl < kKB0; the half-1 wave's last one
-    // repeats block kKB - 1 and is not posted): dims 64 kb + 32 pp + 16 g ..
-    // +15 of pair pp. Lanes of heads past n_heads load head 0 and compute on
-    // it; nothing of theirs is stored. (Unconditional loads: no branch, all in
-    // flight at once.)
+    uint32_t qsc[(kKB + 3) / 4];
     const int kbase = half == 0 ? 0 : kKB0;
-    bf16x8 qraw[kKB0][2][2];
-    {
-        const __bf16 *qrow = a.q + ((int64_t)qi * H + (hv ? head : 0)) * kQK + 16 * g;
+    auto trade_q = [&]() {
+        int ln = lane;                           // recomputed here, not held across the loop
+        asm volatile("" : "+v"(ln));
+        uint8_t *qs_hg = ring + ((cb + 1 + hg) % kRingSteps) * kStepBytes + 16 * ln;
 #pragma unroll
-        for (int kl = 0; kl < kKB0; ++kl)
+        for (int kl = 0; kl < kKB0; ++kl) {
+            const int kb = min(kbase + kl, kKB - 1);
+            bf16x8 raw[2][2];
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-                for (int e = 0; e < 2; ++e)
-                    qraw[kl][pp][e] = *(const bf16x8 *)(qrow + 64 * min(kbase + kl, kKB - 1) + 32 * pp + 8 * e);
-    }
-    // The split, traded with the partner (wave w ^ 2, same heads and lanes)
-    // through ring slots 1 and 2, free until the first gathers of step 1:
-    // k-block kbase + kl of wave w at xq(w) + 4096 kl + 1024 u + 16 lane (u:
-    // hi dwords 0..3, 4..7, lo dwords 0..3, 4..7), its scale code in s_qcode.
-    // Every wave then reads all nine blocks back, so no register array is
-    // indexed by a wave-dependent value.
-    auto trade_q = [&]() {
-        auto xq = [&](int w) {
-            const int hf = w >> 1, hgw = w & 1;
-            return ring + kStepBytes + 4096 * (hf == 0 ? hgw * kKB0 : 2 * kKB0 + hgw * (kKB - kKB0));
-        };
-#pragma unroll
-        for (int kl = 0; kl < kKB0; ++kl) {
+                for (int e = 0; e < 2; ++e) raw[pp][e] = *(const bf16x8 *)(qs_hg + 1024 * (4 * kb + 2 * pp + e));
             // largest |q| of the head over the block: bf16 magnitudes order as
             // the integers in their low 15 bits (two per dword, packed u16 max)
             u16x2 m2 = {0, 0};
@@ -190,7 +186,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const u32x4 w = __builtin_bit_cast(u32x4, qraw[kl][pp][e]);
+                    const u32x4 w = __builtin_bit_cast(u32x4, raw[pp][e]);
 #pragma unroll
                     for (int d = 0; d < 4; ++d)
                         m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[d] & 0x7fff7fffu));
@@ -199,44 +195,46 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             m = max(m, __float_as_uint(xor32(__uint_as_float(m))));
             const int ex = max(__builtin_amdgcn_frexp_expf(__uint_as_float(m)), -119);
             const float qs = __builtin_ldexpf(1.f, 8 - ex);
-            int hw[8], lw[8];
+            u32x4 hw[2], lw[2];
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {           // dword d of the pair: dims 4d .. 4d+3
                     float x[4];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) x[k] = (float)qraw[kl][pp][d >> 1][4 * (d & 1) + k] * qs;
+                    for (int k = 0; k < 4; ++k) x[k] = (float)raw[pp][d >> 1][4 * (d & 1) + k] * qs;
                     int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
                     hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hi, true);
                     const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
                     const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
                     int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - b0[0], x[1] - b0[1], 0, false);
                     lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b1[0], x[3] - b1[1], lo, true);
-                    hw[4 * pp + d] = hi;
-                    lw[4 * pp + d] = lo;
+                    hw[pp][d] = (uint32_t)hi;
+                    lw[pp][d] = (uint32_t)lo;
                 }
             if (kl < kKB - kKB0 || half == 0) {  // uniform
-                uint8_t *x = xq(wv) + 4096 * kl + 16 * lane;
-                *(u32x4 *)(x) = u32x4{(uint32_t)hw[0], (uint32_t)hw[1], (uint32_t)hw[2], (uint32_t)hw[3]};
-                *(u32x4 *)(x + 1024) = u32x4{(uint32_t)hw[4], (uint32_t)hw[5], (uint32_t)hw[6], (uint32_t)hw[7]};
-                *(u32x4 *)(x + 2048) = u32x4{(uint32_t)lw[0], (uint32_t)lw[1], (uint32_t)lw[2], (uint32_t)lw[3]};
-                *(u32x4 *)(x + 3072) = u32x4{(uint32_t)lw[4], (uint32_t)lw[5], (uint32_t)lw[6], (uint32_t)lw[7]};
-                if (g == 0) s_qcode[hg][kbase + kl][col] = (uint8_t)(119 + ex);   // E8M0 of 2^(ex - 8)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    *(u32x4 *)(qs_hg + 1024 * (4 * kb + 2 * pp)) = hw[pp];
+                    *(u32x4 *)(qs_hg + 1024 * (4 * kb + 2 * pp + 1)) = lw[pp];
+                }
+                if (g == 0) s_qcode[hg][kb][col] = (uint8_t)(119 + ex);   // E8M0 of 2^(ex - 8)
             }
         }
         lds_barrier();                           // both halves posted
 #pragma unroll
+        for (int i = 0; i < (kKB + 3) / 4; ++i) qsc[i] = 0;
+#pragma unroll
         for (int kb = 0; kb < kKB; ++kb) {
-            const int oh = kb < kKB0 ? 0 : 1;        // the half that split it
-            const uint8_t *x = xq(hg + 2 * oh) + 4096 * (kb - kKB0 * oh) + 16 * lane;
-            const u32x4 h0 = *(const u32x4 *)(x), h1 = *(const u32x4 *)(x + 1024);
-            const u32x4 l0 = *(const u32x4 *)(x + 2048), l1 = *(const u32x4 *)(x + 3072);
+            const u32x4 h0 = *(const u32x4 *)(qs_hg + 1024 * (4 * kb));
+            const u32x4 l0 = *(const u32x4 *)(qs_hg + 1024 * (4 * kb + 1));
+            const u32x4 h1 = *(const u32x4 *)(qs_hg + 1024 * (4 * kb + 2));
+            const u32x4 l1 = *(const u32x4 *)(qs_hg + 1024 * (4 * kb + 3));
             qh[kb] = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
             ql[kb] = i32x8{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
             qsc[kb >> 2] |= (uint32_t)s_qcode[hg][kb][col] << (8 * (kb & 3));
         }
-        lds_barrier();                           // traded: slot 1 may take its gather
+        lds_barrier();                           // traded: the Q slots may take gathers
     };
 
     // DMA lane constants. Main instruction k of a block (k < 16) moves rows
@@ -347,262 +345,373 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         return r;
     };
 
-    // DMA instructions of this wave in a step: u < 8 are main instructions
-    // ins = wv + 4u (block ins >> 4, main instruction ins & 15 of it); u = 8 is
-    // tail instruction wv & 1 of block wv >> 1. Entries past the chunk (the
-    // pipeline's tail) hold -1 or a row of an earlier chunk of this query,
-    // both fetched harmlessly (row 0 for -1) and never used. (Lane terms pass
-    // through an empty asm at each use, so they are recomputed rather than
-    // hoisted into registers for every instruction.)
-    auto dma_row = [&](int s, int u) -> int {
+    // Gathers. Virtual step v of a chunk lands in ring slot (cb + v) % 3: v <
+    // n_steps are its key steps; v = n_steps, n_steps + 1 carry the next
+    // query's Q (head groups 0, 1) when the chunk is the query's last, and
+    // otherwise nothing is gathered. DMA instructions of this wave in a key
+    // step: u < 8 are main instructions ins = wv + 4u (block ins >> 4, main
+    // instruction ins & 15 of it); u = 8 is tail instruction wv & 1 of block
+    // wv >> 1. Table entries past the chunk hold -1 (row 0, fetched and never
+    // used). (Lane terms pass through an empty asm at each use, so they are
+    // recomputed rather than hoisted into registers for every instruction.)
+    auto dma_row = [&](int v, int u) -> int {
         int ln = lane;
         asm volatile("" : "+v"(ln));
         int e;
         if (u < 8) {
             const int ins = wv + kWaves * u;
-            e = kStepBlocks * kBlk * s + kBlk * (ins >> 4) + 2 * (ins & 15) + (ln >> 5);
+            e = kStepBlocks * kBlk * v + kBlk * (ins >> 4) + 2 * (ins & 15) + (ln >> 5);
         } else {
-            e = kStepBlocks * kBlk * s + kBlk * (wv >> 1) + 16 * (wv & 1) + (ln >> 2);
+            e = kStepBlocks * kBlk * v + kBlk * (wv >> 1) + 16 * (wv & 1) + (ln >> 2);
         }
         return max(s_row[e], 0);
     };
-    auto dma_go = [&](int s, int u, int j) {
+    auto dma_go = [&](int slot, int u, int j) {
         int dm = dma_main, dt = dma_tail;
         asm volatile("" : "+v"(dm), "+v"(dt));
         uint32_t coff;
-        uint8_t *dst = ring + (s % kRingSteps) * kStepBytes;
+        uint32_t dst = lds_addr(smem) + (uint32_t)(slot * kStepBytes);
         if (u < 8) {
             const int ins = wv + kWaves * u, k = ins & 15;
             coff = 16u * (uint32_t)(dm ^ ((((2 * k) & 7) << 1) | ((k >> 3) & 1)));
-            dst += (ins >> 4) * kBlockBytes + k * 1024;
+            dst += (uint32_t)((ins >> 4) * kBlockBytes + k * 1024);
         } else {
             const int t = wv & 1;
             coff = (uint32_t)kMainPitch + 16u * (uint32_t)(dt ^ (t << 1));
-            dst += (wv >> 1) * kBlockBytes + kTailBase + t * 1024;
+            dst += (uint32_t)((wv >> 1) * kBlockBytes + kTailBase + t * 1024);
         }
-        dma16_opaque(kvq, (uint32_t)j * (uint32_t)a.kv_stride + coff, dst);
+        dma16_lds(kvq, (uint32_t)j * (uint32_t)a.kv_stride + coff, dst);
+    };
+    // Q of query q, head group h, into ring slot `slot`: instruction u of this
+    // wave is chunk (kb, pp, e) = (u, (wv >> 1) & 1, wv & 1), 1 KB at
+    // 1024 (wv + 4u). Heads past n_heads fetch head 0.
+    auto q_lane = [&](int h) -> uint32_t {
+        const int hq = 32 * h + col;
+        return (uint32_t)(hq < H ? hq : 0) * (kQK * 2) + 32u * (uint32_t)g + 64u * (uint32_t)((wv >> 1) & 1) +
+               16u * (uint32_t)(wv & 1);
+    };
+    auto q_one = [&](int q, uint32_t lo, int slot, int u) {
+        dma16_lds(a.q + (int64_t)q * H * kQK, lo + 128u * (uint32_t)u,
+                  lds_addr(smem) + (uint32_t)(slot * kStepBytes + (wv + kWaves * u) * 1024));
+    };
+    auto q_go = [&](int q, int h, int slot) {
+        const uint32_t lo = q_lane(h);
+#pragma unroll
+        for (int u = 0; u < kKB; ++u) q_one(q, lo, slot, u);
+    };
+    // thread index as a value the compiler cannot hoist: per-entry offsets
+    // derived from it are recomputed at each use instead of held (and
+    // spilled) across the query loop, whose reloads would wait for the
+    // gathers in flight
+    auto tid_opq = [&]() {
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        return t;
+    };
+    // index list of query q into s_next (entries past the list repeat its last)
+    auto fetch_idx = [&](int q) {
+        const int cn0 = min(kIdx, a.k), t = tid_opq();
+        const int32_t *ib = a.indices + (int64_t)q * a.k;
+#pragma unroll
+        for (int i = 0; i < kEnt; ++i)
+            dma4_lds(ib, 4u * (uint32_t)min(t + kThreads * i, cn0 - 1), lds_addr(s_next) + 4u * (uint32_t)(kThreads * i + kWave * wv));
     };
     // Row table of the chunk starting at entry c0 (jv: its raw entries of this
     // thread): rows posted (-1 where masked), then the gather of step 0 and the
     // row scales into LDS by DMA (one 4-byte lane per entry).
     auto post_rows = [&](int c0, int *jv) {
-        const int cn = min(kIdx, n_keys - c0);
+        const int cn = min(kIdx, n_keys - c0), t = tid_opq();
 #pragma unroll
         for (int i = 0; i < kEnt; ++i) {
-            const int e = tid + kThreads * i;
+            const int e = t + kThreads * i;
             jv[i] = e < cn && jv[i] >= 0 && jv[i] <= pos ? jv[i] : -1;
             s_row[e] = jv[i];
         }
         lds_barrier();                                   // rows posted
 #pragma unroll
-        for (int u = 0; u < kDmaStep; ++u) dma_go(0, u, dma_row(0, u));
+        for (int u = 0; u < kDmaStep; ++u) dma_go(cb, u, dma_row(0, u));
         const uint8_t *scale0 = a.kv_scale + kv0 * a.scale_stride;   // scale of row 0
 #pragma unroll
         for (int i = 0; i < kEnt; ++i)                   // masked entries fetch row 0's
-            dma4_opaque(scale0, (uint32_t)max(jv[i], 0) * (uint32_t)a.scale_stride, &s_sig[kThreads * i + kWave * wv]);
+            dma4_lds(scale0, (uint32_t)max(jv[i], 0) * (uint32_t)a.scale_stride, lds_addr(s_sig) + 4u * (uint32_t)(kThreads * i + kWave * wv));
     };
-    auto gather_step1 = [&]() {
+    // virtual step 1: key step 1, or the next query's Q head group 0, or
+    // nothing; true if it issued (kDmaStep instructions)
+    auto gather_v1 = [&]() -> bool {
+        const int sl1 = cb == kRingSteps - 1 ? 0 : cb + 1;
+        if (n_steps > 1) {                               // uniform
 #pragma unroll
-        for (int u = 0; u < kDmaStep; ++u) dma_go(1, u, dma_row(1, u));
+            for (int u = 0; u < kDmaStep; ++u) dma_go(sl1, u, dma_row(1, u));
+            return true;
+        }
+        if (q_next) {
+            q_go(qn, 0, sl1);
+            return true;
+        }
+        return false;
+    };
+    auto chunk_steps = [&](int c0) { return (min(kIdx, n_keys - c0) + kStepBlocks * kBlk - 1) / (kStepBlocks * kBlk); };
+    auto set_query = [&](int q) {
+        qi = q;
+        const int b = seq_of_row(a.batch.cu_q, a.batch.num_seqs, qi);
+        kv0 = a.batch.cu_kv[b];
+        const int L = a.batch.cu_kv[b + 1] - (int)kv0;
+        pos = min(a.batch.q_pos[qi], L - 1);
+        n_keys = DENSE ? pos + 1 : a.k;
+        idx_row = DENSE ? nullptr : a.indices + (int64_t)qi * a.k;
+        kvq = a.kv + kv0 * a.kv_stride;
     };
 
-    // every row-table entry the gather may read holds -1 or a row of this
-    // sequence before the first chunk's table lands
+    // every row-table entry the gather may read holds -1 or a row of the
+    // current query's sequence
     for (int e = tid; e < kIdx + kPad; e += kThreads) s_row[e] = -1;
-    // The first chunk is staged here, before the loops: the Q split and trade
-    // run while its step 0 and scales fly (the compiler's waits for the Q
-    // loads stay exact: loads complete in issue order and the gathers were
-    // issued after them), and the raw Q registers die before the step loop.
-    post_rows(0, j0);
-    trade_q();
-    gather_step1();
-    bool staged = true;                           // the next chunk's rows and first gathers are in flight
-
-    bool need_init = true;                        // reference max not yet set (uniform)
-    for (;;) {                                    // attempts: one unless a block overshoots
-#pragma unroll
-    for (int nb = 0; nb < kOwn; ++nb) o[nb] = zero16();
-    l_run = 0.f;
-    bool redo = false;
-    bool my_vote = false;                         // wave-uniform
-    for (int c0 = 0; c0 < n_keys && !redo; c0 += kIdx) {
-        const int cn = min(kIdx, n_keys - c0);
-        const int n_steps = (cn + kStepBlocks * kBlk - 1) / (kStepBlocks * kBlk);
-        if (!staged) {               // uniform: later chunks and redo attempts
-            int jv[kEnt];
-#pragma unroll
-            for (int i = 0; i < kEnt; ++i) {
-                const int e = tid + kThreads * i;
-                jv[i] = DENSE ? c0 + e : idx_row[c0 + min(e, cn - 1)];   // unconditional loads
-            }
-            post_rows(c0, jv);
-            gather_step1();
-        }
-        staged = false;
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaStep) : "memory");   // step 0 and the scales landed
-        lds_barrier();               // scales and step 0 everywhere
-#pragma unroll
-        for (int i = 0; i < kEnt; ++i) {                 // this thread's entries
-            const int e = tid + kThreads * i;
-            const bool v = s_row[e] >= 0;
-            s_mul[e] = v ? s_sig[e] * a.scale_log2 : 0.f;
-            s_bias[e] = v ? 0.f : -INFINITY;
-        }
-        lds_barrier();               // table complete
-
-        // prologue: logits of block `half` of step 0 (and the reference max)
-        f32x16 s_cur = qk(ring + half * kBlockBytes, true, [](int) {});
-        if (need_init) {             // uniform: the first chunk of the first attempt
-            const int e0 = half * kBlk + 16 * g;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 mu = *(const f32x4 *)&s_mul[e0 + 4 * i];
-                const f32x4 bi = *(const f32x4 *)&s_bias[e0 + 4 * i];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaf(s_cur[4 * i + j], mu[j], bi[j]));
-            }
-            m_run = group_max(mx);
-            need_init = false;
-        }
-        const float msub = m_run == -INFINITY ? 0.f : m_run;
-
-        // step s: logits of step s + 1 (QK MFMAs) interleaved with the softmax
-        // of step s and the issue of the gather of step s + 2; then PV of step s
-        for (int s = 0; s < n_steps; ++s) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // step s + 1 landed
-            lds_barrier();           // step s + 1 everywhere; PV of step s - 1 done
-
-            const int e0 = (kStepBlocks * s + half) * kBlk + 16 * g;      // entry of LDS row 16g
-            const uint8_t *kstep = ring + (s % kRingSteps) * kStepBytes;
-            const uint8_t *knext = ring + ((s + 1) % kRingSteps) * kStepBytes + half * kBlockBytes;
-            // gather of step s + 2 into the slots of step s - 1: row of
-            // instruction u read in QK pair 2u, the DMA issued in pair 2u + 1
-            int jn = 0;
-            // softmax of step s: group i of the scales read in pair 4i, key k
-            // finished in pair k + 2
-            f32x4 mu[4], bi[4], sg[4];
-            float mx = -INFINITY;
-            float pw[16];            // probability times sigma_j: the PV weight
-            auto hook = [&](int p) {
-                if ((p & 1) == 1 && (p >> 1) < kDmaStep) dma_go(s + 2, p >> 1, jn);
-                if ((p & 1) == 0 && (p >> 1) < kDmaStep) jn = dma_row(s + 2, p >> 1);
-                if ((p & 3) == 0 && (p >> 2) < 4) {
-                    mu[p >> 2] = *(const f32x4 *)&s_mul[e0 + p];
-                    bi[p >> 2] = *(const f32x4 *)&s_bias[e0 + p];
-                    sg[p >> 2] = *(const f32x4 *)&s_sig[e0 + p];
-                }
-                if (p >= 2) {
-                    const int k = p - 2, i = k >> 2, j = k & 3;
-                    const float t = fmaf(s_cur[k], mu[i][j], bi[i][j]);
-                    mx = fmaxf(mx, t);
-                    const float pr = __builtin_amdgcn_exp2f(fminf(t - msub, kClampLog2));
-                    l_run += pr;
-                    pw[k] = pr * sg[i][j];
-                }
-            };
-            static_assert(kPairs == 16 + 2 && 2 * kDmaStep <= kPairs, "hook schedule");
-            const f32x16 s_next = qk(knext, s + 1 < n_steps, hook);
-            m_seen = fmaxf(m_seen, mx);
-            // also catches valid keys while the reference is unset (-inf)
-            my_vote |= __any(mx > m_run + kHeadroom);
-
-            // PV weights of the own block as E4M3 hi + lo under a per-head E8M0
-            // scale 2^pe (the block's largest weight lands in [128, 256)); the
-            // lane's 16 keys are LDS rows 16g .. 16g+15, piece g of the 32
-            float pmax = 0.f;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) pmax = fmaxf(pmax, pw[k]);
-            pmax = fmaxf(pmax, xor32(pmax));
-            const int pe = min(max(__builtin_amdgcn_frexp_expf(pmax) - 8, -127), 127);
-            u32x4 ph, pl;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                float x[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) x[q] = __builtin_ldexpf(pw[4 * d + q], -pe);
-                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hi, true);
-                const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-                const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - b0[0], x[1] - b0[1], 0, false);
-                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b1[0], x[3] - b1[1], lo, true);
-                ph[d] = (uint32_t)hi;
-                pl[d] = (uint32_t)lo;
-            }
-            s_ph[wv][g][col] = ph;
-            s_pl[wv][g][col] = pl;
-            if (g == 0) s_pe[wv][col] = 127 + pe;
-            i32x8 vn = v_ld(kstep, 0);
-            lds_barrier();           // weights of both blocks posted
-            // B: own weights in bytes 0..15, the partner's (same heads, same
-            // rows of its block) in bytes 16..31; lane half 0 carries the own
-            // block's scale, half 1 the partner's
-            const u32x4 hp = s_ph[wv ^ 2][g][col], lp = s_pl[wv ^ 2][g][col];
-            const i32x8 ah = {(int)ph[0], (int)ph[1], (int)ph[2], (int)ph[3],
-                              (int)hp[0], (int)hp[1], (int)hp[2], (int)hp[3]};
-            const i32x8 al = {(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3],
-                              (int)lp[0], (int)lp[1], (int)lp[2], (int)lp[3]};
-            const int sa = g == 0 ? 127 + pe : s_pe[wv ^ 2][col];
-            pv(kstep, ah, al, sa, vn);
-            s_cur = s_next;
-        }
-        // the tail DMA must land before the ring is reused
+    // the first query's index list and Q, as a previous query would have left them
+    if (query_of(0) >= 0) {                       // uniform
+        const int q0 = query_of(0);
+        if (!DENSE) fetch_idx(q0);
+        q_go(q0, 0, 1);
+        q_go(q0, 1, 2);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        s_vote[wv] = my_vote ? 1 : 0;                // same value from every lane
-        lds_barrier();        // votes posted; every wave is done with the ring and the table
+        lds_barrier();
+    }
+
+    for (int k = 0;; ++k) {
+        const int q = query_of(k);
+        if (q < 0) break;                         // uniform
+        set_query(q);
+        qn = query_of(k + 1);
+        // chunk 0 staged ahead of the loops: its row table (from the index list
+        // prefetched into s_next), the gathers of its step 0, the next query's
+        // index list, the Q split and trade, then virtual step 1
+        n_steps = chunk_steps(0);
+        q_next = qn >= 0 && n_keys <= kIdx;
         {
-            const int4 v = *(const int4 *)&s_vote[0];
-            redo = (v.x | v.y | v.z | v.w) != 0;
+            int jv[kEnt];
+            const int t = tid_opq();
+#pragma unroll
+            for (int i = 0; i < kEnt; ++i) jv[i] = DENSE ? t + kThreads * i : s_next[t + kThreads * i];
+            post_rows(0, jv);
         }
-        lds_barrier();        // votes read before the next chunk posts again
-    }
-    if (!redo) break;
-    // redo the query with a larger reference: the head group's largest block max
-    m_run = fmaxf(m_run, group_max(m_seen));
-    }
+        if (!DENSE && qn >= 0) fetch_idx(qn);     // s_next is read; refill it
+        trade_q();
+        bool v1 = gather_v1();
+        bool staged = true;                       // chunk 0's table and first gathers are in flight
+        m_run = -INFINITY;
+        m_seen = -INFINITY;
+        bool need_init = true;                    // reference max not yet set (uniform)
+        for (;;) {                                // attempts: one unless a block overshoots
+#pragma unroll
+        for (int nb = 0; nb < kOwn; ++nb) o[nb] = zero16();
+        l_run = 0.f;
+        bool redo = false;
+        bool my_vote = false;                     // wave-uniform
+        for (int c0 = 0; c0 < n_keys && !redo; c0 += kIdx) {
+            n_steps = chunk_steps(c0);
+            q_next = qn >= 0 && c0 + kIdx >= n_keys;
+            if (!staged) {           // uniform: later chunks and redo attempts
+                const int cn = min(kIdx, n_keys - c0), t = tid_opq();
+                int jv[kEnt];
+#pragma unroll
+                for (int i = 0; i < kEnt; ++i) {
+                    const int e = t + kThreads * i;
+                    jv[i] = DENSE ? c0 + e : idx_row[c0 + min(e, cn - 1)];   // unconditional loads
+                }
+                post_rows(c0, jv);
+                v1 = gather_v1();
+            }
+            staged = false;
+            if (v1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaStep) : "memory");   // step 0 and the scales landed
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();           // scales and step 0 everywhere
+            const int tt = tid_opq();
+#pragma unroll
+            for (int i = 0; i < kEnt; ++i) {             // this thread's entries
+                const int e = tt + kThreads * i;
+                const bool v = s_row[e] >= 0;
+                s_mul[e] = v ? s_sig[e] * a.scale_log2 : 0.f;
+                s_bias[e] = v ? 0.f : -INFINITY;
+            }
+            lds_barrier();           // table complete
 
-    // ---- epilogue: l over both waves of the head group; LSE
-    {
-        const float lh = l_run + xor32(l_run);
-        if (g == 0) s_x[hg][half][col] = lh;
-    }
-    lds_barrier();
-    const float lt = s_x[hg][0][col] + s_x[hg][1][col];
-    if (half == 0 && g == 0 && hv)
-        a.lse[(int64_t)qi * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            // prologue: logits of block `half` of step 0 (and the reference max)
+            f32x16 s_cur = qk(ring + cb * kStepBytes + half * kBlockBytes, true, [](int) {});
+            if (need_init) {             // uniform: the first chunk of the first attempt
+                const int e0 = half * kBlk + 16 * g;
+                float mx = -INFINITY;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 mu = *(const f32x4 *)&s_mul[e0 + 4 * i];
+                    const f32x4 bi = *(const f32x4 *)&s_bias[e0 + 4 * i];
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaf(s_cur[4 * i + j], mu[j], bi[j]));
+                }
+                m_run = group_max(mx);
+                need_init = false;
+            }
+            const float msub = m_run == -INFINITY ? 0.f : m_run;
+            // step s: logits of step s + 1 (QK MFMAs) interleaved with the
+            // softmax of step s and the issue of the gather of step s + 2; then
+            // PV of step s
+            // Steps whose step s + 2 exists gather it in the hook (the main
+            // loop); the last two (the tail) instead carry the next query's Q
+            // when q_next, else nothing. sl: ring slot of step s.
+            int sl = cb;
+            auto step = [&](int s, auto TAIL) {
+                constexpr bool kTail = decltype(TAIL)::value != 0;
+                const int sl1 = sl == kRingSteps - 1 ? 0 : sl + 1;
+                const int sl2 = sl1 == kRingSteps - 1 ? 0 : sl1 + 1;
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // step s + 1 landed
+                lds_barrier();       // step s + 1 everywhere; PV of step s - 1 done
+                // tail: the next query's Q, head group s + 2 - n_steps, into
+                // the free slot (without a next query, this one's again, unused)
+                const int q_src = q_next ? qn : qi;
+                const uint32_t q_lo = kTail ? q_lane(s + 2 - n_steps) : 0u;
+                const int e0 = (kStepBlocks * s + half) * kBlk + 16 * g;      // entry of LDS row 16g
+                const uint8_t *kstep = ring + sl * kStepBytes;
+                const uint8_t *knext = ring + sl1 * kStepBytes + half * kBlockBytes;
+                // gather of step s + 2 into the slots of step s - 1: row of
+                // instruction u read in QK pair 2u, the DMA issued in pair 2u + 1
+                int jn = 0;
+                // softmax of step s: group i of the scales read in pair 4i, key k
+                // finished in pair k + 2
+                f32x4 mu[4], bi[4], sg[4];
+                float mx = -INFINITY;
+                float pw[16];            // probability times sigma_j: the PV weight
+                auto hook = [&](int p) {
+                    if (!kTail && (p & 1) == 1 && (p >> 1) < kDmaStep) dma_go(sl2, p >> 1, jn);
+                    if (!kTail && (p & 1) == 0 && (p >> 1) < kDmaStep) jn = dma_row(s + 2, p >> 1);
+                    if (kTail && (p & 1) == 1 && (p >> 1) < kKB) q_one(q_src, q_lo, sl2, p >> 1);
+                    if ((p & 3) == 0 && (p >> 2) < 4) {
+                        mu[p >> 2] = *(const f32x4 *)&s_mul[e0 + p];
+                        bi[p >> 2] = *(const f32x4 *)&s_bias[e0 + p];
+                        sg[p >> 2] = *(const f32x4 *)&s_sig[e0 + p];
+                    }
+                    if (p >= 2) {
+                        const int k = p - 2, i = k >> 2, j = k & 3;
+                        const float t = fmaf(s_cur[k], mu[i][j], bi[i][j]);
+                        mx = fmaxf(mx, t);
+                        const float pr = __builtin_amdgcn_exp2f(fminf(t - msub, kClampLog2));
+                        l_run += pr;
+                        pw[k] = pr * sg[i][j];
+                    }
+                };
+                static_assert(kPairs == 16 + 2 && 2 * kDmaStep <= kPairs, "hook schedule");
+                const f32x16 s_next = qk(knext, s + 1 < n_steps, hook);
+                m_seen = fmaxf(m_seen, mx);
+                // also catches valid keys while the reference is unset (-inf)
+                my_vote |= __any(mx > m_run + kHeadroom);
 
-    // lane (head col, g) holds dims 32 nb + 8 i + 4 g .. +3 of its head in
-    // accumulator elements 4 i .. 4 i + 3 of tile nb
-    __bf16 *stage = (__bf16 *)smem + wv * 32 * O_LD;          // 32 heads x 256 bf16 per wave
-#pragma unroll
-    for (int nb = 0; nb < kOwn; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bf16x4 v;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[nb][4 * i + j] * inv);
-            *(bf16x4 *)(stage + col * O_LD + 32 * nb + 8 * i + 4 * g) = v;
+                // PV weights of the own block as E4M3 hi + lo under a per-head E8M0
+                // scale 2^pe (the block's largest weight lands in [128, 256)); the
+                // lane's 16 keys are LDS rows 16g .. 16g+15, piece g of the 32
+                float pmax = 0.f;
+    #pragma unroll
+                for (int k = 0; k < 16; ++k) pmax = fmaxf(pmax, pw[k]);
+                pmax = fmaxf(pmax, xor32(pmax));
+                const int pe = min(max(__builtin_amdgcn_frexp_expf(pmax) - 8, -127), 127);
+                u32x4 ph, pl;
+    #pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    float x[4];
+    #pragma unroll
+                    for (int q = 0; q < 4; ++q) x[q] = __builtin_ldexpf(pw[4 * d + q], -pe);
+                    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hi, true);
+                    const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+                    const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - b0[0], x[1] - b0[1], 0, false);
+                    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b1[0], x[3] - b1[1], lo, true);
+                    ph[d] = (uint32_t)hi;
+                    pl[d] = (uint32_t)lo;
+                }
+                s_ph[wv][g][col] = ph;
+                s_pl[wv][g][col] = pl;
+                if (g == 0) s_pe[wv][col] = 127 + pe;
+                i32x8 vn = v_ld(kstep, 0);
+                lds_barrier();           // weights of both blocks posted
+                // B: own weights in bytes 0..15, the partner's (same heads, same
+                // rows of its block) in bytes 16..31; lane half 0 carries the own
+                // block's scale, half 1 the partner's
+                const u32x4 hp = s_ph[wv ^ 2][g][col], lp = s_pl[wv ^ 2][g][col];
+                const i32x8 ah = {(int)ph[0], (int)ph[1], (int)ph[2], (int)ph[3],
+                                  (int)hp[0], (int)hp[1], (int)hp[2], (int)hp[3]};
+                const i32x8 al = {(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3],
+                                  (int)lp[0], (int)lp[1], (int)lp[2], (int)lp[3]};
+                const int sa = g == 0 ? 127 + pe : s_pe[wv ^ 2][col];
+                pv(kstep, ah, al, sa, vn);
+                s_cur = s_next;
+                sl = sl1;
+            };
+            int s = 0;
+            for (; s < n_steps - 2; ++s) step(s, IC<0>{});
+            for (; s < n_steps; ++s) step(s, IC<1>{});
+            // the tail DMA must land before the ring is reused
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            s_vote[wv] = my_vote ? 1 : 0;                // same value from every lane
+            lds_barrier();        // votes posted; every wave is done with the ring and the table
+            {
+                const int4 v = *(const int4 *)&s_vote[0];
+                redo = (v.x | v.y | v.z | v.w) != 0;
+            }
+            lds_barrier();        // votes read before the next chunk posts again
+            cb = (cb + n_steps - 1) % kRingSteps;                   // the next chunk's step 0: the last step's slot
         }
-    lds_barrier();
-    // 32 rows x 512 B per wave: two rows per pass, 16 B per lane
+        if (!redo) break;
+        // redo the query with a larger reference: the head group's largest block max
+        m_run = fmaxf(m_run, group_max(m_seen));
+        }
+
+        // ---- epilogue: l over both waves of the head group; LSE
+        {
+            const float lh = l_run + xor32(l_run);
+            if (g == 0) s_x[hg][half][col] = lh;
+        }
+        lds_barrier();
+        const float lt = s_x[hg][0][col] + s_x[hg][1][col];
+        if (half == 0 && g == 0 && hv)
+            a.lse[(int64_t)qi * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        // O staged through the last step's slot (the next query's step 0),
+        // 32 heads x 128 dims per wave and pass; each wave reads back only its
+        // own rows, so no barrier. Lane (head col, g) holds dims 32 nb + 8 i +
+        // 4 g .. +3 of its head in accumulator elements 4 i .. 4 i + 3 of tile nb.
+        __bf16 *stage = (__bf16 *)(ring + cb * kStepBytes) + wv * 32 * O_LD;
 #pragma unroll
-    for (int pr = 0; pr < 16; ++pr) {
-        const int hr = 2 * pr + g;
-        const int h = 32 * hg + hr;
-        if (h < H) {
-            const u32x4 v = *(const u32x4 *)(stage + hr * O_LD + 8 * col);
-            *(u32x4 *)(a.out + ((int64_t)qi * H + h) * kV + 32 * kOwn * half + 8 * col) = v;
+        for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+            for (int nb = 0; nb < kOwn / 2; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[kOwn / 2 * ps + nb][4 * i + j] * inv);
+                    *(bf16x4 *)(stage + col * O_LD + 32 * nb + 8 * i + 4 * g) = v;
+                }
+            // 32 rows x 256 B: four rows per pass, 16 B per lane
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int hr = 4 * it + (lane >> 4);
+                const int h = 32 * hg + hr;
+                const u32x4 v = *(const u32x4 *)(stage + hr * O_LD + 8 * (lane & 15));
+                if (h < H)
+                    *(u32x4 *)(a.out + ((int64_t)qi * H + h) * kV + 32 * kOwn * half + 16 * kOwn * ps +
+                               8 * (lane & 15)) = v;
+            }
         }
     }
 }
 
+// One persistent workgroup per compute unit (the LDS allows one), each
+// running its share of the queries.
 template <bool DENSE> hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute((const void *)attn_f8_kernel<DENSE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_f8_kernel<DENSE>), dim3(a.batch.total_q), dim3(kThreads), kLdsBytes, s, a);
+    int dev = 0, n_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int grid = std::min(a.batch.total_q, std::max(n_cu, 1));
+    hipLaunchKernelGGL((attn_f8_kernel<DENSE>), dim3(grid), dim3(kThreads), kLdsBytes, s, a);
     return hipGetLastError();
 }
 

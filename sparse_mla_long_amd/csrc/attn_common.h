@@ -64,6 +64,22 @@ __device__ __forceinline__ void dma4_opaque(const void *base, uint32_t off, void
                  ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
+// LDS address (the 32-bit offset M0 takes) of an LDS object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_void_ptr)p; }
+// The two transfers above with the destination as a wave-uniform LDS address,
+// for callers that compute it by integer arithmetic from lds_addr() of an
+// array (no generic pointers to convert and null-check at every call).
+__device__ __forceinline__ void dma16_lds(const void *base, uint32_t off, uint32_t lds) {
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_lds(const void *base, uint32_t off, uint32_t lds) {
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
+
 __device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x8 &d, int at) {
     const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
     const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
