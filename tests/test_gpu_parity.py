@@ -188,7 +188,7 @@ def test_indexer_small_integers_bit_exact(sm, H, D):
 
 # ----------------------------------------------------------------- top-k --
 @pytest.mark.parametrize("kind", ["all_equal", "relu_zeros", "small_int", "signed_zero", "normal",
-                                  "coarse"])
+                                  "coarse", "sample_low", "sample_high"])
 def test_topk_ties_bit_exact(sm, kind):
     g = torch.Generator().manual_seed(3)
     n, L, k = 24, 70000, 2048
@@ -205,6 +205,12 @@ def test_topk_ties_bit_exact(sm, kind):
         s[:, ::97] = 1.0
     elif kind == "coarse":                 # many exact ties inside the threshold bin
         s = torch.round(torch.randn(n, L, generator=g) * 4) * 2.5
+    elif kind in ("sample_low", "sample_high"):
+        # periodic structure: one 128-byte line in 16 holds the row's lowest
+        # (or highest) scores, far from the rest
+        lines = (torch.arange(L) % 512) < 32
+        s = torch.randn(n, L, generator=g) + (100.0 if kind == "sample_low" else 0.0)
+        s[:, lines] = torch.randn(n, int(lines.sum()), generator=g) + (0.0 if kind == "sample_low" else 1e4)
     else:
         s = torch.randn(n, L, generator=g) * 100
     batch = sm.Batch([0, n], [0, L], pos, "cuda")
