@@ -59,7 +59,6 @@ constexpr int kStepBytes = kStepBlocks * kBlockBytes;
 constexpr int kDmaStep = kStepBytes / 1024 / kWaves;       // 9 DMA instructions per wave and step
 constexpr int kRingSteps = 3;                              // steps resident in LDS
 constexpr int kIdx = 2048;                                 // index-list entries per chunk
-constexpr int kPad = 2 * 64;                               // row-table entries the pipeline tail reads
 constexpr int kEnt = kIdx / 256;                           // table entries per thread
 constexpr int kPairs = kQK / 32;                           // 16-byte K chunks per lane half
 constexpr int kKB = kQK / 64;                              // QK k-blocks of the FP8 MFMA
@@ -67,7 +66,7 @@ constexpr int kOwn = kV / 64;                              // output tiles (32 d
 constexpr int O_LD = 16 * kOwn + 8;                        // epilogue staging pitch (bf16): 128 dims a pass
 
 constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
-constexpr size_t kStaticBytes = (size_t)kIdx * 20 + kPad * 4 + kWaves * 2 * 2 * 32 * 16 + kWaves * 32 * 4 +
+constexpr size_t kStaticBytes = (size_t)kIdx * 20 + kWaves * 2 * 2 * 32 * 16 + kWaves * 32 * 4 +
                                  2 * 2 * 32 * 4 + kWaves * 4 + 2 * kKB * 32;
 static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
 static_assert(kDmaStep * kWaves * 1024 == kStepBytes, "DMA split");
@@ -106,7 +105,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     uint8_t *ring = smem;
     // entry table in its own LDS objects, so LDS reads of it are not ordered
     // behind the in-flight ring DMA
-    __shared__ __attribute__((aligned(16))) int32_t s_row[kIdx + kPad];   // row, or -1
+    __shared__ __attribute__((aligned(16))) int32_t s_row[kIdx];   // row, or -1
     __shared__ __attribute__((aligned(16))) float s_sig[kIdx];      // sigma_j (row scale)
     __shared__ __attribute__((aligned(16))) float s_mul[kIdx];      // sigma_j * scale * log2e, or 0
     __shared__ __attribute__((aligned(16))) float s_bias[kIdx];     // 0, or -inf if masked
@@ -351,8 +350,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     // otherwise nothing is gathered. DMA instructions of this wave in a key
     // step: u < 8 are main instructions ins = wv + 4u (block ins >> 4, main
     // instruction ins & 15 of it); u = 8 is tail instruction wv & 1 of block
-    // wv >> 1. Table entries past the chunk hold -1 (row 0, fetched and never
-    // used). (Lane terms pass through an empty asm at each use, so they are
+    // wv >> 1. Entries of the last step past the chunk hold -1 (row 0, fetched
+    // and never used). (Lane terms pass through an empty asm at each use, so they are
     // recomputed rather than hoisted into registers for every instruction.)
     auto dma_row = [&](int v, int u) -> int {
         int ln = lane;
@@ -464,7 +463,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 
     // every row-table entry the gather may read holds -1 or a row of the
     // current query's sequence
-    for (int e = tid; e < kIdx + kPad; e += kThreads) s_row[e] = -1;
+    for (int e = tid; e < kIdx; e += kThreads) s_row[e] = -1;
     // the first query's index list and Q, as a previous query would have left them
     if (query_of(0) >= 0) {                       // uniform
         const int q0 = query_of(0);
