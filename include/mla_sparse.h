@@ -2,7 +2,8 @@
  * mla_sparse.h -- C ABI of an MI355X (gfx950) library for GLM-style causal
  * prefill attention over a multi-head latent attention (MLA) KV cache.
  *
- * The path has three calls, run in this order for one attention layer:
+ * The path has three calls, run in this order for one attention layer, and a
+ * fourth that merges attention results computed over parts of the keys:
  *
  *   mla_indexer_score   the indexer scores every earlier token of each query
  *                       (spke.com GLM-5.3 PCP/DCP article, section "Warum nicht
@@ -16,6 +17,9 @@
  *                       the first 512 (same article, footnote 1), with the
  *                       log-sum-exp of every (query, head) as a second output
  *                       (the mergeable quantity of its section "DCP").
+ *   mla_merge_attention combines attention results over disjoint key sets
+ *                       (key shards, or splits of one query's keys) through
+ *                       their log-sum-exp.
  *
  * Batches are packed: sequence b owns query rows [cu_q[b], cu_q[b+1]) and
  * latent-KV rows [cu_kv[b], cu_kv[b+1]); every query carries its true
@@ -143,6 +147,29 @@ mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const v
                                 int64_t kv_row_stride, int64_t kv_scale_stride,
                                 const int32_t *indices, int32_t k, int32_t n_heads,
                                 float sm_scale, void *out, float *lse, void *stream);
+
+/* Merge of attention results over disjoint key sets by their log-sum-exp
+ * (spke.com article, section "DCP": every GPU attends over its share of the
+ * KV and the partial results combine through the LSE; the same merge makes
+ * split-KV attention on one GPU). For every query i and head h, with parts
+ * r = 0 .. n_parts-1 computed by mla_sparse_prefill over key sets that
+ * partition the wanted set:
+ *
+ *     lse[i,h]   = ln sum_r exp(lse_r[i,h])
+ *     out[i,h,c] = sum_r exp(lse_r[i,h] - lse[i,h]) * out_r[i,h,c],   c < 512
+ *
+ * which is attention over the union of the sets. A part with lse_r = -inf (an
+ * empty set) contributes nothing; if every part is empty, out = 0 and
+ * lse = -inf. The merge works in fp32 and rounds out to bf16 (nearest even).
+ *   o_parts   host array of n_parts device pointers, each [total_q, n_heads, 512] bf16, 16-byte aligned
+ *   lse_parts host array of n_parts device pointers, each [total_q, n_heads] fp32
+ *   out       device [total_q, n_heads, 512] bf16, 16-byte aligned
+ *   lse       device [total_q, n_heads] fp32
+ * out and lse must not overlap any part. Supported: 1 <= n_parts <= 16
+ * (MLA_ERR_UNSUPPORTED above). */
+mla_status_t mla_merge_attention(const void *const *o_parts, const float *const *lse_parts,
+                                 int32_t n_parts, int32_t total_q, int32_t n_heads, void *out,
+                                 float *lse, void *stream);
 
 /* Static description of a status code. */
 const char *mla_status_string(mla_status_t status);

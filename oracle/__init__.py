@@ -170,6 +170,25 @@ def attention_seq(q, kv, q_pos, sm_scale: float, kv_scale=None, indices=None,
     return out, lse
 
 
+def merge_lse(o_parts, lse_parts):
+    """Attention over the union of disjoint key sets, from the results of each
+    set (spke.com GLM-5.3 PCP/DCP article, section "DCP": partial attention
+    results combine through their log-sum-exp). o_parts [n_parts, ..., 512],
+    lse_parts [n_parts, ...] (natural log, -inf for an empty set). In float64:
+    lse = ln sum_r exp(lse_r), out = sum_r exp(lse_r - lse) o_r; every part
+    empty gives out = 0, lse = -inf. Returns (out, lse)."""
+    o = np.asarray(o_parts, dtype=np.float64)
+    l = np.asarray(lse_parts, dtype=np.float64)
+    m = l.max(axis=0)
+    any_set = np.isfinite(m)
+    ref = np.where(any_set, m, 0.0)
+    w = np.exp(l - ref)                                  # an empty part weighs 0
+    tot = np.where(any_set, w.sum(axis=0), 1.0)
+    lse = np.where(any_set, ref + np.log(tot), -np.inf)
+    out = np.where(any_set[..., None], (w[..., None] * o).sum(axis=0) / tot[..., None], 0.0)
+    return out, lse
+
+
 # ------------------------------------------------------------ ragged batch --
 def _seq_of_rows(cu_q: np.ndarray, rows: np.ndarray) -> np.ndarray:
     return np.searchsorted(cu_q, rows, side="right") - 1

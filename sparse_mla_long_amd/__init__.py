@@ -56,7 +56,9 @@ def load_library(path: str = LIB_PATH):
     L.mla_topk_select.argtypes = [BP, P, I64, I32, P, P]
     L.mla_sparse_prefill.argtypes = [BP, P, P, P, ctypes.c_int, I64, I64, P, I32, I32,
                                      ctypes.c_float, P, P, P]
-    for f in ("mla_indexer_score", "mla_topk_select", "mla_sparse_prefill"):
+    L.mla_merge_attention.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                      I32, I32, I32, P, P, P]
+    for f in ("mla_indexer_score", "mla_topk_select", "mla_sparse_prefill", "mla_merge_attention"):
         getattr(L, f).restype = ctypes.c_int
     L.mla_status_string.argtypes = [ctypes.c_int]
     L.mla_status_string.restype = ctypes.c_char_p
@@ -217,6 +219,37 @@ def sparse_prefill(batch: Batch, q: torch.Tensor, kv: torch.Tensor,
         batch.c, _ptr(q), _ptr(kv), _ptr(kv_scale) if dtype == MLA_KV_FP8_E4M3 else None, dtype,
         int(kv_row_stride), int(kv_scale_stride), _ptr(indices), int(k), H, float(sm_scale),
         _ptr(out), _ptr(lse), _stream(q)))
+    return out, lse
+
+
+def merge_attention(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor],
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """mla_merge_attention: attention over the union of disjoint key sets from
+    the parts' results. o_parts: tensors [total_q, H, 512] bf16; lse_parts:
+    [total_q, H] fp32 (all on one device). Returns (out, lse) like sparse_prefill."""
+    n = len(o_parts)
+    if n != len(lse_parts) or n < 1:
+        raise ValueError("need as many lse parts as o parts (at least one)")
+    o0 = o_parts[0]
+    if o0.dim() != 3 or o0.shape[2] != V_DIM:
+        raise ValueError("o parts must be [total_q, H, 512]")
+    total_q, H = o0.shape[0], o0.shape[1]
+    dev = o0.device
+    for o, l in zip(o_parts, lse_parts):
+        _need(o, "o part", torch.bfloat16, dev, (total_q, H, V_DIM))
+        _need(l, "lse part", torch.float32, dev, (total_q, H))
+    if out is None:
+        out = torch.empty((total_q, H, V_DIM), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, dev, (total_q, H, V_DIM))
+    if lse is None:
+        lse = torch.empty((total_q, H), dtype=torch.float32, device=dev)
+    else:
+        _need(lse, "lse", torch.float32, dev, (total_q, H))
+    optrs = (ctypes.c_void_p * n)(*[o.data_ptr() for o in o_parts])
+    lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_parts])
+    _check(load_library().mla_merge_attention(optrs, lptrs, n, int(total_q), int(H), _ptr(out),
+                                              _ptr(lse), _stream(o0)))
     return out, lse
 
 

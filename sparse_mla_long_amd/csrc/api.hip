@@ -191,6 +191,34 @@ mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const v
     return hip_status(mla::launch_attention(a, fp8, (hipStream_t)stream), "attention launch");
 }
 
+mla_status_t mla_merge_attention(const void *const *o_parts, const float *const *lse_parts,
+                                 int32_t n_parts, int32_t total_q, int32_t n_heads, void *out,
+                                 float *lse, void *stream) {
+    if (n_parts < 1) return fail(MLA_ERR_INVALID_ARG, "n_parts must be >= 1 (got %d)", n_parts);
+    if (n_parts > mla::kMergeMaxParts)
+        return fail(MLA_ERR_UNSUPPORTED, "n_parts %d > %d", n_parts, mla::kMergeMaxParts);
+    if (total_q < 0 || n_heads < 1)
+        return fail(MLA_ERR_INVALID_ARG, "total_q must be >= 0 and n_heads >= 1 (got %d, %d)", total_q, n_heads);
+    if (!o_parts || !lse_parts) return fail(MLA_ERR_INVALID_ARG, "o_parts / lse_parts is NULL");
+    if (total_q == 0) return ok();
+    if (!out || !lse) return fail(MLA_ERR_INVALID_ARG, "out / lse is NULL");
+    if (!aligned(out, 16) || !aligned(lse, 4)) return fail(MLA_ERR_INVALID_ARG, "out / lse misaligned");
+    mla::MergeArgs a{};
+    for (int32_t r = 0; r < n_parts; ++r) {
+        if (!o_parts[r] || !lse_parts[r])
+            return fail(MLA_ERR_INVALID_ARG, "part %d: o / lse pointer is NULL", r);
+        if (!aligned(o_parts[r], 16) || !aligned(lse_parts[r], 4))
+            return fail(MLA_ERR_INVALID_ARG, "part %d: o / lse pointer misaligned", r);
+        a.o[r] = (const __bf16 *)o_parts[r];
+        a.lse[r] = lse_parts[r];
+    }
+    a.n_parts = n_parts;
+    a.rows = (int64_t)total_q * n_heads;
+    a.out = (__bf16 *)out;
+    a.lse_out = lse;
+    return hip_status(mla::launch_merge(a, (hipStream_t)stream), "merge launch");
+}
+
 const char *mla_status_string(mla_status_t s) {
     switch (s) {
     case MLA_OK: return "MLA_OK";

@@ -51,11 +51,24 @@ struct AttnArgs {
     float *lse;                 // [total_q, n_heads]
 };
 
+// LSE merge of attention parts over disjoint key sets
+constexpr int kMergeMaxParts = 16;
+constexpr int kMergeDim = 512;              // output dims per (query, head) row
+struct MergeArgs {
+    const __bf16 *o[kMergeMaxParts];        // part r: [rows, 512]
+    const float *lse[kMergeMaxParts];       // part r: [rows]
+    int32_t n_parts;
+    int64_t rows;                           // total_q * n_heads
+    __bf16 *out;                            // [rows, 512]
+    float *lse_out;                         // [rows]
+};
+
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 constexpr int32_t kTopkMaxRow = 1 << 19;   // longest score row top-k takes (its bitmaps sit in LDS)
 hipError_t launch_attention(const AttnArgs &a, bool fp8, hipStream_t s);
 // FP8 (E4M3) latent rows (launch_attention dispatches to it)
 hipError_t launch_attention_fp8_f8(const AttnArgs &a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 
 }  // namespace mla

@@ -149,6 +149,26 @@ def test_attention_argument_checks(lib):
     assert attn_call(lib, mid, sstride=1024) == UNSUPPORTED       # scales: 5.1 GB >= 4 GiB
 
 
+def test_merge_argument_checks(lib):
+    """mla_merge_attention validates on the host before any HIP call."""
+    import ctypes
+    def call(n=2, total_q=4, H=8, o=(FAKE, FAKE), l=(FAKE, FAKE), out=FAKE, lse=FAKE):
+        optr = (ctypes.c_void_p * max(len(o), 1))(*o) if o is not None else None
+        lptr = (ctypes.c_void_p * max(len(l), 1))(*l) if l is not None else None
+        return lib.mla_merge_attention(optr, lptr, n, total_q, H, out, lse, None)
+    assert call(n=0) == INVALID
+    assert call(n=17, o=(FAKE,) * 17, l=(FAKE,) * 17) == UNSUPPORTED
+    assert call(total_q=-1) == INVALID
+    assert call(H=0) == INVALID
+    assert call(o=None) == INVALID
+    assert call(o=(FAKE, None)) == INVALID
+    assert call(l=(FAKE + 2, FAKE)) == INVALID              # misaligned LSE part
+    assert call(o=(FAKE + 8, FAKE)) == INVALID              # 16-byte part loads
+    assert call(out=None) == INVALID
+    assert call(out=FAKE + 4) == INVALID
+    assert call(total_q=0, out=None, lse=None) == sm.MLA_OK  # nothing to merge, nothing enqueued
+
+
 def test_empty_batch_enqueues_nothing(lib):
     """total_q == 0 returns OK without any HIP call (so it works with no GPU)."""
     b, keep = make_batch(cu_q=(0, 0), cu_kv=(0, 10))

@@ -45,7 +45,8 @@ def assert_close(name, got, ref, atol, rtol):
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
-    err = np.abs(got - ref)
+    with np.errstate(invalid="ignore"):          # inf - inf where both are the same infinity
+        err = np.abs(got - ref)
     bad = ~(both_inf | (err <= atol + rtol * np.abs(ref)))
     if bad.any():
         i = np.argwhere(bad)[0]
@@ -275,3 +276,69 @@ def test_full_size_sampled_rows(sm, name, kv_dtype):
         check_path(sm, inp, rows, "%s-%s" % (name, kv_dtype))
     del inp
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------- LSE merge and key shards --
+def test_merge_random_parts(sm):
+    """mla_merge_attention against oracle.merge_lse on the same bf16 parts:
+    random outputs and LSEs, some parts empty (-inf), some rows with every
+    part empty."""
+    g = torch.Generator().manual_seed(11)
+    n_parts, total_q, H = 5, 300, 16
+    o = [(torch.randn(total_q, H, 512, generator=g) * 3).to(torch.bfloat16) for _ in range(n_parts)]
+    l = [torch.randn(total_q, H, generator=g) * 20 for _ in range(n_parts)]
+    for r in range(n_parts):                     # empty parts here and there
+        l[r][torch.rand(total_q, H, generator=g) < 0.3] = -math.inf
+    for r in range(n_parts):                     # rows 0..9: every part empty
+        l[r][:10] = -math.inf
+        o[r][:10] = 0
+    out, lse = sm.merge_attention([t.cuda() for t in o], [t.cuda() for t in l])
+    torch.cuda.synchronize()
+    r_out, r_lse = oracle.merge_lse([t.float().numpy() for t in o], [t.numpy() for t in l])
+    # fp32 weights and sums, out rounded once to bf16
+    assert_close("merge out", out.float().cpu().numpy(), r_out, 2e-2, 1e-2)
+    assert_close("merge lse", lse.cpu().numpy(), r_lse, 1e-5, 1e-6)
+    assert (out[:10] == 0).all().item() and torch.isneginf(lse[:10]).all().item()
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_dcp_key_shards_merge_to_full(sm, kv_dtype):
+    """DCP-style attention on one GPU: the tiny batch's KV rows dealt round-
+    robin to 8 shards (row j on shard j mod 8), attention of every query over
+    each shard's part of its top-k list, then mla_merge_attention. The merge
+    must match the unsharded GPU result and the oracle."""
+    wl = mla_inputs.WORKLOADS["tiny"]
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu", kv_dtype=kv_dtype))
+    batch = sm.Batch.from_inputs(inp)
+    scores = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
+    idx = sm.topk_select(batch, scores, wl.topk)
+    full_o, full_l = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale)
+    n_shards, L, k = 8, wl.total_kv, wl.topk
+    idx_h = idx.cpu().numpy()
+    parts_o, parts_l = [], []
+    for r in range(n_shards):
+        rows = np.arange(r, L, n_shards)
+        sel = np.where((idx_h >= 0) & (idx_h % n_shards == r), idx_h // n_shards, -1)
+        loc = np.full_like(idx_h, -1)                    # shard-local lists, ascending, -1 padded
+        for i in range(idx_h.shape[0]):
+            v = np.sort(sel[i][sel[i] >= 0])
+            loc[i, : len(v)] = v
+        Lr = len(rows)
+        sb = sm.Batch([0, wl.total_q], [0, Lr], torch.full((wl.total_q,), Lr - 1, dtype=torch.int32), "cuda")
+        rt = torch.as_tensor(rows, device="cuda")
+        kv_r = inp["kv"][rt].contiguous()
+        sc_r = inp["kv_scale"][rt].contiguous() if inp["kv_scale"] is not None else None
+        o_r, l_r = sm.sparse_prefill(sb, inp["q"], kv_r, sc_r, torch.as_tensor(loc, device="cuda"),
+                                     wl.sm_scale)
+        parts_o.append(o_r)
+        parts_l.append(l_r)
+    m_o, m_l = sm.merge_attention(parts_o, parts_l)
+    torch.cuda.synchronize()
+    tol = TOL[kv_dtype]
+    assert_close("dcp out vs unsharded", m_o.float().cpu().numpy(), full_o.float().cpu().numpy(), 2e-2, 2e-2)
+    assert_close("dcp lse vs unsharded", m_l.cpu().numpy(), full_l.cpu().numpy(), 1e-3, 1e-3)
+    rows = np.arange(0, wl.total_q, 7)
+    r_out, r_lse = oracle.attention_rows(inp, rows, idx_h[rows])
+    rt = torch.as_tensor(rows, device="cuda")
+    assert_close("dcp out vs oracle", m_o[rt].float().cpu().numpy(), r_out, tol, tol)
+    assert_close("dcp lse vs oracle", m_l[rt].cpu().numpy(), r_lse, tol, tol)

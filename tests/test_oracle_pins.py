@@ -218,7 +218,8 @@ def test_keep_all_topk_makes_sparse_equal_dense_exactly():
 def test_weights_sum_to_one_and_lse_merge():
     """(a) rows with one shared latent part u and random rope parts give
     O = (sum_j p_j) u, so O / u == 1; (b) splitting the selected set into two
-    halves and merging by log-sum-exp reproduces the full result."""
+    halves, or into eight round-robin shards, and merging the parts with
+    oracle.merge_lse reproduces the full result."""
     rng = np.random.default_rng(4)
     L, H = 40, 2
     q, kv = _rand_seq(rng, H, L)
@@ -240,10 +241,24 @@ def test_weights_sum_to_one_and_lse_merge():
     oa, la = oracle.attention_seq(q, kv, p, SM, indices=even, q_fmt=FMT_F64, kv_fmt=FMT_F64)
     ob, lb = oracle.attention_seq(q, kv, p, SM, indices=odd, q_fmt=FMT_F64, kv_fmt=FMT_F64)
     assert np.isneginf(lb[0]).all() and (ob[0] == 0).all()     # empty half: O = 0, LSE = -inf
-    Lm = np.logaddexp(la, lb)
-    om = np.exp(la - Lm)[..., None] * oa + np.exp(lb - Lm)[..., None] * ob
+    om, Lm = oracle.merge_lse([oa, ob], [la, lb])
     np.testing.assert_allclose(Lm, full_l, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(om, full_o, rtol=1e-10, atol=1e-13)
+    # eight round-robin key shards (row j on shard j mod 8), most rows with
+    # some empty shards, merge back to the full result too
+    parts = []
+    for r in range(8):
+        ind = np.full((L, L), -1, np.int32)
+        for i in range(L):
+            sel = list(range(r, i + 1, 8))
+            ind[i, : len(sel)] = sel
+        parts.append(oracle.attention_seq(q, kv, p, SM, indices=ind, q_fmt=FMT_F64, kv_fmt=FMT_F64))
+    om8, Lm8 = oracle.merge_lse([o_ for o_, _ in parts], [l_ for _, l_ in parts])
+    np.testing.assert_allclose(Lm8, full_l, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(om8, full_o, rtol=1e-10, atol=1e-13)
+    # every part empty: O = 0, LSE = -inf
+    oz, lz = oracle.merge_lse([ob[:1], ob[:1]], [lb[:1], lb[:1]])
+    assert (oz == 0).all() and np.isneginf(lz).all()
 
 
 def test_closed_forms_first_row_and_identical_rows():
