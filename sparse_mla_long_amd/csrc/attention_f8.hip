@@ -1,5 +1,6 @@
 // Absorbed (MQA-form) MLA attention over FP8 (E4M3) latent rows: four waves
-// per query, each computing whole 576-dim logits for its own key blocks.
+// per query, each computing whole 576-dim logits for its own key blocks, in
+// persistent workgroups that prefetch the next query.
 //
 // Every token has one latent row of 576 values (512 latent + 64 rope) shared
 // by all heads; a query's heads attend with QK over all 576 dims and PV over
@@ -7,11 +8,17 @@
 // gathered row serves every head (section "PCP"). Blocks of 32 gathered rows
 // land in LDS once and feed QK and PV of all 64 heads.
 //
-// Work split: one query per 256-thread workgroup, one wave per SIMD. Wave w
-// owns head group hg = w & 1 (32 heads) and half = w >> 1. A step moves two
-// blocks (2s, 2s+1): the wave computes logits and softmax of block 2s + half,
-// and PV of both blocks over output dims 256 half .. +255, with the partner
-// wave's probabilities (wave w ^ 2, same heads) taken from LDS.
+// Work split: one persistent 256-thread workgroup per CU runs its share of the
+// queries, one wave per SIMD. Wave w owns head group hg = w & 1 (32 heads) and
+// half = w >> 1. A step moves two blocks (2s, 2s+1): the wave computes logits
+// and softmax of block 2s + half, and PV of both blocks over output dims
+// 256 half .. +255, with the partner wave's probabilities (wave w ^ 2, same
+// heads) taken from LDS.
+//  * Next query: a chunk's last two steps have no step s+2 to gather; their
+//    ring slots receive the next query's Q by DMA (one head group per slot)
+//    and its index list goes into its own LDS buffer, so a query starts
+//    without waiting on global memory. The two waves of a head group split
+//    half of Q's k-blocks each into E4M3 operands, in place, and read all back.
 //  * QK: S^T[key x head] = K Q^T over all 576 dims on 32x32x64 FP8 MFMA,
 //    K straight from LDS, Q^T as an exact hi + lo pair of E4M3 operands (two
 //    MFMAs per 64 dims); the wave's Q^T operands (144 VGPRs) stay in
@@ -34,9 +41,9 @@
 //    swizzles make the QK reads (16 rows, one chunk) and the transposed V
 //    reads (8 rows, two chunks) bank-conflict free, and keep the gather's
 //    per-lane offsets independent of the instruction but for a scalar term.
-//  * The barrier opening a step retires the step before (its ring slots take
-//    the gather of step s+2) and publishes step s, which every wave waited
-//    for on its own DMA counter.
+//  * The barrier opening step s retires step s-1 (its ring slot takes the
+//    gather of step s+2) and publishes step s+1, whose gather every wave
+//    waited for on its own DMA counter.
 // Entries of the index list outside 0..p_i are masked (probability 0).
 #include "attn_common.h"
 #include "common.h"
