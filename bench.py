@@ -68,16 +68,21 @@ def workload_flops(wl) -> dict:
     return {"indexer": f_idx, "attention": f_attn, **pc}
 
 
-def kernel_bytes(wl, kv_dtype: str) -> dict:
+def kernel_bytes(wl, kv_dtype: str, idx_dtype: str = "bf16") -> dict:
     """Algorithmic HBM bytes per launch of each kernel (inputs read once,
-    outputs written once; gathered rows counted per selected pair)."""
+    outputs written once; gathered rows counted per selected pair). FP8
+    indexer inputs are 1-byte codes plus an fp32 scale per row."""
     pc = pair_counts(wl)
     row = D_QK + 4 if kv_dtype == "fp8" else 2 * D_QK
     q_bytes = wl.total_q * wl.n_heads * (2 * D_QK + 2 * D_V + 4)
     out = {"attention": pc["selected"] * (row + (0 if wl.dense else 4)) + q_bytes}
     if not wl.dense:
-        out["indexer"] = pc["causal"] * 4 + wl.total_q * wl.idx_heads * (2 * wl.idx_dim + 4) \
-            + wl.total_kv * 2 * wl.idx_dim
+        if idx_dtype == "fp8":
+            out["indexer"] = pc["causal"] * 4 + wl.total_q * wl.idx_heads * (wl.idx_dim + 8) \
+                + wl.total_kv * (wl.idx_dim + 4)
+        else:
+            out["indexer"] = pc["causal"] * 4 + wl.total_q * wl.idx_heads * (2 * wl.idx_dim + 4) \
+                + wl.total_kv * 2 * wl.idx_dim
         out["topk"] = pc["causal"] * 4 + wl.total_q * wl.topk * 4
     return out
 
@@ -110,11 +115,17 @@ def _counter_rows(path: str, counter: str) -> list:
         return [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
 
 
+def traffic_key(workload: str, kv_dtype: str, idx_dtype: str = "bf16") -> str:
+    key = "%s/%s" % (workload, kv_dtype)
+    return key if idx_dtype == "bf16" else key + "/indexer-" + idx_dtype
+
+
 def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str,
-                    kv_dtype: str, command: str) -> dict:
+                    kv_dtype: str, command: str, idx_dtype: str = "bf16") -> dict:
     """Turn the two counter passes into bytes per launch and store them."""
     n = calib_mib << 20
-    rec = {"workload": workload, "kv_dtype": kv_dtype, "calibration_bytes": n,
+    rec = {"workload": workload, "kv_dtype": kv_dtype, "indexer_dtype": idx_dtype,
+           "calibration_bytes": n,
            "command": command, "kernels": {}}
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = _counter_rows(path, counter)
@@ -139,20 +150,20 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: st
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             table = json.load(fh)
-    table["%s/%s" % (workload, kv_dtype)] = rec
+    table[traffic_key(workload, kv_dtype, idx_dtype)] = rec
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(table, fh, indent=1, sort_keys=True)
         fh.write("\n")
     return rec
 
 
-def measured_traffic(workload: str, kv_dtype: str, name: str):
+def measured_traffic(workload: str, kv_dtype: str, name: str, idx_dtype: str = "bf16"):
     """HBM bytes per launch of kernel `name` from the stored counter passes,
     or None when there are none or the kernel's sources changed since."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as fh:
-        rec = json.load(fh).get("%s/%s" % (workload, kv_dtype))
+        rec = json.load(fh).get(traffic_key(workload, kv_dtype, idx_dtype))
     d = rec and rec["kernels"].get(name)
     if not d or d["source_hash"] != kernel_source_hash(name) or "fetch_bytes" not in d \
             or "write_bytes" not in d:
@@ -211,6 +222,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sparse32k")
     ap.add_argument("--kv-dtype", default=None, help="override the workload's KV dtype (bf16/fp8)")
+    ap.add_argument("--indexer-dtype", default="bf16", choices=("bf16", "fp8"),
+                    help="indexer queries and keys: bf16, or E4M3 codes with an fp32 scale per "
+                         "row (mla_indexer_score_fp8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -227,7 +241,7 @@ def main():
             raise SystemExit("--ingest-counters needs the --copy-calibration-mib of the runs")
         rec = ingest_counters(args.ingest_counters[0], args.ingest_counters[1],
                               args.copy_calibration_mib, wl.name, args.kv_dtype or wl.kv_dtype,
-                              args.command)
+                              args.command, args.indexer_dtype)
         print(json.dumps(rec, indent=1))
         return
 
@@ -246,7 +260,8 @@ def main():
     torch.cuda.set_device(dev)
     wl = mla_inputs.WORKLOADS[args.workload]
     kv_dtype = args.kv_dtype or wl.kv_dtype
-    inp = mla_inputs.make_inputs(wl, dev, kv_dtype=kv_dtype)
+    idx_dtype = args.indexer_dtype
+    inp = mla_inputs.make_inputs(wl, dev, kv_dtype=kv_dtype, idx_dtype=idx_dtype)
     batch = sm.Batch.from_inputs(inp, dev)
     scores = None if wl.dense else torch.empty((wl.total_q, wl.max_kv_len), dtype=torch.float32,
                                                device=dev)
@@ -267,7 +282,11 @@ def main():
             mark(1)
             return
         mark(0)
-        sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"], scores=scores)
+        if idx_dtype == "fp8":
+            sm.indexer_score_fp8(batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"],
+                                 inp["k_idx_scale"], inp["w"], scores=scores)
+        else:
+            sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"], scores=scores)
         mark(1)
         sm.topk_select(batch, scores, wl.topk, indices=indices)
         mark(2)
@@ -297,19 +316,22 @@ def main():
                                        for s in range(args.steps)]))
                      for i, n in enumerate(names)}
     fl = workload_flops(wl)
-    byts = kernel_bytes(wl, kv_dtype)
+    byts = kernel_bytes(wl, kv_dtype, idx_dtype)
+    # peak of the MFMA type each contraction's operands call for: the indexer's
+    # input dtype; attention bf16 (FP8 KV: its peak enters mfma_peak_frac below)
+    peak_of = {"indexer": PEAK_TFLOPS[idx_dtype], "attention": PEAK_TFLOPS["bf16"]}
     kern = {}
     for n in names:
         t = per_kernel_ms[n] * 1e-3
         d = {"ms": per_kernel_ms[n]}
         if n in ("indexer", "attention"):
             tf = fl[n] / t / 1e12
-            d.update({"tflops": tf, "bound": "mfma", "peak_tflops": PEAK_TFLOPS["bf16"],
-                      "frac": tf / PEAK_TFLOPS["bf16"]})
+            d.update({"tflops": tf, "bound": "mfma", "peak_tflops": peak_of[n],
+                      "frac": tf / peak_of[n]})
         if n in byts:
             d["algo_bytes"] = byts[n]
             d["gbs"] = byts[n] / t / 1e9
-        d["traffic"] = measured_traffic(wl.name, kv_dtype, n)
+        d["traffic"] = measured_traffic(wl.name, kv_dtype, n, idx_dtype)
         kern[n] = d
     kern["topk"] = kern.get("topk", {})
     if "topk" in per_kernel_ms:
@@ -330,7 +352,7 @@ def main():
     ms_step = elapsed / args.steps * 1e3
     t_kernels = sum(per_kernel_ms.values()) * 1e-3
     p_attn = PEAK_TFLOPS["fp8" if kv_dtype == "fp8" else "bf16"]
-    mfma_frac = (fl["indexer"] / (PEAK_TFLOPS["bf16"] * 1e12) +
+    mfma_frac = (fl["indexer"] / (PEAK_TFLOPS[idx_dtype] * 1e12) +
                  fl["attention"] / (p_attn * 1e12)) / (ms_step * 1e-3)
     res = {
         "metric": "prefill query-tokens/s on 1 MI355X + % MFMA peak (64 heads, top-k 2048)",
@@ -345,11 +367,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "seq_lens": list(wl.kv_lens), "total_q": wl.total_q,
                    "n_heads": wl.n_heads, "indexer": "%dx%d" % (wl.idx_heads, wl.idx_dim),
+                   "indexer_dtype": None if wl.dense else idx_dtype,
                    "topk": None if wl.dense else wl.topk, "kv_dtype": kv_dtype,
                    "dense": wl.dense, "parallelism": "single GPU"},
         "mfma_peak_frac": mfma_frac,
-        "mfma_peak_frac_note": "(F_indexer/P_bf16 + F_attention/P_attn)/t_step, P_attn = fp8 peak "
-                               "for FP8 KV whatever MFMA type the kernel uses",
+        "mfma_peak_frac_note": "(F_indexer/P_idx + F_attention/P_attn)/t_step, P_attn = fp8 peak "
+                               "for FP8 KV whatever MFMA type the kernel uses, P_idx = the peak "
+                               "of the indexer's input dtype",
         "flops": {"indexer": fl["indexer"], "attention": fl["attention"]},
         "kernels": kern,
         "kernel_sum_ms": t_kernels * 1e3,

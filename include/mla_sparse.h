@@ -10,6 +10,9 @@
  *                       TP oder DP?": it scores every earlier token to pick the
  *                       2,048 that sparse MLA attends to; its cost grows with
  *                       the square of the prompt length, section "PCP").
+ *                       mla_indexer_score_fp8 is the same score from FP8
+ *                       queries and keys with a scale each (footnote 3 stores
+ *                       an indexer key as 128 FP8 values plus a 4-byte scale).
  *   mla_topk_select     keeps the k best-scoring earlier tokens per query.
  *   mla_sparse_prefill  absorbed (MQA-form) MLA attention over the kept tokens:
  *                       one 576-value latent row per token (512 latent + 64
@@ -103,6 +106,28 @@ typedef struct {
 mla_status_t mla_indexer_score(const mla_batch_t *batch, const void *q_idx, const void *k_idx,
                                const float *w, int32_t n_heads, int32_t head_dim, float *scores,
                                int64_t ld_scores, void *stream);
+
+/* Indexer scores from FP8 queries and keys (spke.com article, footnote 3: an
+ * indexer key is kept as 128 FP8 values plus a 4-byte scale per token). With
+ * decoded E4M3 codes qc, kc and the scales sq, sk:
+ *
+ *     scores[i * ld_scores + j] =
+ *         sum_h w[i, h] * max(0, sum_d (sq[i, h] * qc[i, h, d]) * (sk[j] * kc[j, d]))
+ *
+ * for every key j <= q_pos[i]; entries j > q_pos[i] are not written. The
+ * code products are exact and accumulate in fp32; the scales are applied to
+ * the finished dot products (ReLU commutes with a non-negative factor).
+ *   q_idx    device [total_q, n_heads, head_dim] E4M3 codes (1 byte each), 16-byte aligned
+ *   q_scale  device [total_q, n_heads] fp32, finite and >= 0, 4-byte aligned
+ *   k_idx    device [total_kv, head_dim] E4M3 codes (row = cu_seqlens_kv[b] + j), 16-byte aligned
+ *   k_scale  device [total_kv] fp32, finite and >= 0, 4-byte aligned
+ *   w, scores, ld_scores, n_heads, head_dim: as mla_indexer_score.
+ * A negative or non-finite scale gives undefined scores (not checked: device
+ * data), and so are scores from NaN codes (0x7f, 0xff). */
+mla_status_t mla_indexer_score_fp8(const mla_batch_t *batch, const void *q_idx, const float *q_scale,
+                                   const void *k_idx, const float *k_scale, const float *w,
+                                   int32_t n_heads, int32_t head_dim, float *scores,
+                                   int64_t ld_scores, void *stream);
 
 /* Top-k selection over the indexer scores of each query (same section: keep
  * the 2,048 best earlier tokens). For query i with n_i = q_pos[i] + 1 scored

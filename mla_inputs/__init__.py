@@ -182,13 +182,28 @@ def fp8_kv(n_rows: int, seed: int, device="cpu", chunk_rows: int = 8192):
     return codes, sigma
 
 
+def quantize_e4m3_chunked(x: torch.Tensor, chunk_rows: int = 1 << 16):
+    """quantize_e4m3_rows over the rows of x viewed as [-1, x.shape[-1]], in
+    chunks (bounds the fp32 temporary). Returns (codes like x as uint8,
+    scales of shape x.shape[:-1])."""
+    flat = x.reshape(-1, x.shape[-1])
+    codes = torch.empty(flat.shape, dtype=torch.uint8, device=x.device)
+    sigma = torch.empty((flat.shape[0],), dtype=torch.float32, device=x.device)
+    for r in range(0, flat.shape[0], chunk_rows):
+        codes[r:r + chunk_rows], sigma[r:r + chunk_rows] = quantize_e4m3_rows(flat[r:r + chunk_rows])
+    return codes.view(x.shape), sigma.view(x.shape[:-1])
+
+
 def make_inputs(wl: Workload, device="cpu", kv_dtype: Optional[str] = None,
-                with_indexer: Optional[bool] = None) -> dict:
+                with_indexer: Optional[bool] = None, idx_dtype: str = "bf16") -> dict:
     """All tensors of one workload on ``device``.
 
     q   [total_q, H, 576] bf16    absorbed query (512 latent + 64 rope)
     kv  [total_kv, 576]   bf16, or uint8 E4M3 codes with kv_scale [total_kv] fp32
     q_idx [total_q, H_I, D_I] bf16, k_idx [total_kv, D_I] bf16, w [total_q, H_I] fp32
+    (idx_dtype "fp8": q_idx and k_idx are the E4M3 codes of those same draws,
+    one scale per (query, head) row in q_idx_scale [total_q, H_I] and per key
+    in k_idx_scale [total_kv])
     plus the batch description (int32 cu_seqlens_q/kv, q_pos) on ``device``
     and on the host (numpy).
     """
@@ -218,6 +233,12 @@ def make_inputs(wl: Workload, device="cpu", kv_dtype: Optional[str] = None,
         out["q_idx"] = normal_bf16((wl.total_q, wl.idx_heads, wl.idx_dim), s, T_QI, device)
         out["k_idx"] = normal_bf16((wl.total_kv, wl.idx_dim), s, T_KI, device)
         out["w"] = uniform_f32((wl.total_q, wl.idx_heads), s, T_W, device)
+        if idx_dtype == "fp8":
+            out["q_idx"], out["q_idx_scale"] = quantize_e4m3_chunked(out["q_idx"])
+            out["k_idx"], out["k_idx_scale"] = quantize_e4m3_chunked(out["k_idx"])
+        elif idx_dtype != "bf16":
+            raise ValueError(idx_dtype)
+    out["idx_dtype"] = idx_dtype
     return out
 
 

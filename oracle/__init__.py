@@ -57,6 +57,8 @@ def lib():
             L.oracle_e4m3_decode.restype = D
             L.oracle_indexer.argtypes = [I64, I64, I64, I64, P, P, P, P, P, I64]
             L.oracle_indexer.restype = None
+            L.oracle_indexer_e4m3.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, I64]
+            L.oracle_indexer_e4m3.restype = None
             L.oracle_topk.argtypes = [I64, P, I64, P, I32, P]
             L.oracle_topk.restype = None
             L.oracle_attention.argtypes = [I64, I64, I64, ctypes.c_int, P, ctypes.c_int, P, P,
@@ -121,6 +123,29 @@ def indexer_seq(q_idx_bits: np.ndarray, k_idx_bits: np.ndarray, w: np.ndarray,
     if n:
         lib().oracle_indexer(n, h, d, L, _ptr(q_idx_bits), _ptr(k_idx_bits), _ptr(w),
                              _ptr(q_pos), _ptr(scores), L)
+    return scores
+
+
+def indexer_seq_fp8(q_codes: np.ndarray, q_scale: np.ndarray, k_codes: np.ndarray,
+                    k_scale: np.ndarray, w: np.ndarray, q_pos: np.ndarray) -> np.ndarray:
+    """Scores from FP8 indexer inputs: q_codes [n, H_I, D_I] and k_codes [L, D_I]
+    uint8 E4M3, q_scale [n, H_I] and k_scale [L] fp32, w [n, H_I] fp32.
+    [n, L] fp32, NaN where j > q_pos[i]."""
+    q_codes = np.ascontiguousarray(q_codes, dtype=np.uint8)
+    k_codes = np.ascontiguousarray(k_codes, dtype=np.uint8)
+    q_scale = np.ascontiguousarray(q_scale, dtype=np.float32)
+    k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    q_pos = np.ascontiguousarray(q_pos, dtype=np.int32)
+    n, h, d = q_codes.shape
+    L = k_codes.shape[0]
+    assert k_codes.shape[1] == d and w.shape == (n, h) and q_scale.shape == (n, h)
+    assert k_scale.shape == (L,)
+    assert n == 0 or int(q_pos.max()) < L
+    scores = np.full((n, L), np.nan, dtype=np.float32)
+    if n:
+        lib().oracle_indexer_e4m3(n, h, d, L, _ptr(q_codes), _ptr(q_scale), _ptr(k_codes),
+                                  _ptr(k_scale), _ptr(w), _ptr(q_pos), _ptr(scores), L)
     return scores
 
 
@@ -206,19 +231,27 @@ def _take_rows(x, rows: np.ndarray) -> np.ndarray:
 
 
 def indexer_rows(batch: dict, rows: Sequence[int]):
-    """Oracle scores for selected global query rows of a packed batch.
+    """Oracle scores for selected global query rows of a packed batch (FP8
+    indexer inputs when the batch holds "k_idx_scale" and "q_idx_scale").
     Returns a list of fp32 arrays, row r of length q_pos[r] + 1."""
     rows = np.asarray(rows, dtype=np.int64)
     cu_q, cu_kv = batch["cu_seqlens_q_host"], batch["cu_seqlens_kv_host"]
     q_pos = np.asarray(batch["q_pos_host"])
+    fp8 = batch.get("k_idx_scale") is not None
     kI = as_numpy(batch["k_idx"])
     qI, w = _take_rows(batch["q_idx"], rows), _take_rows(batch["w"], rows)
+    if fp8:
+        qs, ks = _take_rows(batch["q_idx_scale"], rows), as_numpy(batch["k_idx_scale"])
     seq = _seq_of_rows(cu_q, rows)
     result = [None] * len(rows)
     for b in np.unique(seq):
         sel = np.nonzero(seq == b)[0]
         r = rows[sel]
-        sc = indexer_seq(qI[sel], kI[cu_kv[b]:cu_kv[b + 1]], w[sel], q_pos[r])
+        ka, kb = cu_kv[b], cu_kv[b + 1]
+        if fp8:
+            sc = indexer_seq_fp8(qI[sel], qs[sel], kI[ka:kb], ks[ka:kb], w[sel], q_pos[r])
+        else:
+            sc = indexer_seq(qI[sel], kI[ka:kb], w[sel], q_pos[r])
         for t, s in zip(sel, sc):
             result[t] = s[: q_pos[rows[t]] + 1].copy()
     return result

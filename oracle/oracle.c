@@ -13,7 +13,9 @@
  *     absolute position p_i and every key j <= p_i:
  *         I_ij = sum_h w_ih * max(0, sum_d qI_ihd * kI_jd)
  *     accumulated in fp64 and rounded once to fp32.  No extra scale: a scale
- *     is the caller's to fold into w.
+ *     is the caller's to fold into w.  With FP8 inputs (footnote 3: an
+ *     indexer key is 128 FP8 values plus a 4-byte scale) qI and kI are the
+ *     decoded E4M3 codes times their row's scale.
  *
  *  2. Top-k (same section): the k largest I_ij over j <= p_i, ties to the
  *     smaller j; all of 0..p_i when p_i + 1 <= k.  Emitted in ascending j,
@@ -73,18 +75,24 @@ static double load_elem(int fmt, const void *base, int64_t row_elems, int64_t r,
 }
 
 /* ---- 1. indexer ------------------------------------------------------- */
-/* q_idx [n, n_heads, head_dim] bf16; k_idx [L, head_dim] bf16 (one sequence);
- * w [n, n_heads] fp32; q_pos [n]; scores [n, ld], written for j <= q_pos[i]. */
-void oracle_indexer(int64_t n, int64_t n_heads, int64_t head_dim, int64_t L,
-                    const uint16_t *q_idx, const uint16_t *k_idx, const float *w,
-                    const int32_t *q_pos, float *scores, int64_t ld) {
+/* One sequence, any element format. q [n * n_heads rows of head_dim];
+ * k [L rows of head_dim]; q_scale [n * n_heads] and k_scale [L] are read for
+ * E4M3 only (each decoded element times its row's scale); w [n, n_heads];
+ * q_pos [n]; scores [n, ld], written for j <= q_pos[i]. */
+static void indexer_any(int64_t n, int64_t n_heads, int64_t head_dim, int64_t L, int fmt,
+                        const void *q_idx, const float *q_scale, const void *k_idx,
+                        const float *k_scale, const float *w, const int32_t *q_pos, float *scores,
+                        int64_t ld) {
     double *kd = (double *)malloc(sizeof(double) * (size_t)(L * head_dim));
-    for (int64_t t = 0; t < L * head_dim; ++t) kd[t] = oracle_bf16_decode(k_idx[t]);
+    for (int64_t j = 0; j < L; ++j)
+        for (int64_t d = 0; d < head_dim; ++d)
+            kd[j * head_dim + d] = load_elem(fmt, k_idx, head_dim, j, d, k_scale);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < n; ++i) {
         double *qd = (double *)malloc(sizeof(double) * (size_t)(n_heads * head_dim));
-        for (int64_t t = 0; t < n_heads * head_dim; ++t)
-            qd[t] = oracle_bf16_decode(q_idx[i * n_heads * head_dim + t]);
+        for (int64_t h = 0; h < n_heads; ++h)
+            for (int64_t d = 0; d < head_dim; ++d)
+                qd[h * head_dim + d] = load_elem(fmt, q_idx, head_dim, i * n_heads + h, d, q_scale);
         int64_t p = q_pos[i];
         for (int64_t j = 0; j <= p && j < L; ++j) {
             double acc = 0.0;
@@ -98,6 +106,26 @@ void oracle_indexer(int64_t n, int64_t n_heads, int64_t head_dim, int64_t L,
         free(qd);
     }
     free(kd);
+}
+
+/* q_idx [n, n_heads, head_dim] bf16; k_idx [L, head_dim] bf16 (one sequence);
+ * w [n, n_heads] fp32; q_pos [n]; scores [n, ld], written for j <= q_pos[i]. */
+void oracle_indexer(int64_t n, int64_t n_heads, int64_t head_dim, int64_t L,
+                    const uint16_t *q_idx, const uint16_t *k_idx, const float *w,
+                    const int32_t *q_pos, float *scores, int64_t ld) {
+    indexer_any(n, n_heads, head_dim, L, FMT_BF16, q_idx, NULL, k_idx, NULL, w, q_pos, scores, ld);
+}
+
+/* FP8 indexer inputs (article, footnote 3: an indexer key is 128 FP8 values
+ * and a 4-byte scale): q_idx [n, n_heads, head_dim] and k_idx [L, head_dim]
+ * E4M3 codes, q_scale [n, n_heads], k_scale [L] fp32. An element is
+ * decode(code) * scale of its row; the score is then the formula above. */
+void oracle_indexer_e4m3(int64_t n, int64_t n_heads, int64_t head_dim, int64_t L,
+                         const uint8_t *q_idx, const float *q_scale, const uint8_t *k_idx,
+                         const float *k_scale, const float *w, const int32_t *q_pos,
+                         float *scores, int64_t ld) {
+    indexer_any(n, n_heads, head_dim, L, FMT_E4M3, q_idx, q_scale, k_idx, k_scale, w, q_pos,
+                scores, ld);
 }
 
 /* ---- 2. top-k --------------------------------------------------------- */

@@ -8,6 +8,8 @@ import of its symbols fails loudly.
 
 Calls (same names as the C ABI, without the ``mla_`` prefix):
   indexer_score(batch, q_idx, k_idx, w, ...)   -> scores [total_q, ld] fp32
+  indexer_score_fp8(batch, q_idx, q_scale, k_idx, k_scale, w, ...)
+                                               -> scores from E4M3 codes with scales
   topk_select(batch, scores, k, ...)           -> indices [total_q, k] int32
   sparse_prefill(batch, q, kv, ...)            -> (out [total_q, H, 512] bf16, lse [total_q, H] fp32)
 """
@@ -36,8 +38,8 @@ class MlaBatch(ctypes.Structure):
                 ("q_pos", ctypes.c_void_p)]
 
 
-EXPORTS = ("mla_indexer_score", "mla_topk_select", "mla_sparse_prefill", "mla_status_string",
-           "mla_last_error", "mla_abi_version")
+EXPORTS = ("mla_indexer_score", "mla_indexer_score_fp8", "mla_topk_select", "mla_sparse_prefill",
+           "mla_merge_attention", "mla_status_string", "mla_last_error", "mla_abi_version")
 
 _lib = None
 
@@ -53,12 +55,14 @@ def load_library(path: str = LIB_PATH):
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     BP = ctypes.POINTER(MlaBatch)
     L.mla_indexer_score.argtypes = [BP, P, P, P, I32, I32, P, I64, P]
+    L.mla_indexer_score_fp8.argtypes = [BP, P, P, P, P, P, I32, I32, P, I64, P]
     L.mla_topk_select.argtypes = [BP, P, I64, I32, P, P]
     L.mla_sparse_prefill.argtypes = [BP, P, P, P, ctypes.c_int, I64, I64, P, I32, I32,
                                      ctypes.c_float, P, P, P]
     L.mla_merge_attention.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                       I32, I32, I32, P, P, P]
-    for f in ("mla_indexer_score", "mla_topk_select", "mla_sparse_prefill", "mla_merge_attention"):
+    for f in ("mla_indexer_score", "mla_indexer_score_fp8", "mla_topk_select", "mla_sparse_prefill",
+              "mla_merge_attention"):
         getattr(L, f).restype = ctypes.c_int
     L.mla_status_string.argtypes = [ctypes.c_int]
     L.mla_status_string.restype = ctypes.c_char_p
@@ -156,6 +160,31 @@ def indexer_score(batch: Batch, q_idx: torch.Tensor, k_idx: torch.Tensor, w: tor
         ld = scores.shape[1]
     _check(load_library().mla_indexer_score(batch.c, _ptr(q_idx), _ptr(k_idx), _ptr(w), n_heads,
                                             head_dim, _ptr(scores), ld, _stream(q_idx)))
+    return scores
+
+
+def indexer_score_fp8(batch: Batch, q_idx: torch.Tensor, q_scale: torch.Tensor,
+                      k_idx: torch.Tensor, k_scale: torch.Tensor, w: torch.Tensor,
+                      scores: Optional[torch.Tensor] = None, ld: Optional[int] = None) -> torch.Tensor:
+    """mla_indexer_score_fp8: q_idx [total_q, H, D] and k_idx [total_kv, D] are
+    uint8 E4M3 codes, q_scale [total_q, H] and k_scale [total_kv] fp32 (>= 0).
+    Returns scores [total_q, ld] fp32 (entries j > q_pos[i] are left as they were)."""
+    dev = batch.device
+    n_heads, head_dim = q_idx.shape[1], q_idx.shape[2]
+    _need(q_idx, "q_idx", torch.uint8, dev, (batch.total_q, n_heads, head_dim))
+    _need(q_scale, "q_scale", torch.float32, dev, (batch.total_q, n_heads))
+    _need(k_idx, "k_idx", torch.uint8, dev, (batch.total_kv, head_dim))
+    _need(k_scale, "k_scale", torch.float32, dev, (batch.total_kv,))
+    _need(w, "w", torch.float32, dev, (batch.total_q, n_heads))
+    if scores is None:
+        ld = ld or max(batch.max_kv_len, 1)
+        scores = torch.empty((batch.total_q, ld), dtype=torch.float32, device=dev)
+    else:
+        _need(scores, "scores", torch.float32, dev)
+        ld = scores.shape[1]
+    _check(load_library().mla_indexer_score_fp8(batch.c, _ptr(q_idx), _ptr(q_scale), _ptr(k_idx),
+                                                _ptr(k_scale), _ptr(w), n_heads, head_dim,
+                                                _ptr(scores), ld, _stream(q_idx)))
     return scores
 
 
@@ -261,7 +290,11 @@ def prefill(batch: Batch, inp: dict, topk: int, sm_scale: float, dense: bool = F
         out, lse = sparse_prefill(batch, inp["q"], inp["kv"], inp.get("kv_scale"), None,
                                   sm_scale)
         return out, lse, None
-    sc = indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"], scores=scores)
+    if inp.get("k_idx_scale") is not None:
+        sc = indexer_score_fp8(batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"],
+                               inp["k_idx_scale"], inp["w"], scores=scores)
+    else:
+        sc = indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"], scores=scores)
     idx = topk_select(batch, sc, topk)
     out, lse = sparse_prefill(batch, inp["q"], inp["kv"], inp.get("kv_scale"), idx, sm_scale)
     return out, lse, idx

@@ -77,9 +77,11 @@ mla_status_t hip_status(hipError_t e, const char *what) {
 
 extern "C" {
 
-mla_status_t mla_indexer_score(const mla_batch_t *batch, const void *q_idx, const void *k_idx,
-                               const float *w, int32_t n_heads, int32_t head_dim, float *scores,
-                               int64_t ld_scores, void *stream) {
+namespace {
+// Shared checks and launch of the two indexer entry points (scales are NULL for bf16).
+mla_status_t indexer(const mla_batch_t *batch, const void *q_idx, const float *q_scale,
+                     const void *k_idx, const float *k_scale, const float *w, int32_t n_heads,
+                     int32_t head_dim, float *scores, int64_t ld_scores, bool fp8, void *stream) {
     mla::IndexerArgs a{};
     mla_status_t st = check_batch(batch, &a.batch);
     if (st != MLA_OK) return st;
@@ -94,24 +96,47 @@ mla_status_t mla_indexer_score(const mla_batch_t *batch, const void *q_idx, cons
     if (batch->total_q == 0) return ok();
     if (!q_idx || !k_idx || !w || !scores)
         return fail(MLA_ERR_INVALID_ARG, "q_idx / k_idx / w / scores is NULL");
+    if (fp8 && (!q_scale || !k_scale))
+        return fail(MLA_ERR_INVALID_ARG, "q_scale / k_scale is NULL");
     if (!aligned(q_idx, 16) || !aligned(k_idx, 16))
         return fail(MLA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
     if (!aligned(w, 4) || !aligned(scores, 4))
         return fail(MLA_ERR_INVALID_ARG, "w and scores must be 4-byte aligned");
+    if (fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4)))
+        return fail(MLA_ERR_INVALID_ARG, "q_scale and k_scale must be 4-byte aligned");
     int64_t blocks = 0;
     for (int32_t s = 0; s < batch->num_seqs; ++s) {
         const int32_t nq = batch->cu_seqlens_q_host[s + 1] - batch->cu_seqlens_q_host[s];
         blocks += (nq + mla::kIdxQueriesPerBlock - 1) / mla::kIdxQueriesPerBlock;
     }
-    a.q_idx = (const __bf16 *)q_idx;
-    a.k_idx = (const __bf16 *)k_idx;
+    a.q_idx = q_idx;
+    a.k_idx = k_idx;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
     a.w = w;
     a.scores = scores;
     a.ld = ld_scores;
     a.n_heads = n_heads;
     a.head_dim = head_dim;
     a.n_blocks = (int32_t)blocks;
+    a.fp8 = fp8;
     return hip_status(mla::launch_indexer(a, (hipStream_t)stream), "indexer launch");
+}
+}  // namespace
+
+mla_status_t mla_indexer_score(const mla_batch_t *batch, const void *q_idx, const void *k_idx,
+                               const float *w, int32_t n_heads, int32_t head_dim, float *scores,
+                               int64_t ld_scores, void *stream) {
+    return indexer(batch, q_idx, nullptr, k_idx, nullptr, w, n_heads, head_dim, scores, ld_scores,
+                   false, stream);
+}
+
+mla_status_t mla_indexer_score_fp8(const mla_batch_t *batch, const void *q_idx, const float *q_scale,
+                                   const void *k_idx, const float *k_scale, const float *w,
+                                   int32_t n_heads, int32_t head_dim, float *scores,
+                                   int64_t ld_scores, void *stream) {
+    return indexer(batch, q_idx, q_scale, k_idx, k_scale, w, n_heads, head_dim, scores, ld_scores,
+                   true, stream);
 }
 
 mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int64_t ld_scores,

@@ -10,9 +10,17 @@
 // the whole sweep. In the 32x32 accumulator layout a lane owns one key column
 // and 16 head rows, so ReLU, the w-weighting and most of the head reduction
 // stay in the lane; one cross-lane add finishes it. Keys stream HBM -> LDS by
-// direct DMA through a ring of 64-key tiles shared by the eight waves, three
+// direct DMA through a ring of 128-key tiles shared by the eight waves, three
 // tiles ahead, 16-byte chunks XOR-swizzled by key row so the B-operand reads
 // are bank-conflict-free; one barrier per tile.
+//
+// FP8 variant (the same article, footnote 3: an indexer key is stored as 128
+// FP8 values plus a 4-byte scale). Queries and keys are E4M3 codes with an
+// fp32 scale per (query, head) and per key; the contraction runs on the E4M3
+// MFMA (32x32x64) on the raw codes. Because ReLU(c x) = c ReLU(x) for c >= 0,
+// the query scale folds into w and the key scale multiplies the finished
+// score, so the scales cost no work per head. The key scales travel with the
+// key tile (one 4-byte-per-lane DMA per wave and tile).
 #include "attn_common.h"
 #include "common.h"
 #include "kernels.h"
@@ -30,15 +38,42 @@ constexpr int kTileRing = 4;
 // also canonicalises its operand first.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-template <int KS, int MB>
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// E4M3 x E4M3 32x32x64 MFMA with unit block scales (E8M0 code 127 = 2^0).
+// Operand layout (lane l, g = l / 32): A row (l % 32), B column (l % 32);
+// operand bytes 0..15 and 16..31 hold two 16-value k-groups of lane half g.
+// The kernel gives A and B the same mapping from memory dims to operand bytes,
+// so which k a byte stands for does not matter to the dot product.
+__device__ __forceinline__ f32x16 mfma_e4m3(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <bool F8> struct QOperand { typedef bf16x8 type; };
+template <> struct QOperand<true> { typedef i32x8 type; };
+
+// DI: indexer head dim; MB: 32-head blocks; F8: E4M3 codes with scales
+// (else bf16).
+template <int DI, int MB, bool F8>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
-    constexpr int DI = KS * 16;          // indexer head dim
-    constexpr int CPR = DI / 8;          // 16-byte chunks per key row
-    constexpr int kTileBytes = kKeyTile * DI * 2;
+    constexpr int RB = F8 ? DI : 2 * DI;         // bytes per key row
+    constexpr int CPR = RB / 16;                 // 16-byte chunks per key row
+    constexpr int KS = F8 ? DI / 64 : DI / 16;   // MFMA k-steps per key
+    constexpr int kTileBytes = kKeyTile * RB;
     constexpr int kDma = kTileBytes / 1024;                 // DMA instructions per tile
     constexpr int kDmaPerWave = kDma / kIdxWaves;
+    constexpr int kVmPerTile = kDmaPerWave + (F8 ? 1 : 0);  // + the key-scale transfer
     static_assert(kDmaPerWave >= 1 && kDma % kIdxWaves == 0, "tile split");
-    __shared__ __attribute__((aligned(16))) uint8_t ktile[kTileRing][kTileBytes];
+    // FP8: a slot also holds the tile's 128 key scales after its key rows (in
+    // the same LDS object, so the compiler's own DMA tracking adds no waits)
+    constexpr int kSlotBytes = kTileBytes + (F8 ? 4 * kKeyTile : 0);
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[kTileRing][kSlotBytes];
+    typedef typename QOperand<F8>::type QOp;
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
 
@@ -69,20 +104,39 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     const int pos = active ? min(a.batch.q_pos[qi], L - 1) : -1;
 
     // A operand (query heads x d) and the w of the 16 rows this lane reduces
-    bf16x8 qf[MB][KS];
+    // (times the query scale of that row in FP8)
+    QOp qf[MB][KS];
     float wr[MB][16];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int h = 32 * mb + col;
         const bool hv = active && h < a.n_heads;
-        const __bf16 *qrow = a.q_idx + ((int64_t)(hv ? qi : 0) * a.n_heads + (hv ? h : 0)) * DI + 8 * g;
+        const int64_t qrow = (int64_t)(hv ? qi : 0) * a.n_heads + (hv ? h : 0);
+        if constexpr (F8) {
+            // lane half g takes dims 64 ks + 32 g .. +31 of k-step ks
+            const uint8_t *qp = (const uint8_t *)a.q_idx + qrow * DI + 32 * g;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qf[mb][ks] = hv ? *(const bf16x8 *)(qrow + 16 * ks) : zero_bf16x8();
+            for (int ks = 0; ks < KS; ++ks)
+                qf[mb][ks] = hv ? cat(*(const i32x4 *)(qp + 64 * ks), *(const i32x4 *)(qp + 64 * ks + 16))
+                                : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        } else {
+            const __bf16 *qp = (const __bf16 *)a.q_idx + qrow * DI + 8 * g;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[mb][ks] = hv ? *(const bf16x8 *)(qp + 16 * ks) : zero_bf16x8();
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int hh = 32 * mb + 8 * (e >> 2) + 4 * g + (e & 3);
-            wr[mb][e] = (active && hh < a.n_heads) ? a.w[(int64_t)qi * a.n_heads + hh] : 0.f;
+            if constexpr (F8) {
+                // unconditional loads (of row 0 for idle rows): no branch per element
+                const bool v = active && hh < a.n_heads;
+                const int64_t at = v ? (int64_t)qi * a.n_heads + hh : 0;
+                const float ws = a.w[at] * a.q_scale[at];
+                wr[mb][e] = v ? ws : 0.f;
+            } else {
+                wr[mb][e] = (active && hh < a.n_heads) ? a.w[(int64_t)qi * a.n_heads + hh] : 0.f;
+            }
         }
     }
 
@@ -95,18 +149,27 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         dma_r[u] = sidx / CPR;
         dma_c[u] = (sidx % CPR) ^ (dma_r[u] & (CPR - 1));
     }
-    // rows past the block's last position read that row instead (results unused)
+    const uint8_t *kbytes = (const uint8_t *)a.k_idx;
+    // rows past the block's last position read that row instead (results unused);
+    // FP8: every wave also brings 64 key scales (waves of equal parity write the
+    // same values to the same place)
     auto issue = [&](int t, int slot) {
 #pragma unroll
         for (int u = 0; u < kDmaPerWave; ++u) {
             const int j = min(t * kKeyTile + dma_r[u], pmax);
-            attn::dma16(a.k_idx + (kv0 + j) * DI + 8 * dma_c[u], &ktile[slot][(wv + kIdxWaves * u) * 1024]);
+            attn::dma16(kbytes + (kv0 + j) * RB + 16 * dma_c[u], &ktile[slot][(wv + kIdxWaves * u) * 1024]);
+        }
+        if constexpr (F8) {
+            const int j = min(t * kKeyTile + 64 * (wv & 1) + lane, pmax);
+            __builtin_amdgcn_global_load_lds(a.k_scale + kv0 + j,
+                                             (attn::lds_void_ptr)&ktile[slot][kTileBytes + 256 * (wv & 1)], 4, 0, 0);
         }
     };
 
     const int n_tiles = pmax / kKeyTile + 1;
     float *srow = a.scores + (int64_t)qi * a.ld;
     f32x16 prev[MB];
+    float prev_sk = 0.f;                                // FP8: scale of key prev_j0 + col
     int prev_j0 = -1;                                   // first key of the pending sub-tile
     // score of key prev_j0 + col for this lane (lane half 0 stores it): ReLU,
     // w and the head sum over four independent partial sums (a single chain
@@ -119,7 +182,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
             for (int e = 0; e < 16; ++e) ps[e & 3] += wr[mb][e] * relu(acc[mb][e]);
         float sc = (ps[0] + ps[1]) + (ps[2] + ps[3]);
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
-        return sc + __uint_as_float(g ? r[0] : r[1]);
+        sc += __uint_as_float(g ? r[0] : r[1]);
+        if constexpr (F8) sc *= prev_sk;
+        return sc;
     };
     auto store = [&](float sc, int j0) {
         const int j = j0 + col;
@@ -129,7 +194,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     for (int p = 0; p < kTileRing - 1; ++p) issue(p, p);
     for (int t = 0; t < n_tiles; ++t) {
         const int t0 = t * kKeyTile;
-        attn::wait_vm_blocks<kDmaPerWave>(kTileRing - 2);   // tile t landed (this wave's part)
+        attn::wait_vm_blocks<kVmPerTile>(kTileRing - 2);     // tile t landed (this wave's part)
         attn::lds_barrier();                                 // ... everywhere; tile t-1 done
         issue(t + kTileRing - 1, (t + kTileRing - 1) % kTileRing);
         const uint8_t *kt = ktile[t % kTileRing];
@@ -146,17 +211,27 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
             const int row = 32 * s + col;
-            const uint8_t *krow = kt + row * (DI * 2);
+            const uint8_t *krow = kt + row * RB;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 bk = *(const bf16x8 *)(krow + 16 * ((2 * ks + g) ^ (row & (CPR - 1))));
+                if constexpr (F8) {
+                    // chunks 4 ks + 2 g and the next: the dims the A operand holds
+                    const int c0 = 4 * ks + 2 * g;
+                    const i32x8 bk = cat(*(const i32x4 *)(krow + 16 * (c0 ^ (row & (CPR - 1)))),
+                                         *(const i32x4 *)(krow + 16 * ((c0 + 1) ^ (row & (CPR - 1)))));
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(qf[mb][ks], bk, acc[mb]);
+                    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_e4m3(qf[mb][ks], bk, acc[mb]);
+                } else {
+                    const bf16x8 bk = *(const bf16x8 *)(krow + 16 * ((2 * ks + g) ^ (row & (CPR - 1))));
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(qf[mb][ks], bk, acc[mb]);
+                }
             }
             sc[s] = epilogue(prev);                      // garbage before the first sub-tile: not stored
             sj[s] = prev_j0;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) prev[mb] = acc[mb];
+            if constexpr (F8) prev_sk = ((const float *)(kt + kTileBytes))[row];
             prev_j0 = t0 + 32 * s;
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -168,19 +243,24 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     store(epilogue(prev), prev_j0);
 }
 
-template <int KS, int MB>
+template <int DI, int MB, bool F8>
 hipError_t launch_t(const IndexerArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((indexer_kernel<KS, MB>), dim3(a.n_blocks), dim3(kIdxThreads), 0, s, a);
+    hipLaunchKernelGGL((indexer_kernel<DI, MB, F8>), dim3(a.n_blocks), dim3(kIdxThreads), 0, s, a);
     return hipGetLastError();
+}
+
+template <bool F8>
+hipError_t launch_dtype(const IndexerArgs &a, hipStream_t s) {
+    const bool two = a.n_heads > 32;
+    if (a.head_dim == 128) return two ? launch_t<128, 2, F8>(a, s) : launch_t<128, 1, F8>(a, s);
+    return two ? launch_t<64, 2, F8>(a, s) : launch_t<64, 1, F8>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t s) {
     if (a.n_blocks <= 0) return hipSuccess;
-    const bool two = a.n_heads > 32;
-    if (a.head_dim == 128) return two ? launch_t<8, 2>(a, s) : launch_t<8, 1>(a, s);
-    return two ? launch_t<4, 2>(a, s) : launch_t<4, 1>(a, s);
+    return a.fp8 ? launch_dtype<true>(a, s) : launch_dtype<false>(a, s);
 }
 
 }  // namespace mla

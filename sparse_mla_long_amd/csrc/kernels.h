@@ -16,14 +16,17 @@ struct BatchDev {
 
 struct IndexerArgs {
     BatchDev batch;
-    const __bf16 *q_idx;   // [total_q, n_heads, head_dim]
-    const __bf16 *k_idx;   // [total_kv, head_dim]
+    const void *q_idx;     // [total_q, n_heads, head_dim] bf16, or E4M3 codes
+    const void *k_idx;     // [total_kv, head_dim] bf16, or E4M3 codes
+    const float *q_scale;  // E4M3: [total_q, n_heads] fp32, >= 0
+    const float *k_scale;  // E4M3: [total_kv] fp32, >= 0
     const float *w;        // [total_q, n_heads]
     float *scores;         // [total_q, ld]
     int64_t ld;
     int32_t n_heads;
     int32_t head_dim;
     int32_t n_blocks;      // sum over sequences of ceil(n_q(b) / queries per block)
+    bool fp8;              // E4M3 queries and keys with scales
 };
 constexpr int kIdxQueriesPerBlock = 8;
 

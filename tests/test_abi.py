@@ -69,6 +69,11 @@ def idx_call(lib, b, q=FAKE, k=FAKE, w=FAKE, H=64, D=128, s=FAKE, ld=None):
     return lib.mla_indexer_score(ctypes.byref(b), q, k, w, H, D, s, ld, None)
 
 
+def idx8_call(lib, b, q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, w=FAKE, H=64, D=128, s=FAKE, ld=None):
+    ld = b.max_kv_len if ld is None else ld
+    return lib.mla_indexer_score_fp8(ctypes.byref(b), q, qs, k, ks, w, H, D, s, ld, None)
+
+
 def topk_call(lib, b, s=FAKE, ld=None, k=8, out=FAKE):
     ld = b.max_kv_len if ld is None else ld
     return lib.mla_topk_select(ctypes.byref(b), s, ld, k, out, None)
@@ -96,6 +101,7 @@ def test_bad_batches_rejected_by_every_call(lib, kw, code):
     b, keep = make_batch(**kw)
     assert idx_call(lib, b) == code
     assert lib.mla_last_error()
+    assert idx8_call(lib, b) == code
     assert topk_call(lib, b) == code
     assert attn_call(lib, b) == code
 
@@ -114,6 +120,23 @@ def test_indexer_argument_checks(lib):
     assert idx_call(lib, b, q=None) == INVALID
     assert idx_call(lib, b, q=FAKE + 8) == INVALID            # misaligned bf16 rows
     assert idx_call(lib, b, s=FAKE + 2) == INVALID
+
+
+def test_indexer_fp8_argument_checks(lib):
+    b, keep = make_batch()
+    assert idx8_call(lib, b, H=0) == INVALID
+    assert idx8_call(lib, b, H=65) == UNSUPPORTED
+    assert idx8_call(lib, b, D=96) == UNSUPPORTED
+    assert idx8_call(lib, b, ld=9) == INVALID
+    assert idx8_call(lib, b, qs=None) == INVALID
+    assert b"scale" in lib.mla_last_error()
+    assert idx8_call(lib, b, ks=None) == INVALID
+    assert idx8_call(lib, b, k=None) == INVALID
+    assert idx8_call(lib, b, q=FAKE + 8) == INVALID           # misaligned code rows
+    assert idx8_call(lib, b, ks=FAKE + 2) == INVALID          # misaligned scales
+    assert idx8_call(lib, b, qs=FAKE + 1) == INVALID
+    empty, keep2 = make_batch(cu_q=(0, 0), cu_kv=(0, 10))
+    assert idx8_call(lib, empty, q=None, qs=None, k=None, ks=None, w=None, s=None) == sm.MLA_OK
 
 
 def test_topk_argument_checks(lib):

@@ -2,7 +2,8 @@
 
 Staged so errors do not compound (the comparison procedure of the method):
   * indexer scores vs the oracle's, |g - r| <= 1e-3 |r| + 1e-4 (fp32 sums of
-    exact bf16 products); bit-exact on small-integer inputs;
+    exact bf16 products); bit-exact on small-integer inputs; FP8 indexer
+    inputs add 2^-14 of the sum of absolute terms (the E4M3 MFMA's summation);
   * top-k bit-exact: the oracle's selection run on the GPU's own score rows;
   * attention on the GPU's own index lists, |g - r| <= atol + rtol |r| with
     atol = rtol = 2e-2 for bf16 KV and 6e-2 for FP8 KV (out and LSE);
@@ -64,16 +65,45 @@ def to_gpu(inp):
     return out
 
 
+# The E4M3 MFMA does not sum its 64 products like IEEE fp32: its error is a
+# fraction of the magnitude of the terms, not of the result (measured up to
+# 2^-16.4 of sum |terms| on these inputs; FP8 matrix units are known to keep
+# a limited number of accumulation bits). FP8 indexer scores therefore get an
+# absolute allowance of 2^-14 of M_ij = sum_h w_ih sum_d |q_ihd k_jd| (decoded
+# and scaled), on top of the indexer tolerance; M_ij is the oracle's score of
+# the sign-cleared codes, where every dot product is non-negative.
+FP8_SUM_REL = 2.0 ** -14
+
+
+def fp8_score_magnitude(inp, rows):
+    mag_inp = dict(inp)
+    mag_inp["q_idx"] = inp["q_idx"] & 0x7f
+    mag_inp["k_idx"] = inp["k_idx"] & 0x7f
+    return oracle.indexer_rows(mag_inp, rows)
+
+
+def run_path(sm, batch, inp):
+    """indexer (bf16 or FP8 inputs) -> top-k -> sparse attention on the GPU."""
+    wl = inp["workload"]
+    if inp.get("k_idx_scale") is not None:
+        scores = sm.indexer_score_fp8(batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"],
+                                      inp["k_idx_scale"], inp["w"])
+    else:
+        scores = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
+    idx = sm.topk_select(batch, scores, wl.topk)
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale)
+    return out, lse, idx, scores
+
+
 def check_path(sm, inp, rows, label, check_indexer=True):
     """Run indexer -> top-k -> attention on the GPU for the whole batch and
     check the given rows against the oracle, stage by stage."""
     wl = inp["workload"]
     batch = sm.Batch.from_inputs(inp)
-    say("[%s] GPU path: %d queries, %d KV rows, H=%d, k=%d, kv=%s" %
-        (label, wl.total_q, wl.total_kv, wl.n_heads, wl.topk, inp["kv_dtype"]))
-    scores = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
-    idx = sm.topk_select(batch, scores, wl.topk)
-    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale)
+    say("[%s] GPU path: %d queries, %d KV rows, H=%d, k=%d, kv=%s, indexer=%s" %
+        (label, wl.total_q, wl.total_kv, wl.n_heads, wl.topk, inp["kv_dtype"],
+         inp.get("idx_dtype", "bf16")))
+    out, lse, idx, scores = run_path(sm, batch, inp)
     torch.cuda.synchronize()
     q_pos = inp["q_pos_host"]
     rows = np.asarray(rows)
@@ -83,8 +113,12 @@ def check_path(sm, inp, rows, label, check_indexer=True):
     if check_indexer:
         say("[%s] oracle indexer on %d rows" % (label, len(rows)))
         r_scores = oracle.indexer_rows(inp, rows)
+        fp8 = inp.get("k_idx_scale") is not None
+        if fp8:
+            mag = fp8_score_magnitude(inp, rows)
         for t, r in enumerate(rows):
-            assert_close("%s indexer row %d" % (label, r), g_scores[t], r_scores[t], 1e-4, 1e-3)
+            atol = 1e-4 + FP8_SUM_REL * mag[t] if fp8 else 1e-4
+            assert_close("%s indexer row %d" % (label, r), g_scores[t], r_scores[t], atol, 1e-3)
     say("[%s] oracle top-k on the GPU's scores" % label)
     r_idx = oracle.topk_rows(g_scores, q_pos[rows], wl.topk)
     mism = np.nonzero((r_idx != g_idx).any(axis=1))[0]
@@ -187,6 +221,45 @@ def test_indexer_small_integers_bit_exact(sm, H, D):
         assert np.array_equal(sc[i, : i + 1].cpu().numpy(), ref[i]), i
 
 
+@pytest.mark.parametrize("H,D", [(64, 128), (4, 64), (33, 128)])
+def test_indexer_fp8_small_integers_bit_exact(sm, H, D):
+    """FP8 indexer on integer codes (|x| <= 8 is exact in E4M3) with
+    power-of-two scales per (query, head) and per key: every product, partial
+    sum and scaling is exact in fp32, so the scores equal the oracle's
+    exactly. Unequal scales pin which row each scale belongs to."""
+    g = torch.Generator().manual_seed(7 * H + D)
+    L, nq = 333, 333
+    q = torch.randint(-8, 9, (nq, H, D), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8)
+    k = torch.randint(-8, 9, (L, D), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8)
+    qs = torch.ldexp(torch.ones(nq, H), torch.randint(-3, 4, (nq, H), generator=g))
+    ks = torch.ldexp(torch.ones(L), torch.randint(-3, 4, (L,), generator=g))
+    w = torch.randint(0, 5, (nq, H), generator=g).float()
+    inp = {"q_idx": q, "k_idx": k, "q_idx_scale": qs, "k_idx_scale": ks, "w": w,
+           "cu_seqlens_q_host": np.array([0, nq], np.int32),
+           "cu_seqlens_kv_host": np.array([0, L], np.int32),
+           "q_pos_host": np.arange(nq, dtype=np.int32)}
+    batch = sm.Batch([0, nq], [0, L], np.arange(nq), "cuda")
+    sc = sm.indexer_score_fp8(batch, q.cuda(), qs.cuda(), k.cuda(), ks.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    ref = oracle.indexer_rows(inp, np.arange(nq))
+    for i in range(nq):
+        assert np.array_equal(sc[i, : i + 1].cpu().numpy(), ref[i]), i
+
+
+@pytest.mark.parametrize("idx_heads,idx_dim", [(4, 64), (64, 128), (48, 128)])
+def test_indexer_fp8_path_all_rows(sm, idx_heads, idx_dim):
+    """FP8 indexer inputs through the whole path, every row: scores within
+    the indexer tolerance, top-k bit-exact on those scores, attention on the
+    GPU's lists. Ragged: an empty sequence, a CP-style gap in the positions,
+    a one-token sequence, rows shorter than k and partial key tiles."""
+    wl = mla_inputs.Workload("fp8-indexer", (300, 0, 1000, 1, 130),
+                             (((0, 300),), (), ((0, 70), (930, 1000)), ((0, 1),), ((64, 130),)),
+                             n_heads=64, idx_heads=idx_heads, idx_dim=idx_dim, topk=96,
+                             kv_dtype="fp8", seed=29)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu", idx_dtype="fp8"))
+    check_path(sm, inp, np.arange(wl.total_q), "fp8-indexer-%dx%d" % (idx_heads, idx_dim))
+
+
 # ----------------------------------------------------------------- top-k --
 @pytest.mark.parametrize("kind", ["all_equal", "relu_zeros", "small_int", "signed_zero", "normal",
                                   "coarse", "sample_low", "sample_high"])
@@ -252,17 +325,17 @@ def test_inline_scale_row_layout(sm):
 
 
 # ------------------------------------------------------- full-size workloads --
-FULL = [("sparse32k", "fp8"), ("sparse32k", "bf16"), ("dense16k", "bf16"), ("cp131k", "fp8"),
-        ("ragged", "fp8")]
+FULL = [("sparse32k", "fp8", "bf16"), ("sparse32k", "bf16", "bf16"), ("dense16k", "bf16", "bf16"),
+        ("cp131k", "fp8", "bf16"), ("ragged", "fp8", "bf16"), ("sparse32k", "fp8", "fp8")]
 
 
-@pytest.mark.parametrize("name,kv_dtype", FULL)
-def test_full_size_sampled_rows(sm, name, kv_dtype):
+@pytest.mark.parametrize("name,kv_dtype,idx_dtype", FULL)
+def test_full_size_sampled_rows(sm, name, kv_dtype, idx_dtype):
     wl = mla_inputs.WORKLOADS[name]
     n_rows = int(os.environ.get("MLA_PARITY_ROWS", "48"))
     rows = mla_inputs.sample_rows(wl, n_rows)
-    say("[%s/%s] generating inputs on the GPU" % (name, kv_dtype))
-    inp = mla_inputs.make_inputs(wl, "cuda", kv_dtype=kv_dtype)
+    say("[%s/%s/indexer %s] generating inputs on the GPU" % (name, kv_dtype, idx_dtype))
+    inp = mla_inputs.make_inputs(wl, "cuda", kv_dtype=kv_dtype, idx_dtype=idx_dtype)
     if wl.dense:
         batch = sm.Batch.from_inputs(inp)
         out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], None, None, wl.sm_scale)
@@ -273,7 +346,7 @@ def test_full_size_sampled_rows(sm, name, kv_dtype):
         assert_close("dense16k out", out[rt].float().cpu().numpy(), r_out, 2e-2, 2e-2)
         assert_close("dense16k lse", lse[rt].cpu().numpy(), r_lse, 2e-2, 2e-2)
     else:
-        check_path(sm, inp, rows, "%s-%s" % (name, kv_dtype))
+        check_path(sm, inp, rows, "%s-%s-idx%s" % (name, kv_dtype, idx_dtype))
     del inp
     torch.cuda.empty_cache()
 

@@ -119,6 +119,69 @@ def test_indexer_single_head_is_relu_dot():
     assert (got == 0).any() and (got > 0).any()
 
 
+# ------------------------------------------------------------ FP8 indexer --
+def _e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """torch's float32 -> float8_e4m3fn cast (RNE), as raw codes."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _torch_e4m3(codes: np.ndarray) -> np.ndarray:
+    """torch's float8_e4m3fn decode (a library decoder, not the oracle's)."""
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(
+        torch.float8_e4m3fn).double().numpy()
+
+
+@pytest.mark.parametrize("H,D", [(4, 64), (3, 128)])
+def test_indexer_fp8_power_of_two_scales_equal_bf16_path(H, D):
+    """An E4M3 code times a power of two is exact in bf16, so with
+    power-of-two scales the FP8 indexer must equal the (pinned) bf16 indexer
+    on the bf16 encodings of the decoded, scaled values -- bit for bit, since
+    both sum the same fp64 terms in the same order. Scales differ per
+    (query, head) and per key, which pins the row each scale belongs to."""
+    rng = np.random.default_rng(31 + H)
+    n, L = 7, 45
+    qc = _e4m3_codes(rng.standard_normal((n, H, D)) * 20)
+    kc = _e4m3_codes(rng.standard_normal((L, D)) * 20)
+    qs = np.ldexp(1.0, rng.integers(-6, 4, (n, H))).astype(np.float32)
+    ks = np.ldexp(1.0, rng.integers(-6, 4, L)).astype(np.float32)
+    w = rng.uniform(0, 1, (n, H)).astype(np.float32)
+    p = rng.integers(0, L, n).astype(np.int32)
+    got = oracle.indexer_seq_fp8(qc, qs, kc, ks, w, p)
+    qv = _torch_e4m3(qc) * qs[:, :, None]
+    kv = _torch_e4m3(kc) * ks[:, None]
+    qb, kb = bf16_bits(qv), bf16_bits(kv)
+    assert np.array_equal(oracle.bf16_bits_to_f64(qb), qv)      # the encodings are exact
+    assert np.array_equal(oracle.bf16_bits_to_f64(kb), kv)
+    ref = oracle.indexer_seq(qb, kb, w, p)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert (got[~np.isnan(got)] > 0).any() and (got[~np.isnan(got)] == 0).any()
+
+
+def test_indexer_fp8_general_scales_brute_force():
+    """Arbitrary positive scales: the FP8 indexer equals a numpy evaluation of
+    sum_h w * max(0, (sq qc) . (sk kc)) on torch-decoded codes; scaling every
+    key scale by c > 0 scales every score by c (the scale multiplies, once)."""
+    rng = np.random.default_rng(77)
+    n, H, D, L = 5, 4, 64, 33
+    qc = _e4m3_codes(rng.standard_normal((n, H, D)) * 50)
+    kc = _e4m3_codes(rng.standard_normal((L, D)) * 50)
+    qs = rng.uniform(0.01, 3.0, (n, H)).astype(np.float32)
+    ks = rng.uniform(0.01, 3.0, L).astype(np.float32)
+    w = rng.uniform(0, 1, (n, H)).astype(np.float32)
+    p = np.full(n, L - 1, np.int32)
+    got = oracle.indexer_seq_fp8(qc, qs, kc, ks, w, p)
+    qv = _torch_e4m3(qc) * qs.astype(np.float64)[:, :, None]
+    kv = _torch_e4m3(kc) * ks.astype(np.float64)[:, None]
+    dots = np.einsum("ihd,jd->ihj", qv, kv)
+    ref = np.einsum("ih,ihj->ij", w.astype(np.float64), np.maximum(dots, 0.0))
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-9)
+    c = np.float32(0.375)
+    got_c = oracle.indexer_seq_fp8(qc, qs, kc, ks * c, w, p)
+    np.testing.assert_allclose(got_c, got * np.float64(c), rtol=1e-6)
+
+
 # -------------------------------------------------------------------- top-k --
 def _brute_topk(s, p, k):
     cand = list(range(p + 1))
