@@ -222,6 +222,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sparse32k")
     ap.add_argument("--kv-dtype", default=None, help="override the workload's KV dtype (bf16/fp8)")
+    ap.add_argument("--split", type=int, default=None,
+                    help="attention through mla_sparse_prefill_split with this many parts per "
+                         "query (0: chosen from the CU count)")
     ap.add_argument("--indexer-dtype", default="bf16", choices=("bf16", "fp8"),
                     help="indexer queries and keys: bf16, or E4M3 codes with an fp32 scale per "
                          "row (mla_indexer_score_fp8)")
@@ -270,6 +273,11 @@ def main():
     out = torch.empty((wl.total_q, wl.n_heads, D_V), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((wl.total_q, wl.n_heads), dtype=torch.float32, device=dev)
     names = ["attention"] if wl.dense else ["indexer", "topk", "attention"]
+    split_ws = None
+    if args.split is not None:
+        need = sm.load_library().mla_sparse_prefill_split_workspace_size(wl.total_q, wl.n_heads,
+                                                                          args.split)
+        split_ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         def mark(i):
@@ -278,7 +286,7 @@ def main():
         if wl.dense:
             mark(0)
             sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], None, wl.sm_scale,
-                              out=out, lse=lse)
+                              out=out, lse=lse, n_split=args.split, workspace=split_ws)
             mark(1)
             return
         mark(0)
@@ -291,7 +299,7 @@ def main():
         sm.topk_select(batch, scores, wl.topk, indices=indices)
         mark(2)
         sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], indices, wl.sm_scale,
-                          out=out, lse=lse)
+                          out=out, lse=lse, n_split=args.split, workspace=split_ws)
         mark(3)
 
     if args.copy_calibration_mib > 0:
@@ -368,6 +376,7 @@ def main():
         "config": {"workload": wl.name, "seq_lens": list(wl.kv_lens), "total_q": wl.total_q,
                    "n_heads": wl.n_heads, "indexer": "%dx%d" % (wl.idx_heads, wl.idx_dim),
                    "indexer_dtype": None if wl.dense else idx_dtype,
+                   "attention_split": args.split,
                    "topk": None if wl.dense else wl.topk, "kv_dtype": kv_dtype,
                    "dense": wl.dense, "parallelism": "single GPU"},
         "mfma_peak_frac": mfma_frac,

@@ -23,6 +23,8 @@
  *   mla_merge_attention combines attention results over disjoint key sets
  *                       (key shards, or splits of one query's keys) through
  *                       their log-sum-exp.
+ *   mla_sparse_prefill_split  split-KV attention: each query's keys in up to
+ *                       16 parts run as separate work items, then merged.
  *
  * Batches are packed: sequence b owns query rows [cu_q[b], cu_q[b+1]) and
  * latent-KV rows [cu_kv[b], cu_kv[b+1]); every query carries its true
@@ -172,6 +174,36 @@ mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const v
                                 int64_t kv_row_stride, int64_t kv_scale_stride,
                                 const int32_t *indices, int32_t k, int32_t n_heads,
                                 float sm_scale, void *out, float *lse, void *stream);
+
+/* Split-KV form of mla_sparse_prefill: the same out and lse, computed with
+ * every query's keys cut into n_split parts that run as separate work items,
+ * so a batch with fewer queries than the GPU has compute units still fills
+ * it. The parts' (out, lse) pairs are combined by the log-sum-exp merge of
+ * the spke.com article, section "DCP" (as mla_merge_attention).
+ * Parts are contiguous and differ in size by at most one: entries
+ * [floor(p k / n_split), floor((p+1) k / n_split)) of each index row, or,
+ * with indices == NULL, keys [floor(p n / n_split), floor((p+1) n / n_split))
+ * of the n = q_pos[i] + 1 causal keys (a part may then be empty).
+ * Arguments as mla_sparse_prefill, plus:
+ *   n_split    1..16; <= k when indices != NULL. 1 runs mla_sparse_prefill.
+ *              0 chooses min(16, max(1, CUs of the current device / total_q)),
+ *              and at most k: one round of work items over the GPU.
+ *   workspace  device, 256-byte aligned, at least
+ *              mla_sparse_prefill_split_workspace_size(total_q, n_heads, n_split)
+ *              bytes (n_split 0: the size for the automatic choice with no k
+ *              limit, which covers every k), owned by the caller; it holds the
+ *              parts' bf16 outputs and fp32 LSEs between the two launches
+ *              (unused when the split is 1).
+ * The parts' outputs are rounded to bf16 before the merge, so results differ
+ * from mla_sparse_prefill by about one more bf16 rounding.
+ * MLA_ERR_UNSUPPORTED also when total_q * n_split exceeds INT32_MAX. */
+size_t mla_sparse_prefill_split_workspace_size(int32_t total_q, int32_t n_heads, int32_t n_split);
+mla_status_t mla_sparse_prefill_split(const mla_batch_t *batch, const void *q, const void *kv,
+                                      const float *kv_scale, mla_kv_dtype_t kv_dtype,
+                                      int64_t kv_row_stride, int64_t kv_scale_stride,
+                                      const int32_t *indices, int32_t k, int32_t n_heads,
+                                      float sm_scale, int32_t n_split, void *workspace,
+                                      size_t workspace_bytes, void *out, float *lse, void *stream);
 
 /* Merge of attention results over disjoint key sets by their log-sum-exp
  * (spke.com article, section "DCP": every GPU attends over its share of the

@@ -117,9 +117,9 @@ def _resume(cached: Sequence[int], new: Sequence[int]):
 
 _RAGGED_KV, _RAGGED_Q = _resume([8960, 32512, 65280, 196608], [512, 2048, 4096, 6144])
 
-# The five workloads: tiny (oracle on every row), dense 16k, sparse 32k,
-# one rank's context-parallel share of a 131,072-token prompt, and a ragged
-# prefix-resume batch.
+# The workloads: tiny (oracle on every row), dense 16k, sparse 32k, one
+# rank's context-parallel share of a 131,072-token prompt, a ragged
+# prefix-resume batch, and a 64-token resume behind a 32k prefix.
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", (1024,), (((0, 1024),),), n_heads=8, idx_heads=4, idx_dim=64,
                      topk=256, kv_dtype="bf16", seed=0),
@@ -131,6 +131,10 @@ WORKLOADS: Dict[str, Workload] = {
                        idx_heads=64, idx_dim=128, topk=2048, kv_dtype="fp8", seed=3),
     "ragged": Workload("ragged", _RAGGED_KV, _RAGGED_Q, n_heads=64, idx_heads=64, idx_dim=128,
                        topk=2048, kv_dtype="fp8", seed=4),
+    # a short new chunk behind a long cached prefix: fewer queries than the
+    # GPU has compute units (the split-KV case)
+    "resume64": Workload("resume64", *_resume([32704], [64]), n_heads=64, idx_heads=64,
+                         idx_dim=128, topk=2048, kv_dtype="fp8", seed=5),
 }
 
 

@@ -4,6 +4,7 @@
 // enqueues nothing and touches no device. Device data (q_pos, indices) is
 // trusted; kernels clamp positions into their sequence so a bad q_pos cannot
 // read outside the sequence's rows.
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string>
@@ -118,7 +119,21 @@ mla_status_t indexer(const mla_batch_t *batch, const void *q_idx, const float *q
     a.ld = ld_scores;
     a.n_heads = n_heads;
     a.head_dim = head_dim;
-    a.n_blocks = (int32_t)blocks;
+    // Few query blocks (a short chunk behind a long prefix): split every
+    // block's keys over several workgroups, about two per CU in all, down to
+    // one 128-key tile each. Each score is still written once.
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        n_cu = 1;
+    int64_t split = 1;
+    if (blocks > 0 && blocks < 2 * (int64_t)n_cu) {
+        split = (2 * (int64_t)n_cu + blocks - 1) / blocks;
+        split = std::min<int64_t>(split, ((int64_t)batch->max_kv_len + 127) / 128);
+        split = std::max<int64_t>(split, 1);
+    }
+    a.key_split = (int32_t)split;
+    a.n_blocks = (int32_t)(blocks * split);
     a.fp8 = fp8;
     return hip_status(mla::launch_indexer(a, (hipStream_t)stream), "indexer launch");
 }
@@ -164,13 +179,16 @@ mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int6
     return hip_status(mla::launch_topk(a, (hipStream_t)stream), "top-k launch");
 }
 
-mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const void *kv,
-                                const float *kv_scale, mla_kv_dtype_t kv_dtype,
-                                int64_t kv_row_stride, int64_t kv_scale_stride,
-                                const int32_t *indices, int32_t k, int32_t n_heads,
-                                float sm_scale, void *out, float *lse, void *stream) {
-    mla::AttnArgs a{};
-    mla_status_t st = check_batch(batch, &a.batch);
+namespace {
+// Checks shared by the attention entry points; fills everything of `a` but the
+// outputs and the split. *none: valid, but there is no query (nothing to run).
+mla_status_t attention_args(const mla_batch_t *batch, const void *q, const void *kv,
+                            const float *kv_scale, mla_kv_dtype_t kv_dtype, int64_t kv_row_stride,
+                            int64_t kv_scale_stride, const int32_t *indices, int32_t k,
+                            int32_t n_heads, float sm_scale, void *out, float *lse,
+                            mla::AttnArgs *a, bool *fp8_out, bool *none) {
+    *none = false;
+    mla_status_t st = check_batch(batch, &a->batch);
     if (st != MLA_OK) return st;
     if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
         return fail(MLA_ERR_INVALID_ARG, "unknown kv_dtype %d", (int)kv_dtype);
@@ -194,7 +212,10 @@ mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const v
     if (fp8 && (int64_t)batch->max_kv_len * kv_scale_stride > (int64_t)UINT32_MAX)
         return fail(MLA_ERR_UNSUPPORTED, "a sequence's KV scales span %lld bytes (>= 4 GiB)",
                     (long long)batch->max_kv_len * kv_scale_stride);
-    if (batch->total_q == 0) return ok();
+    if (batch->total_q == 0) {
+        *none = true;
+        return ok();
+    }
     if (!q || !kv || !out || !lse || (fp8 && !kv_scale))
         return fail(MLA_ERR_INVALID_ARG, "q / kv / out / lse%s is NULL", fp8 ? " / kv_scale" : "");
     if (!aligned(q, 16) || !aligned(kv, 16))
@@ -202,18 +223,111 @@ mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const v
     if (!aligned(out, 16) || !aligned(lse, 4) || (fp8 && !aligned(kv_scale, 4)) ||
         (indices && !aligned(indices, 4)))
         return fail(MLA_ERR_INVALID_ARG, "out / lse / kv_scale / indices misaligned");
-    a.q = (const __bf16 *)q;
-    a.kv = (const uint8_t *)kv;
-    a.kv_scale = (const uint8_t *)kv_scale;
-    a.kv_stride = kv_row_stride;
-    a.scale_stride = kv_scale_stride;
-    a.indices = indices;
-    a.k = indices ? k : 0;
-    a.n_heads = n_heads;
-    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    a->q = (const __bf16 *)q;
+    a->kv = (const uint8_t *)kv;
+    a->kv_scale = (const uint8_t *)kv_scale;
+    a->kv_stride = kv_row_stride;
+    a->scale_stride = kv_scale_stride;
+    a->indices = indices;
+    a->k = indices ? k : 0;
+    a->idx_ld = indices ? k : 0;
+    a->n_heads = n_heads;
+    a->scale_log2 = sm_scale * 1.4426950408889634f;
+    *fp8_out = fp8;
+    return ok();
+}
+
+// Workspace of a split-KV call: the parts' outputs, then their LSEs.
+size_t split_o_bytes(int64_t total_q, int64_t n_heads, int64_t n_split) {
+    return ((size_t)(n_split * total_q * n_heads * MLA_V_DIM * 2) + 255) / 256 * 256;
+}
+
+// n_split == 0: as many parts as fill the current device's compute units once
+// (CUs / total_q), 1..16, and at most k when a list is given.
+int32_t auto_split(int64_t total_q, int32_t k_or_0) {
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+        n_cu = 1;
+    int64_t s = total_q > 0 ? n_cu / total_q : 1;
+    s = std::max<int64_t>(1, std::min<int64_t>(s, mla::kMergeMaxParts));
+    if (k_or_0 > 0) s = std::min<int64_t>(s, k_or_0);
+    return (int32_t)s;
+}
+}  // namespace
+
+mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const void *kv,
+                                const float *kv_scale, mla_kv_dtype_t kv_dtype,
+                                int64_t kv_row_stride, int64_t kv_scale_stride,
+                                const int32_t *indices, int32_t k, int32_t n_heads,
+                                float sm_scale, void *out, float *lse, void *stream) {
+    mla::AttnArgs a{};
+    bool fp8 = false, none = false;
+    mla_status_t st = attention_args(batch, q, kv, kv_scale, kv_dtype, kv_row_stride, kv_scale_stride,
+                                     indices, k, n_heads, sm_scale, out, lse, &a, &fp8, &none);
+    if (st != MLA_OK || none) return st;
+    a.n_split = 1;
     a.out = (__bf16 *)out;
     a.lse = lse;
     return hip_status(mla::launch_attention(a, fp8, (hipStream_t)stream), "attention launch");
+}
+
+size_t mla_sparse_prefill_split_workspace_size(int32_t total_q, int32_t n_heads, int32_t n_split) {
+    if (n_split == 0) n_split = auto_split(total_q, 0);
+    if (total_q <= 0 || n_heads <= 0 || n_split <= 1) return 0;
+    return split_o_bytes(total_q, n_heads, n_split) + (size_t)n_split * total_q * n_heads * 4;
+}
+
+mla_status_t mla_sparse_prefill_split(const mla_batch_t *batch, const void *q, const void *kv,
+                                      const float *kv_scale, mla_kv_dtype_t kv_dtype,
+                                      int64_t kv_row_stride, int64_t kv_scale_stride,
+                                      const int32_t *indices, int32_t k, int32_t n_heads,
+                                      float sm_scale, int32_t n_split, void *workspace,
+                                      size_t workspace_bytes, void *out, float *lse, void *stream) {
+    if (n_split < 0) return fail(MLA_ERR_INVALID_ARG, "n_split must be >= 0 (got %d)", n_split);
+    if (n_split == 0 && batch && batch->total_q > 0) n_split = auto_split(batch->total_q, indices ? k : 0);
+    if (n_split == 0) n_split = 1;
+    if (n_split > mla::kMergeMaxParts)
+        return fail(MLA_ERR_UNSUPPORTED, "n_split %d > %d", n_split, mla::kMergeMaxParts);
+    if (indices && n_split > k)
+        return fail(MLA_ERR_INVALID_ARG, "n_split %d > k %d: every part needs a list entry", n_split, k);
+    mla::AttnArgs a{};
+    bool fp8 = false, none = false;
+    mla_status_t st = attention_args(batch, q, kv, kv_scale, kv_dtype, kv_row_stride, kv_scale_stride,
+                                     indices, k, n_heads, sm_scale, out, lse, &a, &fp8, &none);
+    if (st != MLA_OK || none) return st;
+    if (n_split == 1) {
+        a.n_split = 1;
+        a.out = (__bf16 *)out;
+        a.lse = lse;
+        return hip_status(mla::launch_attention(a, fp8, (hipStream_t)stream), "attention launch");
+    }
+    const int64_t total_q = batch->total_q;
+    if (total_q * n_split > (int64_t)INT32_MAX)
+        return fail(MLA_ERR_UNSUPPORTED, "total_q * n_split = %lld exceeds int32",
+                    (long long)(total_q * n_split));
+    const size_t need = mla_sparse_prefill_split_workspace_size((int32_t)total_q, n_heads, n_split);
+    if (!workspace) return fail(MLA_ERR_INVALID_ARG, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(MLA_ERR_INVALID_ARG, "workspace_bytes %zu < %zu", workspace_bytes, need);
+    uint8_t *ws = (uint8_t *)workspace;
+    const int64_t rows = total_q * n_heads;                 // (query, head) rows per part
+    a.n_split = n_split;
+    a.out = (__bf16 *)ws;
+    a.lse = (float *)(ws + split_o_bytes(total_q, n_heads, n_split));
+    st = hip_status(mla::launch_attention(a, fp8, (hipStream_t)stream), "attention launch");
+    if (st != MLA_OK) return st;
+    mla::MergeArgs m{};
+    for (int32_t r = 0; r < n_split; ++r) {
+        m.o[r] = a.out + r * rows * MLA_V_DIM;
+        m.lse[r] = a.lse + r * rows;
+    }
+    m.n_parts = n_split;
+    m.rows = rows;
+    m.out = (__bf16 *)out;
+    m.lse_out = lse;
+    return hip_status(mla::launch_merge(m, (hipStream_t)stream), "merge launch");
 }
 
 mla_status_t mla_merge_attention(const void *const *o_parts, const float *const *lse_parts,

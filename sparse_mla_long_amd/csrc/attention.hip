@@ -81,14 +81,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
     const int hg = wv >> 1, dh = wv & 1;                             // head group, dim half
     const int tid = threadIdx.x;
-    const int qi = a.batch.total_q - 1 - (int)blockIdx.x;
+    // virtual query v: part v % S of query row v / S (S = 1 without split-KV)
+    const int S = a.n_split;
+    const int vq = a.batch.total_q * S - 1 - (int)blockIdx.x;
+    const int qi = vq / S, part = vq - qi * S;
+    const int64_t orow = (int64_t)part * a.batch.total_q + qi;      // output row
     const int b = seq_of_row(a.batch.cu_q, a.batch.num_seqs, qi);
     const int64_t kv0 = a.batch.cu_kv[b];
     const int L = a.batch.cu_kv[b + 1] - (int)kv0;
     const int pos = min(a.batch.q_pos[qi], L - 1);
     const int H = a.n_heads;
-    const int n_keys = DENSE ? pos + 1 : a.k;
-    const int32_t *idx_row = DENSE ? nullptr : a.indices + (int64_t)qi * a.k;
+    // dense: keys [key_lo, key_lo + n_valid) of 0..pos (an empty part runs one
+    // masked entry); listed: entries [lo, hi) of the row (never empty: S <= k)
+    const int key_lo = DENSE ? part_begin(pos + 1, S, part) : part_begin(a.k, S, part);
+    const int n_valid = (DENSE ? part_begin(pos + 1, S, part + 1) : part_begin(a.k, S, part + 1)) - key_lo;
+    const int n_keys = max(n_valid, 1);
+    const int32_t *idx_row = DENSE ? nullptr : a.indices + (int64_t)qi * a.idx_ld + key_lo;
     const uint8_t *kvq = a.kv + kv0 * a.kv_stride;                   // row 0 of this sequence
     const int chunk_len = TABLE ? kIdx : n_keys;
 
@@ -222,6 +230,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     bool my_vote = false;                        // wave-uniform
     for (int c0 = 0; c0 < n_keys && !redo; c0 += chunk_len) {
         const int cn = min(chunk_len, n_keys - c0);               // entries in this chunk
+        const int cv = min(chunk_len, n_valid - c0);              // dense: the valid ones
         const int n_blk = (cn + kBlk - 1) / kBlk;
         const int n_ent = n_blk * kBlk;
         if (TABLE) {
@@ -243,7 +252,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 const int r = s_row[min(e, kTab - 1)];   // unconditional: no branch, one wait
                 return e < n_ent ? r : -1;
             }
-            return e < cn ? c0 + e : -1;
+            return e < cn ? key_lo + c0 + e : -1;
         };
         // DMA one block into ring slot `slot`: this wave issues instructions
         // wv, wv+4, ... (16-byte slot sidx = ins*64 + lane holds logical chunk
@@ -294,7 +303,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                     *(f32x4 *)bi = *(const f32x4 *)&s_bias[e0 + 4 * q4];
                 } else {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) bi[j] = e0 + 4 * q4 + j < cn ? 0.f : -INFINITY;
+                    for (int j = 0; j < 4; ++j) bi[j] = e0 + 4 * q4 + j < cv ? 0.f : -INFINITY;
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -340,7 +349,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     // ---- epilogue: l over both lane halves; LSE; O / l staged through LDS as bf16
     const float lt = l_run + xor32(l_run);
     if (dh == 0 && g == 0 && head < H)
-        a.lse[(int64_t)qi * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+        a.lse[orow * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     __bf16 *stage = (__bf16 *)smem + wv * 32 * O_LD;          // 32 heads x 256 bf16 per wave
 #pragma unroll
@@ -361,7 +370,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         const int h = 32 * hg + hr;
         if (h < H) {
             const u32x4 v = *(const u32x4 *)(stage + hr * O_LD + 8 * col);
-            *(u32x4 *)(a.out + ((int64_t)qi * H + h) * kV + kVHalf * dh + 8 * col) = v;
+            *(u32x4 *)(a.out + (orow * H + h) * kV + kVHalf * dh + 8 * col) = v;
         }
     }
 }
@@ -373,7 +382,8 @@ template <bool DENSE> hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute((const void *)attn_kernel<DENSE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_kernel<DENSE>), dim3(a.batch.total_q), dim3(kThreads), kLdsBytes, s, a);
+    hipLaunchKernelGGL((attn_kernel<DENSE>), dim3((unsigned)((int64_t)a.batch.total_q * a.n_split)), dim3(kThreads),
+                       kLdsBytes, s, a);
     return hipGetLastError();
 }
 

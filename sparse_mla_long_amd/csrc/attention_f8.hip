@@ -131,17 +131,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const int head = 32 * hg + col;
     const bool hv = head < H;
     const int total_q = a.batch.total_q;
+    const int S = a.n_split;                     // parts per query (virtual queries per row)
+    const int total_v = total_q * S;
 
-    // Persistent workgroup: its k-th query in snake order over the rows, last
-    // rows first (they have the most keys in causal batches), so the
-    // workgroups' totals stay even. -1 past the end.
+    // Persistent workgroup: its k-th virtual query in snake order over the
+    // rows, last rows first (they have the most keys in causal batches), so
+    // the workgroups' totals stay even. -1 past the end. Virtual query v is
+    // part v % S of query row v / S.
     auto query_of = [&](int k) -> int {
         const int G = (int)gridDim.x, bx = (int)blockIdx.x;
         const int r = k * G + ((k & 1) ? G - 1 - bx : bx);
-        return r < total_q ? total_q - 1 - r : -1;
+        return r < total_v ? total_v - 1 - r : -1;
     };
     // the current query and chunk (wave-uniform)
-    int qi = 0, qn = -1;                         // this query, the next one (or -1)
+    int qi = 0, qn = -1;                         // this query's row; the next virtual query (or -1)
+    int qn_row = 0;                              // the next virtual query's row
+    int64_t orow = 0;                            // output row: part * total_q + qi
+    int key_lo = 0, lim = 0;                     // dense: first key of the part; keys above lim are masked
     int pos = 0, n_keys = 0, n_steps = 1;
     int64_t kv0 = 0;
     const int32_t *idx_row = nullptr;
@@ -414,10 +420,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         asm volatile("" : "+v"(t));
         return t;
     };
-    // index list of query q into s_next (entries past the list repeat its last)
-    auto fetch_idx = [&](int q) {
-        const int cn0 = min(kIdx, a.k), t = tid_opq();
-        const int32_t *ib = a.indices + (int64_t)q * a.k;
+    // index list of virtual query v into s_next (entries past the list repeat its last)
+    auto fetch_idx = [&](int v) {
+        const int row = v / S, part = v - row * S;
+        const int lo = part_begin(a.k, S, part);
+        const int cn0 = min(kIdx, part_begin(a.k, S, part + 1) - lo), t = tid_opq();
+        const int32_t *ib = a.indices + (int64_t)row * a.idx_ld + lo;
 #pragma unroll
         for (int i = 0; i < kEnt; ++i)
             dma4_lds(ib, 4u * (uint32_t)min(t + kThreads * i, cn0 - 1), lds_addr(s_next) + 4u * (uint32_t)(kThreads * i + kWave * wv));
@@ -430,7 +438,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 #pragma unroll
         for (int i = 0; i < kEnt; ++i) {
             const int e = t + kThreads * i;
-            jv[i] = e < cn && jv[i] >= 0 && jv[i] <= pos ? jv[i] : -1;
+            jv[i] = e < cn && jv[i] >= 0 && jv[i] <= lim ? jv[i] : -1;
             s_row[e] = jv[i];
         }
         lds_barrier();                                   // rows posted
@@ -451,20 +459,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             return true;
         }
         if (q_next) {
-            q_go(qn, 0, sl1);
+            q_go(qn_row, 0, sl1);
             return true;
         }
         return false;
     };
     auto chunk_steps = [&](int c0) { return (min(kIdx, n_keys - c0) + kStepBlocks * kBlk - 1) / (kStepBlocks * kBlk); };
-    auto set_query = [&](int q) {
-        qi = q;
+    auto set_query = [&](int v) {
+        qi = v / S;
+        const int part = v - qi * S;
+        orow = (int64_t)part * total_q + qi;
         const int b = seq_of_row(a.batch.cu_q, a.batch.num_seqs, qi);
         kv0 = a.batch.cu_kv[b];
         const int L = a.batch.cu_kv[b + 1] - (int)kv0;
         pos = min(a.batch.q_pos[qi], L - 1);
-        n_keys = DENSE ? pos + 1 : a.k;
-        idx_row = DENSE ? nullptr : a.indices + (int64_t)qi * a.k;
+        if (DENSE) {             // keys [lo, hi) of 0..pos; an empty part runs one masked entry
+            key_lo = part_begin(pos + 1, S, part);
+            const int hi = part_begin(pos + 1, S, part + 1);
+            lim = hi - 1;
+            n_keys = hi - key_lo + (hi == key_lo ? 1 : 0);   // (not max(): that form spilled)
+        } else {                 // entries [lo, hi) of the list (never empty: S <= k)
+            const int lo = part_begin(a.k, S, part);
+            lim = pos;
+            n_keys = part_begin(a.k, S, part + 1) - lo;
+            idx_row = a.indices + (int64_t)qi * a.idx_ld + lo;
+        }
         kvq = a.kv + kv0 * a.kv_stride;
     };
 
@@ -475,8 +494,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     if (query_of(0) >= 0) {                       // uniform
         const int q0 = query_of(0);
         if (!DENSE) fetch_idx(q0);
-        q_go(q0, 0, 1);
-        q_go(q0, 1, 2);
+        q_go(q0 / S, 0, 1);
+        q_go(q0 / S, 1, 2);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
     }
@@ -486,6 +505,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         if (q < 0) break;                         // uniform
         set_query(q);
         qn = query_of(k + 1);
+        qn_row = qn >= 0 ? qn / S : 0;
         // chunk 0 staged ahead of the loops: its row table (from the index list
         // prefetched into s_next), the gathers of its step 0, the next query's
         // index list, the Q split and trade, then virtual step 1
@@ -495,7 +515,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             int jv[kEnt];
             const int t = tid_opq();
 #pragma unroll
-            for (int i = 0; i < kEnt; ++i) jv[i] = DENSE ? t + kThreads * i : s_next[t + kThreads * i];
+            for (int i = 0; i < kEnt; ++i) jv[i] = DENSE ? key_lo + t + kThreads * i : s_next[t + kThreads * i];
             post_rows(0, jv);
         }
         if (!DENSE && qn >= 0) fetch_idx(qn);     // s_next is read; refill it
@@ -520,7 +540,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 #pragma unroll
                 for (int i = 0; i < kEnt; ++i) {
                     const int e = t + kThreads * i;
-                    jv[i] = DENSE ? c0 + e : idx_row[c0 + min(e, cn - 1)];   // unconditional loads
+                    jv[i] = DENSE ? key_lo + c0 + e : idx_row[c0 + min(e, cn - 1)];   // unconditional loads
                 }
                 post_rows(c0, jv);
                 v1 = gather_v1();
@@ -570,7 +590,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 lds_barrier();       // step s + 1 everywhere; PV of step s - 1 done
                 // tail: the next query's Q, head group s + 2 - n_steps, into
                 // the free slot (without a next query, this one's again, unused)
-                const int q_src = q_next ? qn : qi;
+                const int q_src = q_next ? qn_row : qi;
                 const uint32_t q_lo = kTail ? q_lane(s + 2 - n_steps) : 0u;
                 const int e0 = (kStepBlocks * s + half) * kBlk + 16 * g;      // entry of LDS row 16g
                 const uint8_t *kstep = ring + sl * kStepBytes;
@@ -675,7 +695,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         lds_barrier();
         const float lt = s_x[hg][0][col] + s_x[hg][1][col];
         if (half == 0 && g == 0 && hv)
-            a.lse[(int64_t)qi * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+            a.lse[orow * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         // O staged through the last step's slot (the next query's step 0),
         // 32 heads x 128 dims per wave and pass; each wave reads back only its
@@ -700,7 +720,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 const int h = 32 * hg + hr;
                 const u32x4 v = *(const u32x4 *)(stage + hr * O_LD + 8 * (lane & 15));
                 if (h < H)
-                    *(u32x4 *)(a.out + ((int64_t)qi * H + h) * kV + 32 * kOwn * half + 16 * kOwn * ps +
+                    *(u32x4 *)(a.out + (orow * H + h) * kV + 32 * kOwn * half + 16 * kOwn * ps +
                                8 * (lane & 15)) = v;
             }
         }
@@ -716,7 +736,7 @@ template <bool DENSE> hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
     int dev = 0, n_cu = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    const int grid = std::min(a.batch.total_q, std::max(n_cu, 1));
+    const int grid = (int)std::min<int64_t>((int64_t)a.batch.total_q * a.n_split, std::max(n_cu, 1));
     hipLaunchKernelGGL((attn_f8_kernel<DENSE>), dim3(grid), dim3(kThreads), kLdsBytes, s, a);
     return hipGetLastError();
 }

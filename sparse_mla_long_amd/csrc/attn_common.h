@@ -96,5 +96,13 @@ __device__ __forceinline__ float xor32(float v) {
 }
 
 
+// First entry of part p when n entries are cut into S contiguous parts whose
+// sizes differ by at most one (split-KV attention: each part is one virtual
+// query of the launch). 32-bit: n * p stays below 2^27 (a sequence's rows span
+// less than 4 GiB, so n < 7.5M keys, and p <= 16).
+__device__ __forceinline__ int part_begin(int n, int S, int p) {
+    return (int)((uint32_t)n * (uint32_t)p / (uint32_t)S);
+}
+
 }  // namespace attn
 }  // namespace mla

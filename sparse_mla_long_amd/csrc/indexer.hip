@@ -77,8 +77,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
 
-    // block -> (sequence, first query); the last blocks of the grid order run first
+    // block -> (sequence, first query, key part); the last blocks of the grid
+    // order run first. With key_split > 1 (few queries), consecutive blocks
+    // take contiguous tile ranges of the same eight queries.
     int blk = a.n_blocks - 1 - (int)blockIdx.x;
+    const int kpart = blk % a.key_split;
+    blk /= a.key_split;
     int b = 0, q0 = 0, q_end = 0;
     for (; b < a.batch.num_seqs; ++b) {
         const int qa = a.batch.cu_q[b], qe = a.batch.cu_q[b + 1];
@@ -166,7 +170,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         }
     };
 
+    // this block's key tiles [t_lo, t_hi) of the 0..pmax the eight queries need
     const int n_tiles = pmax / kKeyTile + 1;
+    const int t_lo = attn::part_begin(n_tiles, a.key_split, kpart);
+    const int t_hi = attn::part_begin(n_tiles, a.key_split, kpart + 1);
+    if (t_lo >= t_hi) return;            // block-uniform
     float *srow = a.scores + (int64_t)qi * a.ld;
     f32x16 prev[MB];
     float prev_sk = 0.f;                                // FP8: scale of key prev_j0 + col
@@ -191,13 +199,13 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         if (g == 0 && j <= pos) srow[j] = sc;
     };
 #pragma unroll
-    for (int p = 0; p < kTileRing - 1; ++p) issue(p, p);
-    for (int t = 0; t < n_tiles; ++t) {
+    for (int p = 0; p < kTileRing - 1; ++p) issue(t_lo + p, p);
+    for (int t = t_lo; t < t_hi; ++t) {
         const int t0 = t * kKeyTile;
         attn::wait_vm_blocks<kVmPerTile>(kTileRing - 2);     // tile t landed (this wave's part)
         attn::lds_barrier();                                 // ... everywhere; tile t-1 done
-        issue(t + kTileRing - 1, (t + kTileRing - 1) % kTileRing);
-        const uint8_t *kt = ktile[t % kTileRing];
+        issue(t + kTileRing - 1, (t - t_lo + kTileRing - 1) % kTileRing);
+        const uint8_t *kt = ktile[(t - t_lo) % kTileRing];
         // Software pipeline over 32-key sub-tiles: the MFMAs of sub-tile u share
         // a scheduling region (closed by a scheduling barrier) with the
         // epilogue of sub-tile u-1; the scores are stored after the tile's

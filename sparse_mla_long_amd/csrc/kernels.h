@@ -25,7 +25,8 @@ struct IndexerArgs {
     int64_t ld;
     int32_t n_heads;
     int32_t head_dim;
-    int32_t n_blocks;      // sum over sequences of ceil(n_q(b) / queries per block)
+    int32_t key_split;     // workgroups per query block, each over a contiguous range of key tiles
+    int32_t n_blocks;      // key_split * sum over sequences of ceil(n_q(b) / queries per block)
     bool fp8;              // E4M3 queries and keys with scales
 };
 constexpr int kIdxQueriesPerBlock = 8;
@@ -46,12 +47,17 @@ struct AttnArgs {
     const uint8_t *kv_scale;    // fp32 scale of row r at kv_scale + r * scale_stride
     int64_t kv_stride;
     int64_t scale_stride;
-    const int32_t *indices;     // [total_q, k] or null (dense causal)
+    const int32_t *indices;     // [total_q, idx_ld], first k entries used; or null (dense causal)
     int32_t k;
+    int32_t idx_ld;             // entries between index rows
     int32_t n_heads;
     float scale_log2;           // sm_scale * log2(e)
-    __bf16 *out;                // [total_q, n_heads, 512]
-    float *lse;                 // [total_q, n_heads]
+    // Split-KV: every query's keys (list entries, or causal keys when dense)
+    // are cut into n_split contiguous parts, each run as its own virtual
+    // query; part p of query i writes output row p * total_q + i. 1: no split.
+    int32_t n_split;
+    __bf16 *out;                // [n_split * total_q, n_heads, 512]
+    float *lse;                 // [n_split * total_q, n_heads]
 };
 
 // LSE merge of attention parts over disjoint key sets

@@ -172,6 +172,40 @@ def test_attention_argument_checks(lib):
     assert attn_call(lib, mid, sstride=1024) == UNSUPPORTED       # scales: 5.1 GB >= 4 GiB
 
 
+def split_call(lib, b, n_split=2, ws=FAKE * 16, ws_bytes=None, k=8, idx=FAKE, **kw):
+    if ws_bytes is None:
+        ws_bytes = lib.mla_sparse_prefill_split_workspace_size(b.total_q, kw.get("H", 64), n_split)
+    return lib.mla_sparse_prefill_split(ctypes.byref(b), kw.get("q", FAKE), kw.get("kv", FAKE),
+                                        kw.get("sc", FAKE), kw.get("dtype", 1), 576, 4, idx, k,
+                                        kw.get("H", 64), 0.07, n_split, ws, ws_bytes,
+                                        kw.get("out", FAKE), kw.get("lse", FAKE), None)
+
+
+def test_split_attention_argument_checks(lib):
+    """mla_sparse_prefill_split: the attention checks, plus the split count and
+    the workspace, all on the host before any HIP call."""
+    b, keep = make_batch()
+    size = lib.mla_sparse_prefill_split_workspace_size
+    # 4 queries x 64 heads x 2 parts: bf16 outputs (256-byte rounded), then fp32 LSEs
+    assert size(4, 64, 2) == 2 * 4 * 64 * 1024 + 2 * 4 * 64 * 4
+    assert size(3, 8, 3) == (3 * 3 * 8 * 1024 + 255) // 256 * 256 + 3 * 3 * 8 * 4
+    assert size(4, 64, 1) == 0 and size(0, 64, 4) == 0
+    assert split_call(lib, b, n_split=-1) == INVALID
+    assert split_call(lib, b, n_split=17) == UNSUPPORTED
+    assert split_call(lib, b, n_split=9, k=8) == INVALID       # a part without a list entry
+    assert split_call(lib, b, ws=None) == INVALID
+    assert split_call(lib, b, ws=FAKE * 16 + 16) == INVALID    # not 256-byte aligned
+    assert split_call(lib, b, ws_bytes=size(4, 64, 2) - 1) == INVALID
+    assert b"workspace" in lib.mla_last_error()
+    assert split_call(lib, b, dtype=7) == INVALID              # the attention checks apply
+    assert split_call(lib, b, H=12) == UNSUPPORTED
+    assert split_call(lib, b, out=None) == INVALID
+    bad, keep2 = make_batch(total_q=3)
+    assert split_call(lib, bad) == INVALID
+    empty, keep3 = make_batch(cu_q=(0, 0), cu_kv=(0, 10))
+    assert split_call(lib, empty, ws=None, out=None, lse=None) == sm.MLA_OK
+
+
 def test_merge_argument_checks(lib):
     """mla_merge_attention validates on the host before any HIP call."""
     import ctypes

@@ -351,6 +351,141 @@ def test_full_size_sampled_rows(sm, name, kv_dtype, idx_dtype):
     torch.cuda.empty_cache()
 
 
+# ------------------------------------------------------- split-KV attention --
+def _few_queries(kv_dtype, seed, k=96):
+    """Few queries (fewer than the CUs) over long rows: ragged, with a CP-style
+    gap and rows shorter than k."""
+    wl = mla_inputs.Workload("split", (700, 1, 2500), (((0, 6), (690, 700)), ((0, 1),),
+                                                      ((0, 2), (2480, 2500))),
+                             n_heads=64, idx_heads=4, idx_dim=64, topk=k, kv_dtype=kv_dtype, seed=seed)
+    return to_gpu(mla_inputs.make_inputs(wl, "cpu"))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("n_split", [0, 2, 3, 7, 16])
+def test_split_kv_listed_keys(sm, kv_dtype, n_split):
+    """mla_sparse_prefill_split over the GPU's own index lists: every row
+    against the oracle on the same lists (parts are rounded to bf16 before the
+    merge; the attention tolerance covers it), and against the unsplit call.
+    n_split 0: the count chosen from the CU count (here CUs / 39 queries)."""
+    inp = _few_queries(kv_dtype, 40 + n_split)
+    wl = inp["workload"]
+    batch = sm.Batch.from_inputs(inp)
+    sc = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
+    idx = sm.topk_select(batch, sc, wl.topk)
+    o1, l1 = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale)
+    o2, l2 = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale,
+                               n_split=n_split)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.total_q)
+    r_out, r_lse = oracle.attention_rows(inp, rows, idx.cpu().numpy())
+    tol = TOL[kv_dtype]
+    assert_close("split%d out" % n_split, o2.float().cpu().numpy(), r_out, tol, tol)
+    assert_close("split%d lse" % n_split, l2.cpu().numpy(), r_lse, tol, tol)
+    assert_close("split%d vs unsplit" % n_split, o2.float().cpu().numpy(),
+                 o1.float().cpu().numpy(), 1e-2, 1e-2)
+    np.testing.assert_allclose(l2.cpu().numpy(), l1.cpu().numpy(), rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_split_kv_dense_with_empty_parts(sm, kv_dtype):
+    """Dense split: key ranges of 0..p_i, so rows with p_i + 1 < n_split have
+    empty parts (out 0, lse -inf before the merge); every row vs the oracle."""
+    inp = _few_queries(kv_dtype, 50)
+    wl = inp["workload"]
+    batch = sm.Batch.from_inputs(inp)
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], None, wl.sm_scale,
+                                 n_split=5)
+    torch.cuda.synchronize()
+    assert (inp["q_pos_host"] + 1 < 5).any()
+    rows = np.arange(wl.total_q)
+    r_out, r_lse = oracle.attention_rows(inp, rows, None)
+    tol = TOL[kv_dtype]
+    assert_close("dense split out", out.float().cpu().numpy(), r_out, tol, tol)
+    assert_close("dense split lse", lse.cpu().numpy(), r_lse, tol, tol)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_split_kv_long_lists_and_single_entry_parts(sm, kv_dtype):
+    """Lists longer than one 2,048-entry chunk (k = 4,500, parts of 1,500 and
+    of 2,250 keys), and n_split = k (one entry per part), against the oracle."""
+    inp = _few_queries(kv_dtype, 60)
+    wl = inp["workload"]
+    batch = sm.Batch.from_inputs(inp)
+    q_pos = inp["q_pos_host"]
+    g = np.random.default_rng(61)
+    lists = np.full((wl.total_q, 4500), -1, np.int32)
+    for i, p in enumerate(q_pos):            # every earlier key, shuffled, -1 padded
+        lists[i, : p + 1] = g.permutation(p + 1)
+    idx = torch.from_numpy(lists).cuda()
+    rows = np.arange(wl.total_q)
+    r_out, r_lse = oracle.attention_rows(inp, rows, lists)
+    tol = TOL[kv_dtype]
+    for n_split in (2, 3):
+        out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale,
+                                     n_split=n_split)
+        torch.cuda.synchronize()
+        assert_close("long split%d out" % n_split, out.float().cpu().numpy(), r_out, tol, tol)
+        assert_close("long split%d lse" % n_split, lse.cpu().numpy(), r_lse, tol, tol)
+    few = idx[:, :5].contiguous()
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], few, wl.sm_scale,
+                                 n_split=5)
+    torch.cuda.synchronize()
+    r_out, r_lse = oracle.attention_rows(inp, rows, lists[:, :5])
+    assert_close("k=n_split out", out.float().cpu().numpy(), r_out, tol, tol)
+    assert_close("k=n_split lse", lse.cpu().numpy(), r_lse, tol, tol)
+
+
+def test_split_kv_tail_of_32k(sm):
+    """The last 64 queries of the 32k workload (top-2,048 lists, FP8 KV):
+    fewer queries than CUs, the case split-KV is for. Split 4 vs unsplit on
+    every row, and sampled rows vs the oracle."""
+    wl = mla_inputs.WORKLOADS["sparse32k"]
+    tail = mla_inputs.Workload("tail64", (32768,), (((32704, 32768),),), n_heads=64, idx_heads=64,
+                               idx_dim=128, topk=2048, kv_dtype="fp8", seed=wl.seed)
+    inp = mla_inputs.make_inputs(tail, "cuda")
+    batch = sm.Batch.from_inputs(inp)
+    sc = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
+    idx = sm.topk_select(batch, sc, tail.topk)
+    o1, l1 = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, tail.sm_scale)
+    o4, l4 = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, tail.sm_scale,
+                               n_split=4)
+    torch.cuda.synchronize()
+    assert_close("tail split4 vs unsplit", o4.float().cpu().numpy(), o1.float().cpu().numpy(),
+                 1e-2, 1e-2)
+    np.testing.assert_allclose(l4.cpu().numpy(), l1.cpu().numpy(), rtol=1e-5, atol=1e-5)
+    rows = np.array([0, 17, 40, 63])
+    r_out, r_lse = oracle.attention_rows(inp, rows, idx[torch.as_tensor(rows).cuda()].cpu().numpy())
+    assert_close("tail split4 out", o4[torch.as_tensor(rows).cuda()].float().cpu().numpy(), r_out,
+                 6e-2, 6e-2)
+    assert_close("tail split4 lse", l4[torch.as_tensor(rows).cuda()].cpu().numpy(), r_lse, 6e-2, 6e-2)
+
+
+def test_resume64_key_split_indexer_and_auto_split(sm):
+    """64 new tokens behind a 32,704-token prefix: eight query blocks, so the
+    indexer splits each block's keys over many workgroups, and attention runs
+    with the automatic split. The whole path on every row, both ways round."""
+    wl = mla_inputs.WORKLOADS["resume64"]
+    inp = mla_inputs.make_inputs(wl, "cuda")
+    batch = sm.Batch.from_inputs(inp)
+    sc = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
+    idx = sm.topk_select(batch, sc, wl.topk)
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale,
+                                 n_split=0)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.total_q)
+    q_pos = inp["q_pos_host"]
+    r_scores = oracle.indexer_rows(inp, rows)
+    g_scores = [sc[int(r), : q_pos[r] + 1].cpu().numpy() for r in rows]
+    for r in rows:
+        assert_close("resume64 indexer row %d" % r, g_scores[r], r_scores[r], 1e-4, 1e-3)
+    r_idx = oracle.topk_rows(g_scores, q_pos[rows], wl.topk)
+    assert np.array_equal(r_idx, idx.cpu().numpy())
+    r_out, r_lse = oracle.attention_rows(inp, rows, idx.cpu().numpy())
+    assert_close("resume64 out", out.float().cpu().numpy(), r_out, 6e-2, 6e-2)
+    assert_close("resume64 lse", lse.cpu().numpy(), r_lse, 6e-2, 6e-2)
+
+
 # ------------------------------------------------- LSE merge and key shards --
 def test_merge_random_parts(sm):
     """mla_merge_attention against oracle.merge_lse on the same bf16 parts:
