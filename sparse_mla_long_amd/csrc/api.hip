@@ -121,7 +121,7 @@ mla_status_t indexer(const mla_batch_t *batch, const void *q_idx, const float *q
     a.head_dim = head_dim;
     // Few query blocks (a short chunk behind a long prefix): split every
     // block's keys over several workgroups, about two per CU in all, down to
-    // one 128-key tile each. Each score is still written once.
+    // one key tile each. Each score is still written once.
     int dev = 0, n_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -129,7 +129,7 @@ mla_status_t indexer(const mla_batch_t *batch, const void *q_idx, const float *q
     int64_t split = 1;
     if (blocks > 0 && blocks < 2 * (int64_t)n_cu) {
         split = (2 * (int64_t)n_cu + blocks - 1) / blocks;
-        split = std::min<int64_t>(split, ((int64_t)batch->max_kv_len + 127) / 128);
+        split = std::min<int64_t>(split, ((int64_t)batch->max_kv_len + mla::kIdxKeyTile - 1) / mla::kIdxKeyTile);
         split = std::max<int64_t>(split, 1);
     }
     a.key_split = (int32_t)split;

@@ -10,9 +10,9 @@
 // the whole sweep. In the 32x32 accumulator layout a lane owns one key column
 // and 16 head rows, so ReLU, the w-weighting and most of the head reduction
 // stay in the lane; one cross-lane add finishes it. Keys stream HBM -> LDS by
-// direct DMA through a ring of 128-key tiles shared by the eight waves, three
-// tiles ahead, 16-byte chunks XOR-swizzled by key row so the B-operand reads
-// are bank-conflict-free; one barrier per tile.
+// direct DMA through two 256-key tile slots shared by the eight waves (the
+// next tile loads while this one is used), 16-byte chunks XOR-swizzled by key
+// row so the B-operand reads are bank-conflict-free; one barrier per tile.
 //
 // FP8 variant (the same article, footnote 3: an indexer key is stored as 128
 // FP8 values plus a 4-byte scale). Queries and keys are E4M3 codes with an
@@ -20,7 +20,8 @@
 // MFMA (32x32x64) on the raw codes. Because ReLU(c x) = c ReLU(x) for c >= 0,
 // the query scale folds into w and the key scale multiplies the finished
 // score, so the scales cost no work per head. The key scales travel with the
-// key tile (one 4-byte-per-lane DMA per wave and tile).
+// key tile (one 4-byte-per-lane DMA per wave and tile; waves w and w + 4 bring
+// the same 64).
 #include "attn_common.h"
 #include "common.h"
 #include "kernels.h"
@@ -30,8 +31,8 @@ namespace {
 
 constexpr int kIdxThreads = kIdxQueriesPerBlock * kWave;  // one wave per query
 constexpr int kIdxWaves = kIdxQueriesPerBlock;
-constexpr int kKeyTile = 128;
-constexpr int kTileRing = 4;
+constexpr int kKeyTile = kIdxKeyTile;
+constexpr int kTileRing = 2;
 
 // ReLU as a signed-integer max on the bit pattern: negative values and -0
 // become +0, everything else passes unchanged. One instruction, where fmaxf
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     constexpr int kDmaPerWave = kDma / kIdxWaves;
     constexpr int kVmPerTile = kDmaPerWave + (F8 ? 1 : 0);  // + the key-scale transfer
     static_assert(kDmaPerWave >= 1 && kDma % kIdxWaves == 0, "tile split");
-    // FP8: a slot also holds the tile's 128 key scales after its key rows (in
+    // FP8: a slot also holds the tile's 256 key scales after its key rows (in
     // the same LDS object, so the compiler's own DMA tracking adds no waits)
     constexpr int kSlotBytes = kTileBytes + (F8 ? 4 * kKeyTile : 0);
     __shared__ __attribute__((aligned(16))) uint8_t ktile[kTileRing][kSlotBytes];
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     }
     const uint8_t *kbytes = (const uint8_t *)a.k_idx;
     // rows past the block's last position read that row instead (results unused);
-    // FP8: every wave also brings 64 key scales (waves of equal parity write the
+    // FP8: every wave also brings 64 key scales (waves w and w + 4 write the
     // same values to the same place)
     auto issue = [&](int t, int slot) {
 #pragma unroll
@@ -164,9 +165,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
             attn::dma16(kbytes + (kv0 + j) * RB + 16 * dma_c[u], &ktile[slot][(wv + kIdxWaves * u) * 1024]);
         }
         if constexpr (F8) {
-            const int j = min(t * kKeyTile + 64 * (wv & 1) + lane, pmax);
+            const int j = min(t * kKeyTile + 64 * (wv % (kKeyTile / 64)) + lane, pmax);
             __builtin_amdgcn_global_load_lds(a.k_scale + kv0 + j,
-                                             (attn::lds_void_ptr)&ktile[slot][kTileBytes + 256 * (wv & 1)], 4, 0, 0);
+                                             (attn::lds_void_ptr)&ktile[slot][kTileBytes + 256 * (wv % (kKeyTile / 64))], 4, 0, 0);
         }
     };
 

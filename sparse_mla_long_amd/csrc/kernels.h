@@ -30,6 +30,7 @@ struct IndexerArgs {
     bool fp8;              // E4M3 queries and keys with scales
 };
 constexpr int kIdxQueriesPerBlock = 8;
+constexpr int kIdxKeyTile = 256;          // keys per indexer LDS tile
 
 struct TopkArgs {
     BatchDev batch;
