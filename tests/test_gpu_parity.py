@@ -326,7 +326,8 @@ def test_inline_scale_row_layout(sm):
 
 # ------------------------------------------------------- full-size workloads --
 FULL = [("sparse32k", "fp8", "bf16"), ("sparse32k", "bf16", "bf16"), ("dense16k", "bf16", "bf16"),
-        ("cp131k", "fp8", "bf16"), ("ragged", "fp8", "bf16"), ("sparse32k", "fp8", "fp8")]
+        ("cp131k", "fp8", "bf16"), ("ragged", "fp8", "bf16"), ("sparse32k", "fp8", "fp8"),
+        ("ragged", "fp8", "fp8")]
 
 
 @pytest.mark.parametrize("name,kv_dtype,idx_dtype", FULL)
