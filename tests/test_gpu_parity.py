@@ -294,6 +294,25 @@ def test_topk_ties_bit_exact(sm, kind):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("k", [1, 4096])
+@pytest.mark.parametrize("kind", ["normal", "coarse"])
+def test_topk_limits_bit_exact(sm, k, kind):
+    """The largest k (4,096) and k = 1, on rows up to the longest the kernel
+    takes (524,288 keys), around the keep-all boundary and at p = 0."""
+    g = torch.Generator().manual_seed(11 + k)
+    L = 524288
+    pos = torch.tensor([0, k - 2, k - 1, k, k + 1, 100000, L - 2, L - 1], dtype=torch.int32).clamp(min=0)
+    n = len(pos)
+    s = torch.randn(n, L, generator=g) * 100
+    if kind == "coarse":
+        s = torch.round(s / 25) * 25
+    batch = sm.Batch([0, n], [0, L], pos, "cuda")
+    idx = sm.topk_select(batch, s.cuda(), k)
+    torch.cuda.synchronize()
+    ref = oracle.topk_seq(s.numpy(), pos.numpy(), k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 # ------------------------------------------------------ ragged and layout --
 def test_ragged_small_batch_all_rows(sm):
     """Empty sequence, gaps in the positions (a CP-style share), rows shorter
