@@ -172,6 +172,15 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     };
 
     // this block's key tiles [t_lo, t_hi) of the 0..pmax the eight queries need
+    // this lane's B-chunk offsets in a tile row block: row 32 s + col has the
+    // swizzle of col (32 s leaves the low bits alone), so sub-tile s only adds
+    // 32 s rows, a constant
+    uint32_t boff[F8 ? 2 * KS : KS];
+#pragma unroll
+    for (int i = 0; i < (F8 ? 2 * KS : KS); ++i) {
+        const int c = F8 ? 4 * (i >> 1) + 2 * g + (i & 1) : 2 * i + g;
+        boff[i] = (uint32_t)(col * RB + 16 * (c ^ (col & (CPR - 1))));
+    }
     const int n_tiles = pmax / kKeyTile + 1;
     const int t_lo = attn::part_begin(n_tiles, a.key_split, kpart);
     const int t_hi = attn::part_begin(n_tiles, a.key_split, kpart + 1);
@@ -219,19 +228,17 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
             f32x16 acc[MB];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
-            const int row = 32 * s + col;
-            const uint8_t *krow = kt + row * RB;
+            const uint8_t *krow = kt + 32 * s * RB;     // + this lane's chunk offset
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 if constexpr (F8) {
                     // chunks 4 ks + 2 g and the next: the dims the A operand holds
                     const int c0 = 4 * ks + 2 * g;
-                    const i32x8 bk = cat(*(const i32x4 *)(krow + 16 * (c0 ^ (row & (CPR - 1)))),
-                                         *(const i32x4 *)(krow + 16 * ((c0 + 1) ^ (row & (CPR - 1)))));
+                    const i32x8 bk = cat(*(const i32x4 *)(krow + boff[2 * ks]), *(const i32x4 *)(krow + boff[2 * ks + 1]));
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_e4m3(qf[mb][ks], bk, acc[mb]);
                 } else {
-                    const bf16x8 bk = *(const bf16x8 *)(krow + 16 * ((2 * ks + g) ^ (row & (CPR - 1))));
+                    const bf16x8 bk = *(const bf16x8 *)(krow + boff[ks]);
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(qf[mb][ks], bk, acc[mb]);
                 }
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
             sj[s] = prev_j0;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) prev[mb] = acc[mb];
-            if constexpr (F8) prev_sk = ((const float *)(kt + kTileBytes))[row];
+            if constexpr (F8) prev_sk = ((const float *)(kt + kTileBytes + 128 * s))[col];
             prev_j0 = t0 + 32 * s;
             __builtin_amdgcn_sched_barrier(0);
         }
