@@ -189,9 +189,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     f32x16 prev[MB];
     float prev_sk = 0.f;                                // FP8: scale of key prev_j0 + col
     int prev_j0 = -1;                                   // first key of the pending sub-tile
-    // score of key prev_j0 + col for this lane (lane half 0 stores it): ReLU,
-    // w and the head sum over four independent partial sums (a single chain
-    // would serialise 32 dependent FMAs), then the other lane half's rows
+    // this lane's half of the score of key prev_j0 + col (its 16 head rows):
+    // ReLU, w and the head sum over four independent partial sums (a single
+    // chain would serialise 32 dependent FMAs); bf16 adds the other half here
     auto epilogue = [&](const f32x16 *acc) -> float {
         float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -199,14 +199,27 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) ps[e & 3] += wr[mb][e] * relu(acc[mb][e]);
         float sc = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
-        sc += __uint_as_float(g ? r[0] : r[1]);
-        if constexpr (F8) sc *= prev_sk;
+        if constexpr (!F8) {     // bf16: the other lane half's rows now (lane half 0 stores)
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
+            sc += __uint_as_float(g ? r[0] : r[1]);
+        }
         return sc;
     };
     auto store = [&](float sc, int j0) {
         const int j = j0 + col;
         if (g == 0 && j <= pos) srow[j] = sc;
+    };
+    // FP8: lane-half sums of two sub-tiles, a (keys ja + col, key scale ska)
+    // and b (jb, skb): one swap gives lanes 0-31 both halves of a and lanes
+    // 32-63 both halves of b, so every lane finishes and stores one score.
+    // (The bf16 form, at higher register pressure, finishes each sub-tile in
+    // the epilogue: holding the halves spilled it.)
+    auto store_pair = [&](float a, int ja, float ska, float b, int jb, float skb) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        float sc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        if constexpr (F8) sc *= g ? skb : ska;
+        const int j0 = g ? jb : ja, j = j0 + col;
+        if (j0 >= 0 && j <= pos) srow[j] = sc;
     };
 #pragma unroll
     for (int p = 0; p < kTileRing - 1; ++p) issue(t_lo + p, p);
@@ -221,7 +234,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         // epilogue of sub-tile u-1; the scores are stored after the tile's
         // MFMAs, so no branch splits that region. Sub-tiles past this query's
         // position compute on later or repeated keys and are not stored.
-        float sc[kKeyTile / 32];
+        float sc[kKeyTile / 32], sk[kKeyTile / 32];
         int sj[kKeyTile / 32];
 #pragma unroll
         for (int s = 0; s < kKeyTile / 32; ++s) {
@@ -244,6 +257,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
                 }
             }
             sc[s] = epilogue(prev);                      // garbage before the first sub-tile: not stored
+            if constexpr (F8) sk[s] = prev_sk;
             sj[s] = prev_j0;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) prev[mb] = acc[mb];
@@ -251,12 +265,18 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
             prev_j0 = t0 + 32 * s;
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (F8) {
 #pragma unroll
-        for (int s = 0; s < kKeyTile / 32; ++s)
-            if (sj[s] >= 0) store(sc[s], sj[s]);
+            for (int s = 0; s < kKeyTile / 32; s += 2) store_pair(sc[s], sj[s], sk[s], sc[s + 1], sj[s + 1], sk[s + 1]);
+        } else {
+#pragma unroll
+            for (int s = 0; s < kKeyTile / 32; ++s)
+                if (sj[s] >= 0) store(sc[s], sj[s]);
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail DMA lands before the LDS is freed
-    store(epilogue(prev), prev_j0);
+    if constexpr (F8) store_pair(epilogue(prev), prev_j0, prev_sk, 0.f, -1, 0.f);
+    else store(epilogue(prev), prev_j0);
 }
 
 template <int DI, int MB, bool F8>
