@@ -82,3 +82,29 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_fp8_indexer_bytes_and_traffic_keys():
+    """FP8 indexer inputs: 1-byte codes plus an fp32 scale per (query, head)
+    row and per key, w as before; scores as before. The stored traffic of
+    the FP8-indexer run sits under its own key."""
+    wl = mla_inputs.WORKLOADS["sparse32k"]
+    pc = bench.pair_counts(wl)
+    b16 = bench.kernel_bytes(wl, "fp8", "bf16")["indexer"]
+    b8 = bench.kernel_bytes(wl, "fp8", "fp8")["indexer"]
+    assert b16 - b8 == wl.total_q * wl.idx_heads * (wl.idx_dim - 4) + wl.total_kv * (wl.idx_dim - 4)
+    assert b8 == pc["causal"] * 4 + wl.total_q * wl.idx_heads * (wl.idx_dim + 8) \
+        + wl.total_kv * (wl.idx_dim + 4)
+    assert bench.kernel_bytes(wl, "fp8")["attention"] == bench.kernel_bytes(wl, "fp8", "fp8")["attention"]
+    assert bench.traffic_key("sparse32k", "fp8") == "sparse32k/fp8"
+    assert bench.traffic_key("sparse32k", "fp8", "fp8") == "sparse32k/fp8/indexer-fp8"
+
+
+def test_resume64_is_a_few_query_workload():
+    """resume64: 64 new tokens at the end of one 32,768-token sequence."""
+    wl = mla_inputs.WORKLOADS["resume64"]
+    assert wl.total_q == 64 and wl.total_kv == 32768
+    assert list(wl.q_pos()) == list(range(32704, 32768))
+    pc = bench.pair_counts(wl)
+    assert pc["causal"] == sum(p + 1 for p in range(32704, 32768))
+    assert pc["selected"] == 64 * 2048
