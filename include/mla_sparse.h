@@ -195,8 +195,12 @@ mla_status_t mla_sparse_prefill(const mla_batch_t *batch, const void *q, const v
  *              parts' bf16 outputs and fp32 LSEs between the two launches
  *              (unused when the split is 1).
  * The parts' outputs are rounded to bf16 before the merge, so results differ
- * from mla_sparse_prefill by about one more bf16 rounding.
- * MLA_ERR_UNSUPPORTED also when total_q * n_split exceeds INT32_MAX. */
+ * from mla_sparse_prefill by about one more bf16 rounding. Two calls in flight
+ * on different streams must not share a workspace.
+ * Errors, besides those of mla_sparse_prefill: MLA_ERR_INVALID_ARG for
+ * n_split < 0, n_split > k with indices, or (when the split is above 1) a
+ * NULL, misaligned or too small workspace; MLA_ERR_UNSUPPORTED for
+ * n_split > 16 or total_q * n_split above INT32_MAX. Nothing is enqueued then. */
 size_t mla_sparse_prefill_split_workspace_size(int32_t total_q, int32_t n_heads, int32_t n_split);
 mla_status_t mla_sparse_prefill_split(const mla_batch_t *batch, const void *q, const void *kv,
                                       const float *kv_scale, mla_kv_dtype_t kv_dtype,
