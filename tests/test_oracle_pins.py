@@ -364,6 +364,29 @@ def test_fp8_rows_decode_with_scale():
     np.testing.assert_allclose(a[1], b[1], rtol=1e-14, atol=1e-15)
 
 
+def test_fp8_quantisation_gap_exceeds_the_fp8_tolerance():
+    """The oracle's FP8-KV output against its unquantised (bf16) KV output on
+    the same fp32 draw: the gap is input quantisation (E4M3 keeps about 2^-4
+    of each value), larger for queries that average few rows. Its maximum is
+    above the FP8 attention tolerance (6e-2), so the GPU must be, and is,
+    compared with the oracle on the same FP8 bytes: a path that read the
+    wrong KV form would fail the comparison. (A scratch draw of this shape:
+    mean 0.010, max 0.21.)"""
+    rng = np.random.default_rng(41)
+    L, H = 256, 8
+    q = bf16_bits(rng.standard_normal((L, H, 576)))
+    x = torch.from_numpy(rng.standard_normal((L, 576)).astype(np.float32))
+    codes, sigma = mla_inputs.quantize_e4m3_rows(x)
+    p = np.arange(L)
+    o8, l8 = oracle.attention_seq(q, codes.numpy(), p, SM, kv_scale=sigma.numpy(), kv_fmt=FMT_E4M3)
+    ob, lb = oracle.attention_seq(q, bf16_bits(x.numpy()), p, SM, kv_fmt=FMT_BF16)
+    gap = np.abs(o8.astype(np.float64) - ob.astype(np.float64))
+    assert 1e-3 < gap.mean() < 3e-2
+    assert gap.max() > 6e-2
+    assert gap[L // 2:].mean() < gap[:8].mean()                           # averaging shrinks it
+    assert np.abs(l8 - lb).max() < 0.25                                   # the LSE moves less
+
+
 # ----------------------------------------------------- batch-level invariants --
 def _small_batch(kv_lens, q_ranges, H=2, HI=2, DI=16, k=8, kv_dtype="bf16", seed=9):
     wl = mla_inputs.Workload("t", tuple(kv_lens), tuple(tuple(r) for r in q_ranges), n_heads=H,
