@@ -57,6 +57,11 @@ __device__ __forceinline__ void dma16_opaque(const void *base, uint32_t off, uin
                  ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
+// The asm sets M0 itself and lists it as clobbered; the compiler warns that
+// M0 is reserved. That is safe only in a kernel where no compiler-generated
+// code keeps a value in M0 across these statements: the kernels that use them
+// issue no builtin LDS DMA (the compiler's M0 user here) and index no register
+// array dynamically (which would use M0 for relative addressing).
 // 4 bytes per lane, the same way (dst + 4 * lane).
 __device__ __forceinline__ void dma4_opaque(const void *base, uint32_t off, void *dst) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)dst);
