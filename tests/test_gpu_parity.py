@@ -180,7 +180,7 @@ def test_wide_logit_range(sm, kv_dtype, listed):
     """Logits spread over hundreds of units (q scaled by 40): block maxima
     climb far above the first block's, across several chunks of the entry
     table, with the keys listed in a shuffled order."""
-    L = 2600
+    L, L2 = 6000, 3000
     wl = mla_inputs.Workload("wide", (L,), (((L - 12, L),),), n_heads=64, idx_heads=4,
                              idx_dim=64, topk=L, kv_dtype=kv_dtype, dense=not listed, seed=25)
     inp = to_gpu(mla_inputs.make_inputs(wl, "cpu"))
@@ -258,6 +258,44 @@ def test_indexer_fp8_path_all_rows(sm, idx_heads, idx_dim):
                              kv_dtype="fp8", seed=29)
     inp = to_gpu(mla_inputs.make_inputs(wl, "cpu", idx_dtype="fp8"))
     check_path(sm, inp, np.arange(wl.total_q), "fp8-indexer-%dx%d" % (idx_heads, idx_dim))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("n_queries", [24, 5000])
+def test_indexer_writes_only_causal_entries(sm, fp8, n_queries):
+    """The score buffer outside j <= q_pos[i] (later keys, and the padding up
+    to ld_scores beyond the longest sequence) keeps what the caller put there,
+    bit for bit: with few queries (the key split over many workgroups) and
+    with many (626 blocks of eight queries, no split), for both input types."""
+    L, L2 = 6000, 3000
+    na = n_queries // 2                      # the last na tokens of the first sequence,
+    nb = n_queries - na                      # the last nb of the second
+    wl = mla_inputs.Workload("causal-only", (L, L2), (((L - na, L),), ((L2 - nb, L2),)),
+                             n_heads=64, idx_heads=64, idx_dim=128, topk=96, kv_dtype="fp8", seed=70)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu", idx_dtype="fp8" if fp8 else "bf16"))
+    batch = sm.Batch.from_inputs(inp)
+    ld = L + 77
+    sentinel = torch.full((wl.total_q, ld), float("nan"), device="cuda")
+    sentinel.view(torch.int32)[:] = 0x7fc0beef
+    scores = sentinel.clone()
+    if fp8:
+        sm.indexer_score_fp8(batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"], inp["k_idx_scale"],
+                             inp["w"], scores=scores)
+    else:
+        sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"], scores=scores)
+    torch.cuda.synchronize()
+    bits = scores.view(torch.int32).cpu().numpy()
+    q_pos = inp["q_pos_host"]
+    col = np.arange(ld)[None, :]
+    written = col <= q_pos[:, None]
+    assert (bits[~written] == 0x7fc0beef).all()
+    assert not (bits[written] == 0x7fc0beef).any()
+    rows = np.array([0, wl.total_q // 2, wl.total_q - 1])
+    ref = oracle.indexer_rows(inp, rows)
+    mag = fp8_score_magnitude(inp, rows) if fp8 else None
+    for t, r in enumerate(rows):
+        atol = 1e-4 + FP8_SUM_REL * mag[t] if fp8 else 1e-4
+        assert_close("causal-only row %d" % r, scores[int(r), : q_pos[r] + 1].cpu().numpy(), ref[t], atol, 1e-3)
 
 
 # ----------------------------------------------------------------- top-k --
@@ -504,6 +542,41 @@ def test_resume64_key_split_indexer_and_auto_split(sm):
     r_out, r_lse = oracle.attention_rows(inp, rows, idx.cpu().numpy())
     assert_close("resume64 out", out.float().cpu().numpy(), r_out, 6e-2, 6e-2)
     assert_close("resume64 lse", lse.cpu().numpy(), r_lse, 6e-2, 6e-2)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dense", [False, True])
+@pytest.mark.parametrize("n_split", [None, 4])
+def test_attention_writes_stay_in_bounds(sm, kv_dtype, dense, n_split):
+    """Guard rows after out and lse, and guard bytes after the split
+    workspace, keep their sentinel: no write lands outside the buffers."""
+    inp = _few_queries(kv_dtype, 80)
+    wl = inp["workload"]
+    batch = sm.Batch.from_inputs(inp)
+    H, nq, G = wl.n_heads, wl.total_q, 5
+    idx = None
+    if not dense:
+        sc = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
+        idx = sm.topk_select(batch, sc, wl.topk)
+    out_all = torch.full((nq + G, H, 512), -7.0, dtype=torch.bfloat16, device="cuda")
+    lse_all = torch.full((nq + G, H), -7.0, dtype=torch.float32, device="cuda")
+    ws = None
+    need = 0
+    if n_split:
+        need = sm.load_library().mla_sparse_prefill_split_workspace_size(nq, H, n_split)
+        ws = torch.full((need + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale,
+                      out=out_all[:nq], lse=lse_all[:nq], n_split=n_split,
+                      workspace=ws[:need] if n_split else None)
+    torch.cuda.synchronize()
+    assert (out_all[nq:].float() == -7.0).all() and (lse_all[nq:] == -7.0).all()
+    assert not (lse_all[:nq] == -7.0).any()
+    if n_split:
+        assert (ws[need:] == 0xA5).all()
+    r_out, r_lse = oracle.attention_rows(inp, np.arange(nq), None if dense else idx.cpu().numpy())
+    tol = TOL[kv_dtype]
+    assert_close("bounds out", out_all[:nq].float().cpu().numpy(), r_out, tol, tol)
+    assert_close("bounds lse", lse_all[:nq].cpu().numpy(), r_lse, tol, tol)
 
 
 # ------------------------------------------------- LSE merge and key shards --
