@@ -602,6 +602,34 @@ def test_merge_random_parts(sm):
     assert (out[:10] == 0).all().item() and torch.isneginf(lse[:10]).all().item()
 
 
+def test_topk_and_merge_writes_stay_in_bounds(sm):
+    """Guard rows after the top-k index array and after the merge outputs keep
+    their sentinel; the written rows are the oracle's."""
+    g = torch.Generator().manual_seed(12)
+    n, L, k, G = 40, 9000, 512, 3
+    pos = torch.randint(0, L, (n,), generator=g, dtype=torch.int32)
+    pos[:4] = torch.tensor([0, k - 1, k, L - 1], dtype=torch.int32)
+    s = torch.randn(n, L, generator=g)
+    batch = sm.Batch([0, n], [0, L], pos, "cuda")
+    idx_all = torch.full((n + G, k), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    sm.topk_select(batch, s.cuda(), k, indices=idx_all[:n])
+    torch.cuda.synchronize()
+    assert (idx_all[n:] == 0x5A5A5A5A).all()
+    assert np.array_equal(idx_all[:n].cpu().numpy(), oracle.topk_seq(s.numpy(), pos.numpy(), k))
+
+    total_q, H, P = 33, 8, 3
+    o = [(torch.randn(total_q, H, 512, generator=g)).to(torch.bfloat16).cuda() for _ in range(P)]
+    l = [(torch.randn(total_q, H, generator=g) * 5).cuda() for _ in range(P)]
+    out_all = torch.full((total_q + G, H, 512), -7.0, dtype=torch.bfloat16, device="cuda")
+    lse_all = torch.full((total_q + G, H), -7.0, dtype=torch.float32, device="cuda")
+    sm.merge_attention(o, l, out=out_all[:total_q], lse=lse_all[:total_q])
+    torch.cuda.synchronize()
+    assert (out_all[total_q:].float() == -7.0).all() and (lse_all[total_q:] == -7.0).all()
+    r_out, r_lse = oracle.merge_lse([t.float().cpu().numpy() for t in o], [t.cpu().numpy() for t in l])
+    assert_close("merge bounds out", out_all[:total_q].float().cpu().numpy(), r_out, 2e-2, 1e-2)
+    assert_close("merge bounds lse", lse_all[:total_q].cpu().numpy(), r_lse, 1e-5, 1e-6)
+
+
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 def test_dcp_key_shards_merge_to_full(sm, kv_dtype):
     """DCP-style attention on one GPU: the tiny batch's KV rows dealt round-
