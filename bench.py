@@ -172,6 +172,32 @@ def measured_traffic(workload: str, kv_dtype: str, name: str, idx_dtype: str = "
 
 
 # ------------------------------------------------------------------ bench --
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def path_dtype(kv_dtype: str, idx_dtype: str, dense: bool) -> tuple:
+    """Arithmetic types of the path: (short label, description)."""
+    attn = ("e4m3 MFMA (Q and P*sigma as exact / 8-bit hi+lo E4M3 pairs: bf16 precision), "
+            "fp32 accumulate" if kv_dtype == "fp8" else "bf16 MFMA, fp32 accumulate")
+    parts = {"attention": attn}
+    kinds = {"e4m3" if kv_dtype == "fp8" else "bf16"}
+    if not dense:
+        parts["indexer"] = ("e4m3 MFMA on E4M3 codes with fp32 scales" if idx_dtype == "fp8"
+                            else "bf16 MFMA") + ", fp32 accumulate"
+        parts["topk"] = "int32 radix select on fp32 score keys"
+        kinds.add("e4m3" if idx_dtype == "fp8" else "bf16")
+    return "+".join(sorted(kinds, reverse=True)), parts
+
+
 def cpu_baseline(inp, wl, budget_s: float = 12.0, seed: int = 7) -> dict:
     """The fp64 oracle (indexer -> top-k -> attention) timed on the host cores
     on a sample of query rows, extrapolated to the whole workload by FLOP
@@ -207,9 +233,8 @@ def cpu_baseline(inp, wl, budget_s: float = 12.0, seed: int = 7) -> dict:
         n = int(min(wl.total_q, max(2 * n, n * budget_s / max(dt, 1e-3))))
     total_fl = sum(workload_flops(wl)[k] for k in ("indexer", "attention"))
     t_full = dt * total_fl / fl
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": wl.total_q / t_full, "unit": "query-tokens/s", "cores": cores,
-            "kind": "oracle",
+    return {"value": wl.total_q / t_full, "unit": "query-tokens/s",
+            "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "%d uniformly drawn query rows of the same workload (whole path in fp64: "
                       "indexer over every earlier key, top-k, attention), %.1f s wall, "
                       "extrapolated by FLOP weight" % (n, dt)}
@@ -228,6 +253,9 @@ def main():
     ap.add_argument("--indexer-dtype", default="bf16", choices=("bf16", "fp8"),
                     help="indexer queries and keys: bf16, or E4M3 codes with an fp32 scale per "
                          "row (mla_indexer_score_fp8)")
+    ap.add_argument("--scrub-steps", type=int, default=10,
+                    help="after the timed steps, this many more, each behind a 1 GiB fill that "
+                         "evicts L2 and MALL (reported as 'scrubbed'; 0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -320,22 +348,53 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    per_kernel_ms = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
-                                       for s in range(args.steps)]))
-                     for i, n in enumerate(names)}
+    def kernel_times(evs):
+        return {n: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, n in enumerate(names)}
+
+    warm = kernel_times(events)
+    # per-kernel figures: the median over the timed steps (the mean beside it)
+    per_kernel_ms = {n: float(np.median(v)) for n, v in warm.items()}
+    per_kernel_mean = {n: float(np.mean(v)) for n, v in warm.items()}
+
+    scrubbed = None
+    if args.scrub_steps > 0:
+        # 1 GiB written by a fill kernel before each step evicts L2 (4 MB per
+        # XCD) and MALL (256 MB); the events bracket the path only
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        sevents = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+                   for _ in range(args.scrub_steps)]
+        for s in range(args.scrub_steps):
+            scrub.fill_(float(s))
+            step(sevents[s])
+        torch.cuda.synchronize()
+        st = kernel_times(sevents)
+        steps_ms = [e[0].elapsed_time(e[-1]) for e in sevents]
+        scrubbed = {"steps": args.scrub_steps, "step_ms_median": float(np.median(steps_ms)),
+                    "query_tokens_per_s": wl.total_q / (float(np.median(steps_ms)) * 1e-3),
+                    "kernel_ms_median": {n: float(np.median(v)) for n, v in st.items()},
+                    "note": "each step behind a 1 GiB fill that evicts L2 and MALL; event time "
+                            "of the path only (the fill is outside the events)"}
+        del scrub
+
     fl = workload_flops(wl)
     byts = kernel_bytes(wl, kv_dtype, idx_dtype)
-    # peak of the MFMA type each contraction's operands call for: the indexer's
-    # input dtype; attention bf16 (FP8 KV: its peak enters mfma_peak_frac below)
-    peak_of = {"indexer": PEAK_TFLOPS[idx_dtype], "attention": PEAK_TFLOPS["bf16"]}
+    # peak of the MFMA type each contraction runs on: the indexer's input
+    # dtype; the attention's KV dtype (the FP8 kernel issues E4M3 MFMAs)
+    peak_of = {"indexer": PEAK_TFLOPS[idx_dtype],
+               "attention": PEAK_TFLOPS["fp8" if kv_dtype == "fp8" else "bf16"]}
     kern = {}
     for n in names:
         t = per_kernel_ms[n] * 1e-3
-        d = {"ms": per_kernel_ms[n]}
+        d = {"ms": per_kernel_ms[n], "ms_mean": per_kernel_mean[n]}
         if n in ("indexer", "attention"):
             tf = fl[n] / t / 1e12
             d.update({"tflops": tf, "bound": "mfma", "peak_tflops": peak_of[n],
                       "frac": tf / peak_of[n]})
+            if n == "attention" and kv_dtype == "fp8":
+                # each bf16-precision product is two E4M3 MFMAs (hi and lo),
+                # so the kernel's own ceiling is half the FP8 peak
+                d["bf16_equiv_peak_tflops"] = PEAK_TFLOPS["bf16"]
+                d["bf16_equiv_frac"] = tf / PEAK_TFLOPS["bf16"]
         if n in byts:
             d["algo_bytes"] = byts[n]
             d["gbs"] = byts[n] / t / 1e9
@@ -353,11 +412,17 @@ def main():
         roof = {"bound": "mfma", "kernel": dominant, "achieved": dk["tflops"],
                 "peak": dk["peak_tflops"], "unit": "TFLOP/s", "frac": dk["frac"],
                 "traffic": dk["traffic"]}
+        if "bf16_equiv_frac" in dk:
+            roof["ceiling"] = {"peak": dk["bf16_equiv_peak_tflops"], "frac": dk["bf16_equiv_frac"],
+                               "note": "peak priced at FP8 (the MFMA the kernel issues); every "
+                                       "QK and PV product is two E4M3 MFMAs (hi + lo) for bf16 "
+                                       "precision, so the kernel's ceiling is the bf16 rate"}
     else:
         roof = {"bound": "hbm", "kernel": dominant, "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": dk["frac"], "traffic": dk["traffic"]}
 
     ms_step = elapsed / args.steps * 1e3
+    dtype_label, dtype_detail = path_dtype(kv_dtype, idx_dtype, wl.dense)
     t_kernels = sum(per_kernel_ms.values()) * 1e-3
     p_attn = PEAK_TFLOPS["fp8" if kv_dtype == "fp8" else "bf16"]
     mfma_frac = (fl["indexer"] / (PEAK_TFLOPS[idx_dtype] * 1e12) +
@@ -371,7 +436,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dtype_label,
+        "dtype_detail": dtype_detail,
         "data": "synthetic",
         "config": {"workload": wl.name, "seq_lens": list(wl.kv_lens), "total_q": wl.total_q,
                    "n_heads": wl.n_heads, "indexer": "%dx%d" % (wl.idx_heads, wl.idx_dim),
@@ -387,7 +453,10 @@ def main():
         "kernels": kern,
         "kernel_sum_ms": t_kernels * 1e3,
         "roofline": roof,
+        "kernel_time_stat": "median over the timed steps (HIP events on the launch stream)",
     }
+    if scrubbed is not None:
+        res["scrubbed"] = scrubbed
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -246,25 +246,32 @@ def make_inputs(wl: Workload, device="cpu", kv_dtype: Optional[str] = None,
     return out
 
 
-def sample_rows(wl: Workload, n: int = 512, seed: int = 12345) -> np.ndarray:
-    """Query rows checked at full size: for each sequence, its first and last 4
-    queries and the queries at p in {k-2, k-1, k, k+1} (the keep-all boundary),
-    then seeded uniform picks up to n. Sorted, unique."""
+def sample_rows(wl: Workload, n: int = 512, seed: int = 12345, per_seq: int = 64) -> np.ndarray:
+    """Query rows checked at full size. Forced: the first and last 4 queries
+    of every contiguous run of positions (a context-parallel share has two
+    runs, its two chunks) and the queries at p in {k-2, k-1, k, k+1} (the
+    keep-all boundary). Then seeded uniform picks: at least min(per_seq, n_b)
+    rows of every sequence b, and up to n rows in all. Sorted, unique."""
     q_pos = wl.q_pos()
     cu = wl.cu_seqlens_q()
+    rng = np.random.default_rng(seed)
     picks = set()
     for b in range(wl.num_seqs):
         a, e = int(cu[b]), int(cu[b + 1])
         if e == a:
             continue
-        picks.update(range(a, min(a + 4, e)))
-        picks.update(range(max(a, e - 4), e))
         seg = q_pos[a:e]
+        breaks = (np.nonzero(np.diff(seg) != 1)[0] + 1).tolist()
+        for s0, s1 in zip([0] + breaks, breaks + [e - a]):
+            picks.update(range(a + s0, a + min(s0 + 4, s1)))
+            picks.update(range(a + max(s0, s1 - 4), a + s1))
         for p in (wl.topk - 2, wl.topk - 1, wl.topk, wl.topk + 1):
             hit = np.nonzero(seg == p)[0]
             if hit.size:
                 picks.add(a + int(hit[0]))
-    rng = np.random.default_rng(seed)
+        want = min(per_seq, e - a)
+        while sum(1 for r in picks if a <= r < e) < want:
+            picks.add(int(rng.integers(a, e)))
     total = wl.total_q
     while len(picks) < min(n, total):
         picks.add(int(rng.integers(0, total)))

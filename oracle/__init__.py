@@ -51,6 +51,8 @@ def lib():
             build(force=False)
             L = ctypes.CDLL(_LIB_PATH)
             P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+            L.oracle_num_threads.argtypes = []
+            L.oracle_num_threads.restype = ctypes.c_int
             L.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
             L.oracle_bf16_decode.restype = D
             L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
@@ -90,6 +92,11 @@ def as_numpy(x) -> Optional[np.ndarray]:
 
 def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops run on."""
+    return int(lib().oracle_num_threads())
 
 
 def bf16_decode(h: int) -> float:

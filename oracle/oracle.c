@@ -36,6 +36,7 @@
  * (-1)^s 2^(e-7) (1 + m/8); e = 15 and m = 7 is NaN; no infinities.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -44,6 +45,9 @@
 #define V_DIM 512
 
 enum { FMT_BF16 = 0, FMT_E4M3 = 1, FMT_F64 = 2 };
+
+/* Threads an OpenMP loop of the oracle uses (OMP_NUM_THREADS, else the cores). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 double oracle_bf16_decode(uint16_t h) {
     uint32_t u = (uint32_t)h << 16;

@@ -5,9 +5,11 @@ Staged so errors do not compound (the comparison procedure of the method):
     exact bf16 products); bit-exact on small-integer inputs; FP8 indexer
     inputs add 2^-14 of the sum of absolute terms (the E4M3 MFMA's summation);
   * top-k bit-exact: the oracle's selection run on the GPU's own score rows;
-  * attention on the GPU's own index lists, |g - r| <= atol + rtol |r| with
-    atol = rtol = 2e-2 for bf16 KV and 6e-2 for FP8 KV (out and LSE);
-  * the set overlap when each side uses its own scores is reported, not gated.
+  * attention on the GPU's own index lists: out within |g - r| <= tol + tol |r|
+    (tol = 2e-2 for bf16 KV, 6e-2 for FP8 KV), LSE within 1e-3 + 1e-4 |r|
+    (fp32 arithmetic; a query missing one 32-key block of 2,048 fails it);
+  * the set overlap when each side uses its own scores is reported, and at
+    full size gated (mean and worst row).
 The tiny workload is checked on every row; the full-size workloads run the
 whole path in the launch configuration the benchmark times and are checked
 on sampled rows.
@@ -22,10 +24,13 @@ import torch
 
 import mla_inputs
 import oracle
+import tolerances as tl
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "fp8": 6e-2}
+TOL = tl.OUT_TOL
+LSE_ATOL, LSE_RTOL = tl.LSE_ATOL, tl.LSE_RTOL
+assert_close = tl.assert_close
 
 
 @pytest.fixture(scope="module")
@@ -39,22 +44,6 @@ def sm():
 
 def say(*a):
     print(*a, flush=True)
-
-
-def assert_close(name, got, ref, atol, rtol):
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    assert got.shape == ref.shape, (name, got.shape, ref.shape)
-    both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
-    with np.errstate(invalid="ignore"):          # inf - inf where both are the same infinity
-        err = np.abs(got - ref)
-    bad = ~(both_inf | (err <= atol + rtol * np.abs(ref)))
-    if bad.any():
-        i = np.argwhere(bad)[0]
-        raise AssertionError("%s: %d / %d outside tolerance (atol=%g rtol=%g); first at %s: "
-                             "got %r ref %r; max err %g" % (name, bad.sum(), bad.size, atol, rtol,
-                                                            tuple(i), got[tuple(i)],
-                                                            ref[tuple(i)], np.nanmax(err)))
 
 
 def to_gpu(inp):
@@ -95,7 +84,15 @@ def run_path(sm, batch, inp):
     return out, lse, idx, scores
 
 
-def check_path(sm, inp, rows, label, check_indexer=True):
+# End-to-end selection overlap |S_oracle & S_gpu| / |S_oracle| when each side
+# picks from its own scores (mean over rows, worst row). Near-ties between the
+# fp64 scores and the GPU's fp32 (bf16 inputs) or E4M3-MFMA (FP8 inputs) sums
+# can swap members at the k-th place, so this is a gate on the rate of such
+# swaps, not a bit-exact check (top-k itself is bit-exact on equal scores).
+OVERLAP_GATE = {"bf16": (0.999, 0.98), "fp8": (0.99, 0.9)}
+
+
+def check_path(sm, inp, rows, label, check_indexer=True, gate_overlap=False):
     """Run indexer -> top-k -> attention on the GPU for the whole batch and
     check the given rows against the oracle, stage by stage."""
     wl = inp["workload"]
@@ -125,9 +122,16 @@ def check_path(sm, inp, rows, label, check_indexer=True):
     assert len(mism) == 0, "%s top-k differs on rows %s" % (label, rows[mism][:8])
     say("[%s] oracle attention on the GPU's index lists" % label)
     r_out, r_lse = oracle.attention_rows(inp, rows, g_idx)
-    tol = TOL[inp["kv_dtype"]]
-    assert_close("%s out" % label, out[rt].float().cpu().numpy(), r_out, tol, tol)
-    assert_close("%s lse" % label, lse[rt].cpu().numpy(), r_lse, tol, tol)
+    tl.assert_attention(label, inp["kv_dtype"], out[rt].float().cpu().numpy(),
+                        lse[rt].cpu().numpy(), r_out, r_lse, say)
+    if check_indexer:
+        own = oracle.topk_rows(r_scores, q_pos[rows], wl.topk)
+        ov = tl.set_overlap(own, g_idx)
+        say("[%s] end-to-end top-k set overlap (own scores each side): mean %.5f, worst row "
+            "%.4f, over %d rows" % (label, ov.mean(), ov.min(), len(rows)))
+        if gate_overlap:
+            mean_min, row_min = OVERLAP_GATE[inp.get("idx_dtype", "bf16")]
+            assert ov.mean() >= mean_min and ov.min() >= row_min, (label, ov.mean(), ov.min())
     return scores, idx, out, lse
 
 
@@ -146,18 +150,34 @@ def test_tiny_all_rows(sm, kv_dtype):
     assert ov > 0.99
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("n_heads", [8, 16, 32, 64])
-def test_dense_attention_small(sm, n_heads):
+def test_dense_attention_small(sm, n_heads, kv_dtype):
     wl = mla_inputs.Workload("dense-small", (300, 77), (((0, 300),), ((0, 77),)), n_heads=n_heads,
-                             idx_heads=4, idx_dim=64, topk=512, kv_dtype="bf16", dense=True, seed=21)
+                             idx_heads=4, idx_dim=64, topk=512, kv_dtype=kv_dtype, dense=True, seed=21)
     inp = to_gpu(mla_inputs.make_inputs(wl, "cpu"))
     batch = sm.Batch.from_inputs(inp)
-    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], None, None, wl.sm_scale)
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], None, wl.sm_scale)
     torch.cuda.synchronize()
     rows = np.arange(wl.total_q)
     r_out, r_lse = oracle.attention_rows(inp, rows, None)
-    assert_close("dense out", out.float().cpu().numpy(), r_out, 2e-2, 2e-2)
-    assert_close("dense lse", lse.cpu().numpy(), r_lse, 2e-2, 2e-2)
+    tl.assert_attention("dense-H%d-%s" % (n_heads, kv_dtype), kv_dtype, out.float().cpu().numpy(),
+                        lse.cpu().numpy(), r_out, r_lse, say)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("n_heads", [8, 16, 32])
+def test_sparse_path_head_counts(sm, n_heads, kv_dtype):
+    """The whole path at the head counts below 64 the attention supports,
+    every row: a ragged batch with an empty sequence, a CP-style gap, a
+    one-token sequence and rows shorter than k (heads past n_heads in a
+    32-head group are masked off in the kernels)."""
+    wl = mla_inputs.Workload("heads", (300, 0, 1000, 1, 130),
+                             (((0, 300),), (), ((0, 70), (930, 1000)), ((0, 1),), ((64, 130),)),
+                             n_heads=n_heads, idx_heads=16, idx_dim=64, topk=96,
+                             kv_dtype=kv_dtype, seed=90 + n_heads)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu"))
+    check_path(sm, inp, np.arange(wl.total_q), "heads-H%d-%s" % (n_heads, kv_dtype))
 
 
 def test_dense_equals_sparse_with_full_lists(sm):
@@ -197,7 +217,7 @@ def test_wide_logit_range(sm, kv_dtype, listed):
     r_out, r_lse = oracle.attention_rows(inp, rows, None if idx is None else idx.cpu().numpy())
     tol = TOL[kv_dtype]
     assert_close("wide out", out.float().cpu().numpy(), r_out, tol, tol)
-    assert_close("wide lse", lse.cpu().numpy(), r_lse, tol, tol)
+    assert_close("wide lse", lse.cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
 
 
 # --------------------------------------------------------------- indexer --
@@ -390,7 +410,7 @@ FULL = [("sparse32k", "fp8", "bf16"), ("sparse32k", "bf16", "bf16"), ("dense16k"
 @pytest.mark.parametrize("name,kv_dtype,idx_dtype", FULL)
 def test_full_size_sampled_rows(sm, name, kv_dtype, idx_dtype):
     wl = mla_inputs.WORKLOADS[name]
-    n_rows = int(os.environ.get("MLA_PARITY_ROWS", "48"))
+    n_rows = int(os.environ.get("MLA_PARITY_ROWS", "512"))
     rows = mla_inputs.sample_rows(wl, n_rows)
     say("[%s/%s/indexer %s] generating inputs on the GPU" % (name, kv_dtype, idx_dtype))
     inp = mla_inputs.make_inputs(wl, "cuda", kv_dtype=kv_dtype, idx_dtype=idx_dtype)
@@ -401,10 +421,10 @@ def test_full_size_sampled_rows(sm, name, kv_dtype, idx_dtype):
         say("[%s] oracle dense attention on %d rows" % (name, len(rows)))
         r_out, r_lse = oracle.attention_rows(inp, rows, None)
         rt = torch.as_tensor(rows, device="cuda")
-        assert_close("dense16k out", out[rt].float().cpu().numpy(), r_out, 2e-2, 2e-2)
-        assert_close("dense16k lse", lse[rt].cpu().numpy(), r_lse, 2e-2, 2e-2)
+        tl.assert_attention("dense16k", "bf16", out[rt].float().cpu().numpy(),
+                            lse[rt].cpu().numpy(), r_out, r_lse, say)
     else:
-        check_path(sm, inp, rows, "%s-%s-idx%s" % (name, kv_dtype, idx_dtype))
+        check_path(sm, inp, rows, "%s-%s-idx%s" % (name, kv_dtype, idx_dtype), gate_overlap=True)
     del inp
     torch.cuda.empty_cache()
 
@@ -439,7 +459,7 @@ def test_split_kv_listed_keys(sm, kv_dtype, n_split):
     r_out, r_lse = oracle.attention_rows(inp, rows, idx.cpu().numpy())
     tol = TOL[kv_dtype]
     assert_close("split%d out" % n_split, o2.float().cpu().numpy(), r_out, tol, tol)
-    assert_close("split%d lse" % n_split, l2.cpu().numpy(), r_lse, tol, tol)
+    assert_close("split%d lse" % n_split, l2.cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
     assert_close("split%d vs unsplit" % n_split, o2.float().cpu().numpy(),
                  o1.float().cpu().numpy(), 1e-2, 1e-2)
     np.testing.assert_allclose(l2.cpu().numpy(), l1.cpu().numpy(), rtol=1e-5, atol=1e-5)
@@ -460,7 +480,7 @@ def test_split_kv_dense_with_empty_parts(sm, kv_dtype):
     r_out, r_lse = oracle.attention_rows(inp, rows, None)
     tol = TOL[kv_dtype]
     assert_close("dense split out", out.float().cpu().numpy(), r_out, tol, tol)
-    assert_close("dense split lse", lse.cpu().numpy(), r_lse, tol, tol)
+    assert_close("dense split lse", lse.cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
@@ -484,14 +504,14 @@ def test_split_kv_long_lists_and_single_entry_parts(sm, kv_dtype):
                                      n_split=n_split)
         torch.cuda.synchronize()
         assert_close("long split%d out" % n_split, out.float().cpu().numpy(), r_out, tol, tol)
-        assert_close("long split%d lse" % n_split, lse.cpu().numpy(), r_lse, tol, tol)
+        assert_close("long split%d lse" % n_split, lse.cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
     few = idx[:, :5].contiguous()
     out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], few, wl.sm_scale,
                                  n_split=5)
     torch.cuda.synchronize()
     r_out, r_lse = oracle.attention_rows(inp, rows, lists[:, :5])
     assert_close("k=n_split out", out.float().cpu().numpy(), r_out, tol, tol)
-    assert_close("k=n_split lse", lse.cpu().numpy(), r_lse, tol, tol)
+    assert_close("k=n_split lse", lse.cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
 
 
 def test_split_kv_tail_of_32k(sm):
@@ -516,7 +536,7 @@ def test_split_kv_tail_of_32k(sm):
     r_out, r_lse = oracle.attention_rows(inp, rows, idx[torch.as_tensor(rows).cuda()].cpu().numpy())
     assert_close("tail split4 out", o4[torch.as_tensor(rows).cuda()].float().cpu().numpy(), r_out,
                  6e-2, 6e-2)
-    assert_close("tail split4 lse", l4[torch.as_tensor(rows).cuda()].cpu().numpy(), r_lse, 6e-2, 6e-2)
+    assert_close("tail split4 lse", l4[torch.as_tensor(rows).cuda()].cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
 
 
 def test_resume64_key_split_indexer_and_auto_split(sm):
@@ -541,7 +561,7 @@ def test_resume64_key_split_indexer_and_auto_split(sm):
     assert np.array_equal(r_idx, idx.cpu().numpy())
     r_out, r_lse = oracle.attention_rows(inp, rows, idx.cpu().numpy())
     assert_close("resume64 out", out.float().cpu().numpy(), r_out, 6e-2, 6e-2)
-    assert_close("resume64 lse", lse.cpu().numpy(), r_lse, 6e-2, 6e-2)
+    assert_close("resume64 lse", lse.cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
@@ -576,7 +596,7 @@ def test_attention_writes_stay_in_bounds(sm, kv_dtype, dense, n_split):
     r_out, r_lse = oracle.attention_rows(inp, np.arange(nq), None if dense else idx.cpu().numpy())
     tol = TOL[kv_dtype]
     assert_close("bounds out", out_all[:nq].float().cpu().numpy(), r_out, tol, tol)
-    assert_close("bounds lse", lse_all[:nq].cpu().numpy(), r_lse, tol, tol)
+    assert_close("bounds lse", lse_all[:nq].cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
 
 
 # ------------------------------------------------- LSE merge and key shards --
@@ -665,9 +685,9 @@ def test_dcp_key_shards_merge_to_full(sm, kv_dtype):
     torch.cuda.synchronize()
     tol = TOL[kv_dtype]
     assert_close("dcp out vs unsharded", m_o.float().cpu().numpy(), full_o.float().cpu().numpy(), 2e-2, 2e-2)
-    assert_close("dcp lse vs unsharded", m_l.cpu().numpy(), full_l.cpu().numpy(), 1e-3, 1e-3)
+    assert_close("dcp lse vs unsharded", m_l.cpu().numpy(), full_l.cpu().numpy(), LSE_ATOL, LSE_RTOL)
     rows = np.arange(0, wl.total_q, 7)
     r_out, r_lse = oracle.attention_rows(inp, rows, idx_h[rows])
     rt = torch.as_tensor(rows, device="cuda")
     assert_close("dcp out vs oracle", m_o[rt].float().cpu().numpy(), r_out, tol, tol)
-    assert_close("dcp lse vs oracle", m_l[rt].cpu().numpy(), r_lse, tol, tol)
+    assert_close("dcp lse vs oracle", m_l[rt].cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)

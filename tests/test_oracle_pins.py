@@ -387,6 +387,43 @@ def test_fp8_quantisation_gap_exceeds_the_fp8_tolerance():
     assert np.abs(l8 - lb).max() < 0.25                                   # the LSE moves less
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_attention_gates_reject_a_dropped_key_block(kv_dtype):
+    """The attention parity gates catch a kernel that skips keys: 16 queries x
+    64 heads near position 4,095 attend to 2,048 random earlier keys; the same
+    attention with one 32-key block of each list left out (entries 1,024 ..
+    1,055) misses the LSE gate on most (query, head) pairs. Its output moves
+    far less, so the O gate alone would catch it only now and then."""
+    import tolerances as tl
+    rng = np.random.default_rng(77)
+    L, H, n, k = 4096, 64, 16, 2048
+    q = bf16_bits(rng.standard_normal((n, H, 576)))
+    x = rng.standard_normal((L, 576)).astype(np.float32)
+    if kv_dtype == "fp8":
+        codes, sigma = mla_inputs.quantize_e4m3_rows(torch.from_numpy(x))
+        kv, kv_scale, fmt = codes.numpy(), sigma.numpy(), FMT_E4M3
+    else:
+        kv, kv_scale, fmt = bf16_bits(x), None, FMT_BF16
+    p = np.arange(L - n, L)
+    idx = np.stack([np.sort(rng.choice(pi + 1, k, replace=False)) for pi in p]).astype(np.int32)
+    dropped = idx.copy()
+    dropped[:, 1024:1056] = -1
+    o, l = oracle.attention_seq(q, kv, p, SM, kv_scale=kv_scale, indices=idx, kv_fmt=fmt)
+    od, ld = oracle.attention_seq(q, kv, p, SM, kv_scale=kv_scale, indices=dropped, kv_fmt=fmt)
+    lse_bad = tl.outside(ld, l, tl.LSE_ATOL, tl.LSE_RTOL)
+    tol = tl.OUT_TOL[kv_dtype]
+    out_bad = tl.outside(od, o, tol, tol)
+    shift = np.abs(ld - l)
+    assert 0.01 < shift.mean() < 0.03                     # about 32/2048 of the mass
+    assert lse_bad.mean() > 0.6, lse_bad.mean()
+    assert out_bad.mean() < 0.1                           # the O gate alone is much weaker
+    # the undropped lists pass both gates against themselves rounded like
+    # the kernel's outputs (bf16 O, fp32 LSE)
+    o_b = torch.from_numpy(o).to(torch.bfloat16).double().numpy()
+    assert not tl.outside(o_b, o, tol, tol).any()
+    assert not tl.outside(l.astype(np.float32), l, tl.LSE_ATOL, tl.LSE_RTOL).any()
+
+
 # ----------------------------------------------------- batch-level invariants --
 def _small_batch(kv_lens, q_ranges, H=2, HI=2, DI=16, k=8, kv_dtype="bf16", seed=9):
     wl = mla_inputs.Workload("t", tuple(kv_lens), tuple(tuple(r) for r in q_ranges), n_heads=H,

@@ -1,0 +1,79 @@
+"""The comparison gates of the parity tests, in one place.
+
+The GPU parity tests and the CPU pins that show these gates would catch a
+wrong kernel (tests/test_oracle_pins.py) use the same constants and the same
+element test, so a gate cannot be loosened in one place only.
+
+* Attention outputs O: |g - r| <= tol + tol |r| with tol = 2e-2 for bf16 KV
+  and 6e-2 for FP8 KV (the bf16-output and FP8-KV tolerances of the method's
+  parity requirements).
+* Attention LSE: |g - r| <= 1e-3 + 1e-4 |r|, for both KV types. The LSE is
+  fp32 arithmetic on fp32 logits: the logit error of the MFMA path is at most
+  about 3e-4 (2^-16.4 of the sum of |terms| of a 576-dim dot product times
+  sm_scale, the bound measured for the FP8 matrix unit's accumulation), the
+  row sum is fp32, and the log is fp32. The bound keeps a 10x margin over
+  that and still rejects a query that loses one 32-key block of a
+  2,048-key list (which moves its LSE by about 0.016 on average).
+* Indexer scores: |g - r| <= 1e-3 |r| + 1e-4 (fp32 sums of exact products).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+OUT_TOL = {"bf16": 2e-2, "fp8": 6e-2}
+LSE_ATOL, LSE_RTOL = 1e-3, 1e-4
+IDX_ATOL, IDX_RTOL = 1e-4, 1e-3
+
+
+def outside(got, ref, atol, rtol) -> np.ndarray:
+    """Boolean mask of the elements of got that miss ref by more than
+    atol + rtol |ref| (equal infinities match)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
+    with np.errstate(invalid="ignore"):          # inf - inf where both are the same infinity
+        err = np.abs(got - ref)
+    return ~(both_inf | (err <= atol + rtol * np.abs(ref)))
+
+
+def assert_close(name, got, ref, atol, rtol):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bad = outside(got, ref, atol, rtol)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        with np.errstate(invalid="ignore"):
+            err = np.abs(got - ref)
+        raise AssertionError("%s: %d / %d outside tolerance (atol=%g rtol=%g); first at %s: "
+                             "got %r ref %r; max err %g" % (name, bad.sum(), bad.size, atol, rtol,
+                                                            tuple(i), got[tuple(i)],
+                                                            ref[tuple(i)], np.nanmax(err)))
+
+
+def max_err(got, ref) -> float:
+    """Largest |got - ref| over elements where both are finite."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    fin = np.isfinite(got) & np.isfinite(ref)
+    return float(np.abs(got[fin] - ref[fin]).max()) if fin.any() else 0.0
+
+
+def assert_attention(name, kv_dtype, out, lse, r_out, r_lse, say=None):
+    """O at the KV type's output tolerance, LSE at the fp32 bound."""
+    tol = OUT_TOL[kv_dtype]
+    assert_close(name + " out", out, r_out, tol, tol)
+    assert_close(name + " lse", lse, r_lse, LSE_ATOL, LSE_RTOL)
+    if say is not None:
+        say("[%s] max |out err| %.3g, max |lse err| %.3g" % (name, max_err(out, r_out),
+                                                            max_err(lse, r_lse)))
+
+
+def set_overlap(a_rows, b_rows) -> np.ndarray:
+    """Per row |A & B| / |A| of two index lists (-1 entries ignored)."""
+    res = []
+    for a, b in zip(a_rows, b_rows):
+        sa = set(int(x) for x in a if x >= 0)
+        sb = set(int(x) for x in b if x >= 0)
+        res.append(len(sa & sb) / max(len(sa), 1))
+    return np.asarray(res)
