@@ -38,9 +38,11 @@
  * Conventions shared by every call:
  *  - Pointers marked "device" must point to GPU memory of the current HIP
  *    device; "host" pointers to CPU memory read during the call only.
- *  - The caller owns every buffer. The library allocates no memory, keeps no
- *    pointer after a call returns, holds no mutable global state and is safe
- *    to call from several host threads.
+ *  - The caller owns every buffer. The library allocates no memory and keeps
+ *    no pointer after a call returns. Its only global state is the scratch
+ *    array of mla_sparse_prefill_split_noalloc (one per GPU, with its device
+ *    address taken once per device under a lock); every other call is safe
+ *    from several host threads.
  *  - Calls validate their arguments on the host, enqueue kernels on `stream`
  *    (a hipStream_t; NULL means the null stream) and return without waiting.
  *    Outputs are valid once the stream has reached that point; inputs must
@@ -208,6 +210,33 @@ mla_status_t mla_sparse_prefill_split(const mla_batch_t *batch, const void *q, c
                                       const int32_t *indices, int32_t k, int32_t n_heads,
                                       float sm_scale, int32_t n_split, void *workspace,
                                       size_t workspace_bytes, void *out, float *lse, void *stream);
+
+/* Bytes of the library's own scratch array behind
+ * mla_sparse_prefill_split_noalloc: the parts of up to 256 virtual queries
+ * (query x part) of 64 heads, i.e. every automatic split (n_split = 0 gives
+ * total_q * n_split <= 256 on a 256-CU GPU). 16 MiB + 64 KiB per GPU. */
+#define MLA_SPLIT_SCRATCH_BYTES (16u * 1024u * 1024u + 64u * 1024u)
+
+/* mla_sparse_prefill_split without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The parts' outputs and LSEs live in
+ * a device array the library owns (MLA_SPLIT_SCRATCH_BYTES on every GPU it
+ * runs on, held until the process ends; its address is looked up once per
+ * device, on the first call with that device current). The call allocates
+ * nothing and calls no allocating routine. Arguments, results and errors as
+ * mla_sparse_prefill_split, plus MLA_ERR_UNSUPPORTED (nothing enqueued) when
+ * mla_sparse_prefill_split_workspace_size(total_q, n_heads, n_split) exceeds
+ * MLA_SPLIT_SCRATCH_BYTES. Nothing in the array needs to start at zero (every
+ * part's rows are written before the merge reads them). All calls on one GPU
+ * share its array and it keeps the last call's contents: calls whose work
+ * overlaps on one GPU (other streams, other host threads) race on it and must
+ * be serialised by the caller. */
+mla_status_t mla_sparse_prefill_split_noalloc(const mla_batch_t *batch, const void *q,
+                                              const void *kv, const float *kv_scale,
+                                              mla_kv_dtype_t kv_dtype, int64_t kv_row_stride,
+                                              int64_t kv_scale_stride, const int32_t *indices,
+                                              int32_t k, int32_t n_heads, float sm_scale,
+                                              int32_t n_split, void *out, float *lse, void *stream);
 
 /* Merge of attention results over disjoint key sets by their log-sum-exp
  * (spke.com article, section "DCP": every GPU attends over its share of the

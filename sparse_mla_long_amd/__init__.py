@@ -12,7 +12,8 @@ Calls (same names as the C ABI, without the ``mla_`` prefix):
                                                -> scores from E4M3 codes with scales
   topk_select(batch, scores, k, ...)           -> indices [total_q, k] int32
   sparse_prefill(batch, q, kv, ...)            -> (out [total_q, H, 512] bf16, lse [total_q, H] fp32)
-      (n_split=S: the split-KV call, mla_sparse_prefill_split)
+      (n_split=S: the split-KV call, mla_sparse_prefill_split; with
+      noalloc=True, mla_sparse_prefill_split_noalloc)
 """
 from __future__ import annotations
 
@@ -41,6 +42,7 @@ class MlaBatch(ctypes.Structure):
 
 EXPORTS = ("mla_indexer_score", "mla_indexer_score_fp8", "mla_topk_select", "mla_sparse_prefill",
            "mla_sparse_prefill_split", "mla_sparse_prefill_split_workspace_size",
+           "mla_sparse_prefill_split_noalloc",
            "mla_merge_attention", "mla_status_string", "mla_last_error", "mla_abi_version")
 
 _lib = None
@@ -63,12 +65,14 @@ def load_library(path: str = LIB_PATH):
                                      ctypes.c_float, P, P, P]
     L.mla_sparse_prefill_split.argtypes = [BP, P, P, P, ctypes.c_int, I64, I64, P, I32, I32,
                                            ctypes.c_float, I32, P, ctypes.c_size_t, P, P, P]
+    L.mla_sparse_prefill_split_noalloc.argtypes = [BP, P, P, P, ctypes.c_int, I64, I64, P, I32,
+                                                   I32, ctypes.c_float, I32, P, P, P]
     L.mla_sparse_prefill_split_workspace_size.argtypes = [I32, I32, I32]
     L.mla_sparse_prefill_split_workspace_size.restype = ctypes.c_size_t
     L.mla_merge_attention.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                       I32, I32, I32, P, P, P]
     for f in ("mla_indexer_score", "mla_indexer_score_fp8", "mla_topk_select", "mla_sparse_prefill",
-              "mla_sparse_prefill_split", "mla_merge_attention"):
+              "mla_sparse_prefill_split", "mla_sparse_prefill_split_noalloc", "mla_merge_attention"):
         getattr(L, f).restype = ctypes.c_int
     L.mla_status_string.argtypes = [ctypes.c_int]
     L.mla_status_string.restype = ctypes.c_char_p
@@ -215,13 +219,16 @@ def sparse_prefill(batch: Batch, q: torch.Tensor, kv: torch.Tensor,
                    indices: Optional[torch.Tensor] = None, sm_scale: float = 192 ** -0.5,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    kv_row_stride: Optional[int] = None, kv_scale_stride: int = 4,
-                   n_split: Optional[int] = None, workspace: Optional[torch.Tensor] = None):
+                   n_split: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                   noalloc: bool = False):
     """mla_sparse_prefill. kv is [total_kv, 576] bf16, or uint8 E4M3 codes with
     kv_scale [total_kv] fp32 (or a strided view given by the byte strides).
     indices [total_q, k] int32 or None for dense causal attention.
     n_split (1..16): mla_sparse_prefill_split, every query's keys in n_split
     parts merged by their LSE; workspace (uint8, device) is allocated here
-    when not given. Returns (out [total_q, H, 512] bf16, lse [total_q, H] fp32)."""
+    when not given. noalloc (with n_split): mla_sparse_prefill_split_noalloc,
+    the parts in the library's own scratch array (no workspace).
+    Returns (out [total_q, H, 512] bf16, lse [total_q, H] fp32)."""
     dev = batch.device
     H = q.shape[1]
     _need(q, "q", torch.bfloat16, dev, (batch.total_q, H, QK_DIM))
@@ -260,6 +267,12 @@ def sparse_prefill(batch: Batch, q: torch.Tensor, kv: torch.Tensor,
             _ptr(indices), int(k), H, float(sm_scale), _ptr(out), _ptr(lse), _stream(q)))
         return out, lse
     L = load_library()
+    if noalloc:
+        _check(L.mla_sparse_prefill_split_noalloc(
+            batch.c, _ptr(q), _ptr(kv), scale, dtype, int(kv_row_stride), int(kv_scale_stride),
+            _ptr(indices), int(k), H, float(sm_scale), int(n_split), _ptr(out), _ptr(lse),
+            _stream(q)))
+        return out, lse
     need = L.mla_sparse_prefill_split_workspace_size(batch.total_q, H, int(n_split))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)

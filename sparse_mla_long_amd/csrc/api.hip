@@ -5,6 +5,7 @@
 // trusted; kernels clamp positions into their sequence so a bad q_pos cannot
 // read outside the sequence's rows.
 #include <algorithm>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string>
@@ -72,6 +73,37 @@ mla_status_t check_batch(const mla_batch_t *b, mla::BatchDev *dev) {
 mla_status_t hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return ok();
     return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Library-owned workspace of mla_sparse_prefill_split_noalloc (the parts'
+// outputs and LSEs between its two launches). Every GPU the library runs on
+// holds its own copy until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: host code uses only the device
+// address taken once per device with hipGetSymbolAddress below.
+static __device__ __align__(256) uint8_t scratch[MLA_SPLIT_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};   // device address of `scratch` per device, once taken
+
+// Device address of the current device's `scratch`, looked up on the first
+// call on that device (with it current) and kept.
+mla_status_t scratch_of_current_device(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MLA_ERR_UNSUPPORTED, "device %d: the scratch table holds %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = g_scratch_dev[dev];
+    return MLA_OK;
 }
 
 }  // namespace
@@ -278,12 +310,15 @@ size_t mla_sparse_prefill_split_workspace_size(int32_t total_q, int32_t n_heads,
     return split_o_bytes(total_q, n_heads, n_split) + (size_t)n_split * total_q * n_heads * 4;
 }
 
-mla_status_t mla_sparse_prefill_split(const mla_batch_t *batch, const void *q, const void *kv,
-                                      const float *kv_scale, mla_kv_dtype_t kv_dtype,
-                                      int64_t kv_row_stride, int64_t kv_scale_stride,
-                                      const int32_t *indices, int32_t k, int32_t n_heads,
-                                      float sm_scale, int32_t n_split, void *workspace,
-                                      size_t workspace_bytes, void *out, float *lse, void *stream) {
+namespace {
+// The split-KV call with the caller's workspace, or (library_scratch) with
+// the current device's `scratch` array.
+mla_status_t split_impl(const mla_batch_t *batch, const void *q, const void *kv,
+                        const float *kv_scale, mla_kv_dtype_t kv_dtype, int64_t kv_row_stride,
+                        int64_t kv_scale_stride, const int32_t *indices, int32_t k,
+                        int32_t n_heads, float sm_scale, int32_t n_split, void *workspace,
+                        size_t workspace_bytes, bool library_scratch, void *out, float *lse,
+                        void *stream) {
     if (n_split < 0) return fail(MLA_ERR_INVALID_ARG, "n_split must be >= 0 (got %d)", n_split);
     if (n_split == 0 && batch && batch->total_q > 0) n_split = auto_split(batch->total_q, indices ? k : 0);
     if (n_split == 0) n_split = 1;
@@ -307,6 +342,16 @@ mla_status_t mla_sparse_prefill_split(const mla_batch_t *batch, const void *q, c
         return fail(MLA_ERR_UNSUPPORTED, "total_q * n_split = %lld exceeds int32",
                     (long long)(total_q * n_split));
     const size_t need = mla_sparse_prefill_split_workspace_size((int32_t)total_q, n_heads, n_split);
+    if (library_scratch) {
+        if (need > (size_t)MLA_SPLIT_SCRATCH_BYTES)
+            return fail(MLA_ERR_UNSUPPORTED,
+                        "the %d parts of %lld queries x %d heads need %zu bytes; the library's "
+                        "scratch array holds %zu (MLA_SPLIT_SCRATCH_BYTES)",
+                        n_split, (long long)total_q, n_heads, need, (size_t)MLA_SPLIT_SCRATCH_BYTES);
+        st = scratch_of_current_device(&workspace);
+        if (st != MLA_OK) return st;
+        workspace_bytes = MLA_SPLIT_SCRATCH_BYTES;
+    }
     if (!workspace) return fail(MLA_ERR_INVALID_ARG, "workspace is NULL");
     if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
@@ -328,6 +373,27 @@ mla_status_t mla_sparse_prefill_split(const mla_batch_t *batch, const void *q, c
     m.out = (__bf16 *)out;
     m.lse_out = lse;
     return hip_status(mla::launch_merge(m, (hipStream_t)stream), "merge launch");
+}
+}  // namespace
+
+mla_status_t mla_sparse_prefill_split(const mla_batch_t *batch, const void *q, const void *kv,
+                                      const float *kv_scale, mla_kv_dtype_t kv_dtype,
+                                      int64_t kv_row_stride, int64_t kv_scale_stride,
+                                      const int32_t *indices, int32_t k, int32_t n_heads,
+                                      float sm_scale, int32_t n_split, void *workspace,
+                                      size_t workspace_bytes, void *out, float *lse, void *stream) {
+    return split_impl(batch, q, kv, kv_scale, kv_dtype, kv_row_stride, kv_scale_stride, indices, k,
+                      n_heads, sm_scale, n_split, workspace, workspace_bytes, false, out, lse, stream);
+}
+
+mla_status_t mla_sparse_prefill_split_noalloc(const mla_batch_t *batch, const void *q,
+                                              const void *kv, const float *kv_scale,
+                                              mla_kv_dtype_t kv_dtype, int64_t kv_row_stride,
+                                              int64_t kv_scale_stride, const int32_t *indices,
+                                              int32_t k, int32_t n_heads, float sm_scale,
+                                              int32_t n_split, void *out, float *lse, void *stream) {
+    return split_impl(batch, q, kv, kv_scale, kv_dtype, kv_row_stride, kv_scale_stride, indices, k,
+                      n_heads, sm_scale, n_split, nullptr, 0, true, out, lse, stream);
 }
 
 mla_status_t mla_merge_attention(const void *const *o_parts, const float *const *lse_parts,

@@ -206,6 +206,28 @@ def test_split_attention_argument_checks(lib):
     assert split_call(lib, empty, ws=None, out=None, lse=None) == sm.MLA_OK
 
 
+def test_split_noalloc_argument_checks(lib):
+    """mla_sparse_prefill_split_noalloc: the split checks, and parts larger
+    than the library's scratch array rejected, all before any HIP call."""
+    def call(b, n_split=2, k=8, H=64, out=FAKE):
+        return lib.mla_sparse_prefill_split_noalloc(ctypes.byref(b), FAKE, FAKE, FAKE, 1, 576, 4,
+                                                    FAKE, k, H, 0.07, n_split, out, FAKE, None)
+    b, keep = make_batch()
+    assert call(b, n_split=-1) == INVALID
+    assert call(b, n_split=17) == UNSUPPORTED
+    assert call(b, n_split=9, k=8) == INVALID                 # a part without a list entry
+    assert call(b, H=12) == UNSUPPORTED                        # the attention checks apply
+    assert call(b, out=None) == INVALID
+    # 257 queries x 64 heads in 2 parts need 33.8 MB: above the 16.06 MiB array
+    big, keep2 = make_batch(cu_q=(0, 257), cu_kv=(0, 300))
+    assert call(big, n_split=2) == UNSUPPORTED
+    assert b"MLA_SPLIT_SCRATCH_BYTES" in lib.mla_last_error()
+    # 256 virtual queries of 64 heads fit exactly
+    assert lib.mla_sparse_prefill_split_workspace_size(64, 64, 4) == 16 * 1024 * 1024 + 64 * 1024
+    empty, keep3 = make_batch(cu_q=(0, 0), cu_kv=(0, 10))
+    assert call(empty, out=None) == sm.MLA_OK
+
+
 def test_merge_argument_checks(lib):
     """mla_merge_attention validates on the host before any HIP call."""
     import ctypes
