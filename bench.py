@@ -84,6 +84,8 @@ def kernel_bytes(wl, kv_dtype: str, idx_dtype: str = "bf16") -> dict:
             out["indexer"] = pc["causal"] * 4 + wl.total_q * wl.idx_heads * (2 * wl.idx_dim + 4) \
                 + wl.total_kv * 2 * wl.idx_dim
         out["topk"] = pc["causal"] * 4 + wl.total_q * wl.topk * 4
+        # fused: the indexer's inputs in, the indices out (no score matrix)
+        out["indexer_topk"] = out["indexer"] - pc["causal"] * 4 + wl.total_q * wl.topk * 4
     return out
 
 
@@ -95,9 +97,11 @@ def kernel_bytes(wl, kv_dtype: str, idx_dtype: str = "bf16") -> dict:
 # hash of the kernel's sources and reported only while the sources match.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"attention": ("attention.hip", "attention_f8.hip", "attn_common.h"),
-                  "indexer": ("indexer.hip", "attn_common.h"), "topk": ("topk.hip",)}
+                  "indexer": ("indexer.hip", "attn_common.h", "cand_select.h"), "topk": ("topk.hip",),
+                  "indexer_topk": ("indexer.hip", "attn_common.h", "cand_select.h", "topk.hip")}
 KERNEL_SYMBOLS = {"attention": ("attn_kernel", "attn_f8_kernel"), "indexer": ("indexer_kernel",),
-                  "topk": ("topk_kernel",)}
+                  "topk": ("topk_kernel",), "indexer_topk": ("indexer_kernel", "cand_merge_kernel")}
+PATH_KERNELS = {"fused": ("indexer_topk", "attention"), "unfused": ("indexer", "topk", "attention")}
 COPY_SYMBOL = "copyBuffer"
 
 
@@ -115,55 +119,62 @@ def _counter_rows(path: str, counter: str) -> list:
         return [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
 
 
-def traffic_key(workload: str, kv_dtype: str, idx_dtype: str = "bf16") -> str:
+def traffic_key(workload: str, kv_dtype: str, idx_dtype: str = "bf16", path: str = "unfused") -> str:
     key = "%s/%s" % (workload, kv_dtype)
-    return key if idx_dtype == "bf16" else key + "/indexer-" + idx_dtype
+    key = key if idx_dtype == "bf16" else key + "/indexer-" + idx_dtype
+    return key if path == "unfused" else key + "/" + path
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str,
-                    kv_dtype: str, command: str, idx_dtype: str = "bf16") -> dict:
-    """Turn the two counter passes into bytes per launch and store them."""
+                    kv_dtype: str, command: str, idx_dtype: str = "bf16", path: str = "unfused") -> dict:
+    """Turn the two counter passes into bytes per launch and store them (a
+    kernel's launches: the sum over the dispatches of its symbols per step)."""
     n = calib_mib << 20
-    rec = {"workload": workload, "kv_dtype": kv_dtype, "indexer_dtype": idx_dtype,
+    rec = {"workload": workload, "kv_dtype": kv_dtype, "indexer_dtype": idx_dtype, "path": path,
            "calibration_bytes": n,
            "command": command, "kernels": {}}
-    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
-        rows = _counter_rows(path, counter)
+    for key, csv_path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _counter_rows(csv_path, counter)
         copies = [float(r["Counter_Value"]) for r in rows if COPY_SYMBOL in r["Kernel_Name"]]
         if not copies:
-            raise SystemExit("no %s dispatch in %s" % (COPY_SYMBOL, path))
+            raise SystemExit("no %s dispatch in %s" % (COPY_SYMBOL, csv_path))
         kib = max(copies)                      # the calibration copy is by far the largest
         factor = n / (kib * 1024.0)
         rec[key + "_factor"] = factor
         rec[key + "_copy_kib"] = kib
-        for name, syms in KERNEL_SYMBOLS.items():
-            vals = [float(r["Counter_Value"]) for r in rows
-                    if any(sym + "<" in r["Kernel_Name"] or sym + "(" in r["Kernel_Name"] for sym in syms)]
-            if vals:
+        for name in PATH_KERNELS[path]:
+            syms = KERNEL_SYMBOLS[name]
+            per_sym = [[float(r["Counter_Value"]) for r in rows
+                        if sym + "<" in r["Kernel_Name"] or sym + "(" in r["Kernel_Name"]]
+                       for sym in syms]
+            per_sym = [v for v in per_sym if v]
+            if per_sym:
                 d = rec["kernels"].setdefault(name, {"source_hash": kernel_source_hash(name)})
-                d[key + "_kib_avg"] = float(np.mean(vals))
-                d[key + "_bytes"] = float(np.mean(vals)) * 1024.0 * factor
-                d[key + "_dispatches"] = len(vals)
+                kib = float(sum(np.mean(v) for v in per_sym))
+                d[key + "_kib_avg"] = kib
+                d[key + "_bytes"] = kib * 1024.0 * factor
+                d[key + "_dispatches"] = max(len(v) for v in per_sym)
     for d in rec["kernels"].values():
         d["bytes"] = d.get("fetch_bytes", 0.0) + d.get("write_bytes", 0.0)
     table = {}
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             table = json.load(fh)
-    table[traffic_key(workload, kv_dtype, idx_dtype)] = rec
+    table[traffic_key(workload, kv_dtype, idx_dtype, path)] = rec
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(table, fh, indent=1, sort_keys=True)
         fh.write("\n")
     return rec
 
 
-def measured_traffic(workload: str, kv_dtype: str, name: str, idx_dtype: str = "bf16"):
+def measured_traffic(workload: str, kv_dtype: str, name: str, idx_dtype: str = "bf16",
+                     path: str = "unfused"):
     """HBM bytes per launch of kernel `name` from the stored counter passes,
     or None when there are none or the kernel's sources changed since."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as fh:
-        rec = json.load(fh).get(traffic_key(workload, kv_dtype, idx_dtype))
+        rec = json.load(fh).get(traffic_key(workload, kv_dtype, idx_dtype, path))
     d = rec and rec["kernels"].get(name)
     if not d or d["source_hash"] != kernel_source_hash(name) or "fetch_bytes" not in d \
             or "write_bytes" not in d:
@@ -250,6 +261,10 @@ def main():
     ap.add_argument("--split", type=int, default=None,
                     help="attention through mla_sparse_prefill_split with this many parts per "
                          "query (0: chosen from the CU count)")
+    ap.add_argument("--path", default="unfused", choices=("fused", "unfused"),
+                    help="unfused: mla_indexer_score, mla_topk_select, attention; fused: "
+                         "mla_indexer_topk (indexer and top-k in one pass, no score matrix) then "
+                         "attention. Identical indices; unfused measures faster at 32k")
     ap.add_argument("--indexer-dtype", default="bf16", choices=("bf16", "fp8"),
                     help="indexer queries and keys: bf16, or E4M3 codes with an fp32 scale per "
                          "row (mla_indexer_score_fp8)")
@@ -272,7 +287,8 @@ def main():
             raise SystemExit("--ingest-counters needs the --copy-calibration-mib of the runs")
         rec = ingest_counters(args.ingest_counters[0], args.ingest_counters[1],
                               args.copy_calibration_mib, wl.name, args.kv_dtype or wl.kv_dtype,
-                              args.command, args.indexer_dtype)
+                              args.command, args.indexer_dtype,
+                              "unfused" if wl.dense else args.path)
         print(json.dumps(rec, indent=1))
         return
 
@@ -294,13 +310,16 @@ def main():
     idx_dtype = args.indexer_dtype
     inp = mla_inputs.make_inputs(wl, dev, kv_dtype=kv_dtype, idx_dtype=idx_dtype)
     batch = sm.Batch.from_inputs(inp, dev)
-    scores = None if wl.dense else torch.empty((wl.total_q, wl.max_kv_len), dtype=torch.float32,
-                                               device=dev)
+    fused = args.path == "fused" and not wl.dense
+    scores = None if wl.dense or fused else torch.empty((wl.total_q, wl.max_kv_len),
+                                                        dtype=torch.float32, device=dev)
+    topk_ws = sm.topk_workspace(batch, wl.topk) if fused else None
     indices = None if wl.dense else torch.empty((wl.total_q, wl.topk), dtype=torch.int32,
                                                 device=dev)
     out = torch.empty((wl.total_q, wl.n_heads, D_V), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((wl.total_q, wl.n_heads), dtype=torch.float32, device=dev)
-    names = ["attention"] if wl.dense else ["indexer", "topk", "attention"]
+    names = (["attention"] if wl.dense else ["indexer_topk", "attention"] if fused
+             else ["indexer", "topk", "attention"])
     split_ws = None
     if args.split is not None:
         need = sm.load_library().mla_sparse_prefill_split_workspace_size(wl.total_q, wl.n_heads,
@@ -318,17 +337,27 @@ def main():
             mark(1)
             return
         mark(0)
-        if idx_dtype == "fp8":
-            sm.indexer_score_fp8(batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"],
-                                 inp["k_idx_scale"], inp["w"], scores=scores)
+        if fused:
+            if idx_dtype == "fp8":
+                sm.indexer_topk_fp8(batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"],
+                                    inp["k_idx_scale"], inp["w"], wl.topk, indices=indices,
+                                    workspace=topk_ws)
+            else:
+                sm.indexer_topk(batch, inp["q_idx"], inp["k_idx"], inp["w"], wl.topk,
+                                indices=indices, workspace=topk_ws)
+            mark(1)
         else:
-            sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"], scores=scores)
-        mark(1)
-        sm.topk_select(batch, scores, wl.topk, indices=indices)
-        mark(2)
+            if idx_dtype == "fp8":
+                sm.indexer_score_fp8(batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"],
+                                     inp["k_idx_scale"], inp["w"], scores=scores)
+            else:
+                sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"], scores=scores)
+            mark(1)
+            sm.topk_select(batch, scores, wl.topk, indices=indices)
+            mark(2)
         sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], indices, wl.sm_scale,
                           out=out, lse=lse, n_split=args.split, workspace=split_ws)
-        mark(3)
+        mark(len(names))
 
     if args.copy_calibration_mib > 0:
         src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
@@ -377,16 +406,17 @@ def main():
         del scrub
 
     fl = workload_flops(wl)
+    fl["indexer_topk"] = fl["indexer"]
     byts = kernel_bytes(wl, kv_dtype, idx_dtype)
     # peak of the MFMA type each contraction runs on: the indexer's input
     # dtype; the attention's KV dtype (the FP8 kernel issues E4M3 MFMAs)
-    peak_of = {"indexer": PEAK_TFLOPS[idx_dtype],
+    peak_of = {"indexer": PEAK_TFLOPS[idx_dtype], "indexer_topk": PEAK_TFLOPS[idx_dtype],
                "attention": PEAK_TFLOPS["fp8" if kv_dtype == "fp8" else "bf16"]}
     kern = {}
     for n in names:
         t = per_kernel_ms[n] * 1e-3
         d = {"ms": per_kernel_ms[n], "ms_mean": per_kernel_mean[n]}
-        if n in ("indexer", "attention"):
+        if n in ("indexer", "indexer_topk", "attention"):
             tf = fl[n] / t / 1e12
             d.update({"tflops": tf, "bound": "mfma", "peak_tflops": peak_of[n],
                       "frac": tf / peak_of[n]})
@@ -398,7 +428,7 @@ def main():
         if n in byts:
             d["algo_bytes"] = byts[n]
             d["gbs"] = byts[n] / t / 1e9
-        d["traffic"] = measured_traffic(wl.name, kv_dtype, n, idx_dtype)
+        d["traffic"] = measured_traffic(wl.name, kv_dtype, n, idx_dtype, args.path)
         kern[n] = d
     kern["topk"] = kern.get("topk", {})
     if "topk" in per_kernel_ms:
@@ -439,7 +469,8 @@ def main():
         "dtype": dtype_label,
         "dtype_detail": dtype_detail,
         "data": "synthetic",
-        "config": {"workload": wl.name, "seq_lens": list(wl.kv_lens), "total_q": wl.total_q,
+        "config": {"workload": wl.name, "path": None if wl.dense else args.path,
+                   "seq_lens": list(wl.kv_lens), "total_q": wl.total_q,
                    "n_heads": wl.n_heads, "indexer": "%dx%d" % (wl.idx_heads, wl.idx_dim),
                    "indexer_dtype": None if wl.dense else idx_dtype,
                    "attention_split": args.split,

@@ -14,6 +14,8 @@
  *                       queries and keys with a scale each (footnote 3 stores
  *                       an indexer key as 128 FP8 values plus a 4-byte scale).
  *   mla_topk_select     keeps the k best-scoring earlier tokens per query.
+ *   mla_indexer_topk    both in one pass, without the score matrix (and
+ *                       mla_indexer_topk_fp8 from FP8 indexer inputs).
  *   mla_sparse_prefill  absorbed (MQA-form) MLA attention over the kept tokens:
  *                       one 576-value latent row per token (512 latent + 64
  *                       rope) serves every head, QK over 576 dims and PV over
@@ -144,6 +146,47 @@ mla_status_t mla_indexer_score_fp8(const mla_batch_t *batch, const void *q_idx, 
  * Supported: 1 <= k <= 4096; max_kv_len <= 524288 (MLA_ERR_UNSUPPORTED otherwise). */
 mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int64_t ld_scores,
                              int32_t k, int32_t *indices, void *stream);
+
+/* Bytes of workspace mla_indexer_topk and mla_indexer_topk_fp8 need for this
+ * batch and k (0 for an invalid batch, k < 1 or no query). It depends on the
+ * current device's compute-unit count, which sets how the keys of a small
+ * batch are split over workgroups: query it with the device the call will
+ * run on current. About total_q * (2k + 256) * 8 bytes when the batch has at
+ * least two eight-query blocks per compute unit. */
+size_t mla_topk_workspace_size(const mla_batch_t *batch, int32_t k);
+
+/* Indexer and top-k in one pass, without the score matrix (spke.com article,
+ * section "PCP": the indexer's cost, and its score matrix, grow with the
+ * square of the prompt length; section "Warum nicht TP oder DP?": it keeps
+ * the 2,048 best earlier tokens). indices[i, 0:k] is exactly what
+ * mla_topk_select gives on the scores mla_indexer_score computes for the same
+ * inputs: the same kernels compute every score with the same instructions in
+ * the same order, and the selection rule (k largest, equal scores to the
+ * smaller j, -0 equal to +0, all keys when q_pos[i] + 1 <= k, ascending,
+ * -1 padded) is applied exactly, to a candidate list that provably holds the
+ * top k. Scores must not be NaN.
+ *   q_idx, k_idx, w, n_heads, head_dim: as mla_indexer_score
+ *   k          1..4096
+ *   indices    device [total_q, k] int32, 4-byte aligned
+ *   workspace  device, 256-byte aligned, at least mla_topk_workspace_size(batch, k)
+ *              bytes, owned by the caller; holds each query's candidate list
+ *              of (score key, index) pairs; two calls in flight on different
+ *              streams must not share it
+ * Errors as mla_indexer_score (ld_scores aside), plus MLA_ERR_INVALID_ARG for
+ * k < 1, a NULL indices or workspace, a misaligned or too small workspace,
+ * and MLA_ERR_UNSUPPORTED for k > 4096. Nothing is enqueued then. */
+mla_status_t mla_indexer_topk(const mla_batch_t *batch, const void *q_idx, const void *k_idx,
+                              const float *w, int32_t n_heads, int32_t head_dim, int32_t k,
+                              int32_t *indices, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* mla_indexer_topk from FP8 indexer inputs: the scores of
+ * mla_indexer_score_fp8 (same arguments q_idx, q_scale, k_idx, k_scale), then
+ * the same exact selection. */
+mla_status_t mla_indexer_topk_fp8(const mla_batch_t *batch, const void *q_idx, const float *q_scale,
+                                  const void *k_idx, const float *k_scale, const float *w,
+                                  int32_t n_heads, int32_t head_dim, int32_t k, int32_t *indices,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Absorbed MLA attention over selected latent rows (spke.com article,
  * footnote 1 and section "PCP": one latent row read per selected key serves

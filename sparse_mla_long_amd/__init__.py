@@ -11,6 +11,8 @@ Calls (same names as the C ABI, without the ``mla_`` prefix):
   indexer_score_fp8(batch, q_idx, q_scale, k_idx, k_scale, w, ...)
                                                -> scores from E4M3 codes with scales
   topk_select(batch, scores, k, ...)           -> indices [total_q, k] int32
+  indexer_topk(batch, q_idx, k_idx, w, k, ...) -> indices, without the score matrix
+  indexer_topk_fp8(batch, q_idx, q_scale, k_idx, k_scale, w, k, ...)
   sparse_prefill(batch, q, kv, ...)            -> (out [total_q, H, 512] bf16, lse [total_q, H] fp32)
       (n_split=S: the split-KV call, mla_sparse_prefill_split; with
       noalloc=True, mla_sparse_prefill_split_noalloc)
@@ -42,7 +44,8 @@ class MlaBatch(ctypes.Structure):
 
 EXPORTS = ("mla_indexer_score", "mla_indexer_score_fp8", "mla_topk_select", "mla_sparse_prefill",
            "mla_sparse_prefill_split", "mla_sparse_prefill_split_workspace_size",
-           "mla_sparse_prefill_split_noalloc",
+           "mla_sparse_prefill_split_noalloc", "mla_topk_workspace_size", "mla_indexer_topk",
+           "mla_indexer_topk_fp8",
            "mla_merge_attention", "mla_status_string", "mla_last_error", "mla_abi_version")
 
 _lib = None
@@ -61,6 +64,10 @@ def load_library(path: str = LIB_PATH):
     L.mla_indexer_score.argtypes = [BP, P, P, P, I32, I32, P, I64, P]
     L.mla_indexer_score_fp8.argtypes = [BP, P, P, P, P, P, I32, I32, P, I64, P]
     L.mla_topk_select.argtypes = [BP, P, I64, I32, P, P]
+    L.mla_topk_workspace_size.argtypes = [BP, I32]
+    L.mla_topk_workspace_size.restype = ctypes.c_size_t
+    L.mla_indexer_topk.argtypes = [BP, P, P, P, I32, I32, I32, P, P, ctypes.c_size_t, P]
+    L.mla_indexer_topk_fp8.argtypes = [BP, P, P, P, P, P, I32, I32, I32, P, P, ctypes.c_size_t, P]
     L.mla_sparse_prefill.argtypes = [BP, P, P, P, ctypes.c_int, I64, I64, P, I32, I32,
                                      ctypes.c_float, P, P, P]
     L.mla_sparse_prefill_split.argtypes = [BP, P, P, P, ctypes.c_int, I64, I64, P, I32, I32,
@@ -71,7 +78,8 @@ def load_library(path: str = LIB_PATH):
     L.mla_sparse_prefill_split_workspace_size.restype = ctypes.c_size_t
     L.mla_merge_attention.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                       I32, I32, I32, P, P, P]
-    for f in ("mla_indexer_score", "mla_indexer_score_fp8", "mla_topk_select", "mla_sparse_prefill",
+    for f in ("mla_indexer_score", "mla_indexer_score_fp8", "mla_topk_select", "mla_indexer_topk",
+              "mla_indexer_topk_fp8", "mla_sparse_prefill",
               "mla_sparse_prefill_split", "mla_sparse_prefill_split_noalloc", "mla_merge_attention"):
         getattr(L, f).restype = ctypes.c_int
     L.mla_status_string.argtypes = [ctypes.c_int]
@@ -214,6 +222,60 @@ def topk_select(batch: Batch, scores: torch.Tensor, k: int,
     return indices
 
 
+def topk_workspace(batch: Batch, k: int) -> torch.Tensor:
+    """A workspace for indexer_topk / indexer_topk_fp8 (mla_topk_workspace_size bytes)."""
+    need = load_library().mla_topk_workspace_size(batch.c, int(k))
+    return torch.empty((max(need, 1),), dtype=torch.uint8, device=batch.device)
+
+
+def indexer_topk(batch: Batch, q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, k: int,
+                 indices: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mla_indexer_topk: the indexer and top-k in one pass, no score matrix.
+    Returns indices [total_q, k] int32 (ascending, -1 padded)."""
+    dev = batch.device
+    n_heads, head_dim = q_idx.shape[1], q_idx.shape[2]
+    _need(q_idx, "q_idx", torch.bfloat16, dev, (batch.total_q, n_heads, head_dim))
+    _need(k_idx, "k_idx", torch.bfloat16, dev, (batch.total_kv, head_dim))
+    _need(w, "w", torch.float32, dev, (batch.total_q, n_heads))
+    indices = _indices_out(batch, k, indices)
+    workspace = topk_workspace(batch, k) if workspace is None else workspace
+    _need(workspace, "workspace", torch.uint8, dev)
+    _check(load_library().mla_indexer_topk(batch.c, _ptr(q_idx), _ptr(k_idx), _ptr(w), n_heads,
+                                           head_dim, int(k), _ptr(indices), _ptr(workspace),
+                                           workspace.numel(), _stream(q_idx)))
+    return indices
+
+
+def indexer_topk_fp8(batch: Batch, q_idx: torch.Tensor, q_scale: torch.Tensor,
+                     k_idx: torch.Tensor, k_scale: torch.Tensor, w: torch.Tensor, k: int,
+                     indices: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mla_indexer_topk_fp8: indexer_score_fp8's scores and top-k in one pass."""
+    dev = batch.device
+    n_heads, head_dim = q_idx.shape[1], q_idx.shape[2]
+    _need(q_idx, "q_idx", torch.uint8, dev, (batch.total_q, n_heads, head_dim))
+    _need(q_scale, "q_scale", torch.float32, dev, (batch.total_q, n_heads))
+    _need(k_idx, "k_idx", torch.uint8, dev, (batch.total_kv, head_dim))
+    _need(k_scale, "k_scale", torch.float32, dev, (batch.total_kv,))
+    _need(w, "w", torch.float32, dev, (batch.total_q, n_heads))
+    indices = _indices_out(batch, k, indices)
+    workspace = topk_workspace(batch, k) if workspace is None else workspace
+    _need(workspace, "workspace", torch.uint8, dev)
+    _check(load_library().mla_indexer_topk_fp8(batch.c, _ptr(q_idx), _ptr(q_scale), _ptr(k_idx),
+                                               _ptr(k_scale), _ptr(w), n_heads, head_dim, int(k),
+                                               _ptr(indices), _ptr(workspace), workspace.numel(),
+                                               _stream(q_idx)))
+    return indices
+
+
+def _indices_out(batch: Batch, k: int, indices: Optional[torch.Tensor]) -> torch.Tensor:
+    if indices is None:
+        return torch.empty((batch.total_q, k), dtype=torch.int32, device=batch.device)
+    _need(indices, "indices", torch.int32, batch.device, (batch.total_q, k))
+    return indices
+
+
 def sparse_prefill(batch: Batch, q: torch.Tensor, kv: torch.Tensor,
                    kv_scale: Optional[torch.Tensor] = None,
                    indices: Optional[torch.Tensor] = None, sm_scale: float = 192 ** -0.5,
@@ -317,13 +379,22 @@ def merge_attention(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.T
 
 
 def prefill(batch: Batch, inp: dict, topk: int, sm_scale: float, dense: bool = False,
-            scores: Optional[torch.Tensor] = None):
+            scores: Optional[torch.Tensor] = None, fused: bool = False):
     """The whole path for one layer: indexer -> top-k -> sparse attention
-    (or dense causal attention when ``dense``). Returns (out, lse, indices)."""
+    (or dense causal attention when ``dense``; with ``fused``, indexer and
+    top-k in one pass). Returns (out, lse, indices)."""
     if dense:
         out, lse = sparse_prefill(batch, inp["q"], inp["kv"], inp.get("kv_scale"), None,
                                   sm_scale)
         return out, lse, None
+    if fused:
+        if inp.get("k_idx_scale") is not None:
+            idx = indexer_topk_fp8(batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"],
+                                   inp["k_idx_scale"], inp["w"], topk)
+        else:
+            idx = indexer_topk(batch, inp["q_idx"], inp["k_idx"], inp["w"], topk)
+        out, lse = sparse_prefill(batch, inp["q"], inp["kv"], inp.get("kv_scale"), idx, sm_scale)
+        return out, lse, idx
     if inp.get("k_idx_scale") is not None:
         sc = indexer_score_fp8(batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"],
                                inp["k_idx_scale"], inp["w"], scores=scores)

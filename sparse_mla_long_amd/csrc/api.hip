@@ -111,49 +111,20 @@ mla_status_t scratch_of_current_device(void **ptr) {
 extern "C" {
 
 namespace {
-// Shared checks and launch of the two indexer entry points (scales are NULL for bf16).
-mla_status_t indexer(const mla_batch_t *batch, const void *q_idx, const float *q_scale,
-                     const void *k_idx, const float *k_scale, const float *w, int32_t n_heads,
-                     int32_t head_dim, float *scores, int64_t ld_scores, bool fp8, void *stream) {
-    mla::IndexerArgs a{};
-    mla_status_t st = check_batch(batch, &a.batch);
-    if (st != MLA_OK) return st;
-    if (n_heads < 1) return fail(MLA_ERR_INVALID_ARG, "n_heads must be >= 1 (got %d)", n_heads);
-    if (head_dim < 1) return fail(MLA_ERR_INVALID_ARG, "head_dim must be >= 1 (got %d)", head_dim);
-    if (n_heads > 64) return fail(MLA_ERR_UNSUPPORTED, "indexer n_heads %d > 64", n_heads);
-    if (head_dim != 64 && head_dim != 128)
-        return fail(MLA_ERR_UNSUPPORTED, "indexer head_dim %d not in {64, 128}", head_dim);
-    if (ld_scores < batch->max_kv_len)
-        return fail(MLA_ERR_INVALID_ARG, "ld_scores %lld < max_kv_len %d", (long long)ld_scores,
-                    batch->max_kv_len);
-    if (batch->total_q == 0) return ok();
-    if (!q_idx || !k_idx || !w || !scores)
-        return fail(MLA_ERR_INVALID_ARG, "q_idx / k_idx / w / scores is NULL");
-    if (fp8 && (!q_scale || !k_scale))
-        return fail(MLA_ERR_INVALID_ARG, "q_scale / k_scale is NULL");
-    if (!aligned(q_idx, 16) || !aligned(k_idx, 16))
-        return fail(MLA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
-    if (!aligned(w, 4) || !aligned(scores, 4))
-        return fail(MLA_ERR_INVALID_ARG, "w and scores must be 4-byte aligned");
-    if (fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4)))
-        return fail(MLA_ERR_INVALID_ARG, "q_scale and k_scale must be 4-byte aligned");
+// Eight-query indexer blocks of a (validated) batch.
+int64_t indexer_blocks(const mla_batch_t *batch) {
     int64_t blocks = 0;
     for (int32_t s = 0; s < batch->num_seqs; ++s) {
         const int32_t nq = batch->cu_seqlens_q_host[s + 1] - batch->cu_seqlens_q_host[s];
         blocks += (nq + mla::kIdxQueriesPerBlock - 1) / mla::kIdxQueriesPerBlock;
     }
-    a.q_idx = q_idx;
-    a.k_idx = k_idx;
-    a.q_scale = q_scale;
-    a.k_scale = k_scale;
-    a.w = w;
-    a.scores = scores;
-    a.ld = ld_scores;
-    a.n_heads = n_heads;
-    a.head_dim = head_dim;
-    // Few query blocks (a short chunk behind a long prefix): split every
-    // block's keys over several workgroups, about two per CU in all, down to
-    // one key tile each. Each score is still written once.
+    return blocks;
+}
+
+// Few query blocks (a short chunk behind a long prefix): split every block's
+// keys over several workgroups, about two per CU in all, down to one key tile
+// each. Each score is still computed once.
+int32_t indexer_key_split(const mla_batch_t *batch, int64_t blocks) {
     int dev = 0, n_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -164,12 +135,115 @@ mla_status_t indexer(const mla_batch_t *batch, const void *q_idx, const float *q
         split = std::min<int64_t>(split, ((int64_t)batch->max_kv_len + mla::kIdxKeyTile - 1) / mla::kIdxKeyTile);
         split = std::max<int64_t>(split, 1);
     }
-    a.key_split = (int32_t)split;
+    return (int32_t)split;
+}
+
+// Workspace of the fused indexer + top-k: candidate lists of
+// cand_capacity(k) (key, j) entries per (query, key part), then the lists'
+// lengths.
+size_t cand_list_bytes(int64_t total_q, int64_t parts, int64_t k) {
+    return ((size_t)(total_q * parts * mla::cand_capacity(k)) * 8 + 255) / 256 * 256;
+}
+size_t topk_ws_bytes(int64_t total_q, int64_t parts, int64_t k) {
+    return cand_list_bytes(total_q, parts, k) + (size_t)(total_q * parts) * 4;
+}
+
+// Shared checks and launch of the indexer entry points (scales are NULL for
+// bf16). topk > 0: the fused form, which writes indices instead of scores
+// and keeps its candidate lists in the workspace.
+mla_status_t indexer(const mla_batch_t *batch, const void *q_idx, const float *q_scale,
+                     const void *k_idx, const float *k_scale, const float *w, int32_t n_heads,
+                     int32_t head_dim, float *scores, int64_t ld_scores, bool fp8, void *stream,
+                     int32_t topk = 0, int32_t *indices = nullptr, void *workspace = nullptr,
+                     size_t workspace_bytes = 0) {
+    mla::IndexerArgs a{};
+    mla_status_t st = check_batch(batch, &a.batch);
+    if (st != MLA_OK) return st;
+    const bool fused = topk != 0;
+    if (n_heads < 1) return fail(MLA_ERR_INVALID_ARG, "n_heads must be >= 1 (got %d)", n_heads);
+    if (head_dim < 1) return fail(MLA_ERR_INVALID_ARG, "head_dim must be >= 1 (got %d)", head_dim);
+    if (fused && topk < 1) return fail(MLA_ERR_INVALID_ARG, "k must be >= 1 (got %d)", topk);
+    if (n_heads > 64) return fail(MLA_ERR_UNSUPPORTED, "indexer n_heads %d > 64", n_heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(MLA_ERR_UNSUPPORTED, "indexer head_dim %d not in {64, 128}", head_dim);
+    if (fused && topk > 4096) return fail(MLA_ERR_UNSUPPORTED, "k %d > 4096", topk);
+    if (!fused && ld_scores < batch->max_kv_len)
+        return fail(MLA_ERR_INVALID_ARG, "ld_scores %lld < max_kv_len %d", (long long)ld_scores,
+                    batch->max_kv_len);
+    if (batch->total_q == 0) return ok();
+    if (!q_idx || !k_idx || !w || (fused ? !indices : !scores))
+        return fail(MLA_ERR_INVALID_ARG, "q_idx / k_idx / w / %s is NULL", fused ? "indices" : "scores");
+    if (fp8 && (!q_scale || !k_scale))
+        return fail(MLA_ERR_INVALID_ARG, "q_scale / k_scale is NULL");
+    if (!aligned(q_idx, 16) || !aligned(k_idx, 16))
+        return fail(MLA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
+    if (!aligned(w, 4) || (fused ? !aligned(indices, 4) : !aligned(scores, 4)))
+        return fail(MLA_ERR_INVALID_ARG, "w and %s must be 4-byte aligned", fused ? "indices" : "scores");
+    if (fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4)))
+        return fail(MLA_ERR_INVALID_ARG, "q_scale and k_scale must be 4-byte aligned");
+    const int64_t blocks = indexer_blocks(batch);
+    const int32_t split = indexer_key_split(batch, blocks);
+    if (fused) {
+        const size_t need = topk_ws_bytes(batch->total_q, split, topk);
+        if (!workspace) return fail(MLA_ERR_INVALID_ARG, "workspace is NULL");
+        if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(MLA_ERR_INVALID_ARG, "workspace_bytes %zu < %zu (mla_topk_workspace_size)",
+                        workspace_bytes, need);
+        a.topk = topk;
+        a.cand = (uint2 *)workspace;
+        a.cand_cap = (int32_t)mla::cand_capacity(topk);
+        a.cand_n = (int32_t *)((uint8_t *)workspace + cand_list_bytes(batch->total_q, split, topk));
+    }
+    a.q_idx = q_idx;
+    a.k_idx = k_idx;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.w = w;
+    a.scores = scores;
+    a.ld = ld_scores;
+    a.n_heads = n_heads;
+    a.head_dim = head_dim;
+    a.key_split = split;
     a.n_blocks = (int32_t)(blocks * split);
     a.fp8 = fp8;
-    return hip_status(mla::launch_indexer(a, (hipStream_t)stream), "indexer launch");
+    st = hip_status(mla::launch_indexer(a, (hipStream_t)stream), "indexer launch");
+    if (st != MLA_OK || !fused) return st;
+    mla::CandSelectArgs m{};
+    m.batch = a.batch;
+    m.cand = a.cand;
+    m.cand_n = a.cand_n;
+    m.cand_cap = a.cand_cap;
+    m.n_parts = split;
+    m.topk = topk;
+    m.indices = indices;
+    return hip_status(mla::launch_cand_select(m, (hipStream_t)stream), "top-k select launch");
 }
 }  // namespace
+
+size_t mla_topk_workspace_size(const mla_batch_t *batch, int32_t k) {
+    mla::BatchDev dev{};
+    if (k < 1 || check_batch(batch, &dev) != MLA_OK || batch->total_q == 0) return 0;
+    return topk_ws_bytes(batch->total_q, indexer_key_split(batch, indexer_blocks(batch)), k);
+}
+
+mla_status_t mla_indexer_topk(const mla_batch_t *batch, const void *q_idx, const void *k_idx,
+                              const float *w, int32_t n_heads, int32_t head_dim, int32_t k,
+                              int32_t *indices, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    if (k == 0) return fail(MLA_ERR_INVALID_ARG, "k must be >= 1 (got 0)");
+    return indexer(batch, q_idx, nullptr, k_idx, nullptr, w, n_heads, head_dim, nullptr, 0, false,
+                   stream, k, indices, workspace, workspace_bytes);
+}
+
+mla_status_t mla_indexer_topk_fp8(const mla_batch_t *batch, const void *q_idx, const float *q_scale,
+                                  const void *k_idx, const float *k_scale, const float *w,
+                                  int32_t n_heads, int32_t head_dim, int32_t k, int32_t *indices,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    if (k == 0) return fail(MLA_ERR_INVALID_ARG, "k must be >= 1 (got 0)");
+    return indexer(batch, q_idx, q_scale, k_idx, k_scale, w, n_heads, head_dim, nullptr, 0, true,
+                   stream, k, indices, workspace, workspace_bytes);
+}
 
 mla_status_t mla_indexer_score(const mla_batch_t *batch, const void *q_idx, const void *k_idx,
                                const float *w, int32_t n_heads, int32_t head_dim, float *scores,

@@ -23,6 +23,7 @@
 // key tile (one 4-byte-per-lane DMA per wave and tile; waves w and w + 4 bring
 // the same 64).
 #include "attn_common.h"
+#include "cand_select.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -59,8 +60,23 @@ template <bool F8> struct QOperand { typedef bf16x8 type; };
 template <> struct QOperand<true> { typedef i32x8 type; };
 
 // DI: indexer head dim; MB: 32-head blocks; F8: E4M3 codes with scales
-// (else bf16).
-template <int DI, int MB, bool F8>
+// (else bf16); TOPK: fused top-k selection instead of stored scores.
+//
+// Fused top-k. A wave keeps its query's candidate list in the workspace: a
+// key is appended, in ascending j, when its score's order key is above tau
+// (0, below every score, until the first compaction). When the list could
+// overflow within the next tile, the wave compacts it (cand_select.h): it
+// finds a threshold t with at least k listed keys at or above it (one
+// 256-bin histogram pass over the key range its appends tracked), keeps the
+// entries at or above t and sets tau = t. A later key at or below t cannot
+// make the top k: at least k earlier keys are at or above it and win any tie
+// by their smaller index. If that leaves the list too long (a bin holding
+// most of the keys), the exact selection keeps just the top k -- ties at the
+// k-th value only with the smallest j -- and tau becomes the k-th value. The
+// list therefore always holds every key that can still reach the top k, and
+// cand_select_kernel's exact selection over it (after this kernel) is the
+// top k of all the scores.
+template <int DI, int MB, bool F8, bool TOPK>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     constexpr int RB = F8 ? DI : 2 * DI;         // bytes per key row
     constexpr int CPR = RB / 16;                 // 16-byte chunks per key row
@@ -74,6 +90,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     // the same LDS object, so the compiler's own DMA tracking adds no waits)
     constexpr int kSlotBytes = kTileBytes + (F8 ? 4 * kKeyTile : 0);
     __shared__ __attribute__((aligned(16))) uint8_t ktile[kTileRing][kSlotBytes];
+    __shared__ uint32_t s_hist[TOPK ? kIdxWaves : 1][256];   // fused top-k: a radix histogram per wave
     typedef typename QOperand<F8>::type QOp;
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
@@ -184,8 +201,56 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     const int n_tiles = pmax / kKeyTile + 1;
     const int t_lo = attn::part_begin(n_tiles, a.key_split, kpart);
     const int t_hi = attn::part_begin(n_tiles, a.key_split, kpart + 1);
-    if (t_lo >= t_hi) return;            // block-uniform
-    float *srow = a.scores + (int64_t)qi * a.ld;
+    // fused top-k: this (query, key part)'s candidate list; rows with at most
+    // k keys keep them all and collect nothing
+    const bool collect = TOPK && active && pos + 1 > a.topk;
+    const int64_t list_id = (int64_t)qi * a.key_split + kpart;
+    uint2 *clist = TOPK && active ? a.cand + list_id * a.cand_cap : nullptr;
+    int nc = 0;                                         // list length (wave-uniform)
+    // append a score whose order key is above tau (all keys of real scores
+    // are above 0; a row that collects nothing never appends)
+    uint32_t tau = 0u;
+    uint32_t lmin = 0xffffffffu, lmax = 0u;             // bounds of this lane's appended keys
+    if (t_lo >= t_hi) {                                 // block-uniform
+        if (TOPK && active && lane == 0) a.cand_n[list_id] = 0;
+        return;
+    }
+    float *srow = TOPK ? nullptr : a.scores + (int64_t)qi * a.ld;
+    // fused top-k: append this lane's score of key j (if ok) to the list
+    auto append = [&](float sc, int j, bool ok) {
+        const uint32_t key = cand::order_key(sc);
+        const bool app = collect && ok && j <= pos && key > tau;
+        const uint64_t m = __ballot(app);
+        if (app) {
+            const int at = nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            clist[at] = make_uint2(key, (uint32_t)j);
+            lmin = min(lmin, key);
+            lmax = max(lmax, key);
+        }
+        nc += __popcll(m);
+    };
+    // fused top-k: drop the entries that can no longer reach the top k
+    auto compact = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's appends have landed
+        uint32_t *hist = s_hist[TOPK ? wv : 0];
+        const cand::Segments sg{clist, 0, 1, nullptr, nc};
+        uint32_t t = cand::wave_bin_threshold(sg, a.topk, cand::wave_umin(lmin), cand::wave_umax(lmax), hist);
+        nc = cand::wave_keep_from(sg, t, [&](int at, uint2 e) {
+            if (at < a.cand_cap) clist[at] = e;
+        });
+        if (nc > (a.topk + a.cand_cap - kKeyTile) / 2) {   // most keys in one bin: the exact top k
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const cand::Segments sk{clist, 0, 1, nullptr, nc};
+            int need_eq;
+            cand::wave_kth(sk, a.topk, hist, t, need_eq);
+            nc = cand::wave_compact(sk, t, need_eq, [&](int at, uint2 e) {
+                if (at < a.cand_cap) clist[at] = e;
+            });
+        }
+        tau = t;                                        // every kept key is at or above t
+        lmin = t;
+    };
     f32x16 prev[MB];
     float prev_sk = 0.f;                                // FP8: scale of key prev_j0 + col
     int prev_j0 = -1;                                   // first key of the pending sub-tile
@@ -207,7 +272,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     };
     auto store = [&](float sc, int j0) {
         const int j = j0 + col;
-        if (g == 0 && j <= pos) srow[j] = sc;
+        if constexpr (TOPK) append(sc, j, g == 0);
+        else if (g == 0 && j <= pos) srow[j] = sc;
     };
     // FP8: lane-half sums of two sub-tiles, a (keys ja + col, key scale ska)
     // and b (jb, skb): one swap gives lanes 0-31 both halves of a and lanes
@@ -219,7 +285,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         float sc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
         if constexpr (F8) sc *= g ? skb : ska;
         const int j0 = g ? jb : ja, j = j0 + col;
-        if (j0 >= 0 && j <= pos) srow[j] = sc;
+        if constexpr (TOPK) append(sc, j, j0 >= 0);
+        else if (j0 >= 0 && j <= pos) srow[j] = sc;
     };
 #pragma unroll
     for (int p = 0; p < kTileRing - 1; ++p) issue(t_lo + p, p);
@@ -268,35 +335,52 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         if constexpr (F8) {
 #pragma unroll
             for (int s = 0; s < kKeyTile / 32; s += 2) store_pair(sc[s], sj[s], sk[s], sc[s + 1], sj[s + 1], sk[s + 1]);
+        } else if constexpr (TOPK) {
+            // both lane halves hold each sub-tile's scores: half g appends
+            // sub-tile s + g of every pair
+#pragma unroll
+            for (int s = 0; s < kKeyTile / 32; s += 2) {
+                const int j0 = g ? sj[s + 1] : sj[s];
+                append(g ? sc[s + 1] : sc[s], j0 + col, j0 >= 0);
+            }
         } else {
 #pragma unroll
             for (int s = 0; s < kKeyTile / 32; ++s)
                 if (sj[s] >= 0) store(sc[s], sj[s]);
         }
+        if constexpr (TOPK) {
+            if (__builtin_amdgcn_readfirstlane(nc) > a.cand_cap - kKeyTile) compact();
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail DMA lands before the LDS is freed
     if constexpr (F8) store_pair(epilogue(prev), prev_j0, prev_sk, 0.f, -1, 0.f);
     else store(epilogue(prev), prev_j0);
+    if constexpr (TOPK) {
+        // the list's length for cand_select_kernel (its entries land before
+        // the kernel ends)
+        if (active && lane == 0) a.cand_n[list_id] = nc;
+    }
 }
 
-template <int DI, int MB, bool F8>
+template <int DI, int MB, bool F8, bool TOPK>
 hipError_t launch_t(const IndexerArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((indexer_kernel<DI, MB, F8>), dim3(a.n_blocks), dim3(kIdxThreads), 0, s, a);
+    hipLaunchKernelGGL((indexer_kernel<DI, MB, F8, TOPK>), dim3(a.n_blocks), dim3(kIdxThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <bool F8>
+template <bool F8, bool TOPK>
 hipError_t launch_dtype(const IndexerArgs &a, hipStream_t s) {
     const bool two = a.n_heads > 32;
-    if (a.head_dim == 128) return two ? launch_t<128, 2, F8>(a, s) : launch_t<128, 1, F8>(a, s);
-    return two ? launch_t<64, 2, F8>(a, s) : launch_t<64, 1, F8>(a, s);
+    if (a.head_dim == 128) return two ? launch_t<128, 2, F8, TOPK>(a, s) : launch_t<128, 1, F8, TOPK>(a, s);
+    return two ? launch_t<64, 2, F8, TOPK>(a, s) : launch_t<64, 1, F8, TOPK>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t s) {
     if (a.n_blocks <= 0) return hipSuccess;
-    return a.fp8 ? launch_dtype<true>(a, s) : launch_dtype<false>(a, s);
+    if (a.topk > 0) return a.fp8 ? launch_dtype<true, true>(a, s) : launch_dtype<false, true>(a, s);
+    return a.fp8 ? launch_dtype<true, false>(a, s) : launch_dtype<false, false>(a, s);
 }
 
 }  // namespace mla

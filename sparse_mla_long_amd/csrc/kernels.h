@@ -28,10 +28,31 @@ struct IndexerArgs {
     int32_t key_split;     // workgroups per query block, each over a contiguous range of key tiles
     int32_t n_blocks;      // key_split * sum over sequences of ceil(n_q(b) / queries per block)
     bool fp8;              // E4M3 queries and keys with scales
+    // Fused top-k (topk > 0): no scores are written. Each (query, key part)
+    // keeps a candidate list of (order key, j) entries in ascending j that
+    // holds every key able to reach the query's top k; cand_select_kernel
+    // then selects the top k over the parts' lists.
+    int32_t topk;
+    uint2 *cand;           // [total_q * key_split, cand_cap]
+    int32_t cand_cap;      // entries per list (>= 2 topk + kIdxKeyTile)
+    int32_t *cand_n;       // [total_q * key_split] final list lengths
 };
 constexpr int kIdxQueriesPerBlock = 8;
 constexpr int kIdxKeyTile = 256;          // keys per indexer LDS tile
+// Candidate list entries for top-k k: k kept after every compaction, room for
+// k more plus one key tile of appends before the next.
+constexpr int64_t cand_capacity(int64_t k) { return (2 * k + kIdxKeyTile + 63) / 64 * 64; }
 
+// Exact top-k selection over the key parts' candidate lists of each query.
+struct CandSelectArgs {
+    BatchDev batch;
+    const uint2 *cand;
+    const int32_t *cand_n;
+    int32_t cand_cap;
+    int32_t n_parts;
+    int32_t topk;
+    int32_t *indices;
+};
 struct TopkArgs {
     BatchDev batch;
     const float *scores;
@@ -75,6 +96,7 @@ struct MergeArgs {
 
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+hipError_t launch_cand_select(const CandSelectArgs &a, hipStream_t s);
 constexpr int32_t kTopkMaxRow = 1 << 19;   // longest score row top-k takes (its bitmaps sit in LDS)
 hipError_t launch_attention(const AttnArgs &a, bool fp8, hipStream_t s);
 // FP8 (E4M3) latent rows (launch_attention dispatches to it)

@@ -20,6 +20,7 @@
 // the histogram and the candidate list lives in LDS, and the kernel keeps to
 // 64 VGPRs, so several rows share a CU and hide each other's latency: the
 // kernel is bound by latency, not by its few instructions per key.
+#include "cand_select.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -47,8 +48,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __device__ __forceinline__ void hist_add(uint32_t *hist, bool pred, uint32_t d) {
     const uint64_t act = __ballot(pred);
     if (act == 0) return;
-    const int leader = __ffsll((unsigned long long)act) - 1;
-    const uint32_t d0 = __shfl(d, leader);
+    const int leader = __ffsll((unsigned long long)act) - 1;   // uniform: a lane read, no LDS
+    const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
     const uint64_t same = __ballot(pred && d == d0);
     if (lane_id() == leader) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
     if (pred && d != d0) atomicAdd(&hist[d], 1u);
@@ -375,7 +376,135 @@ void topk_kernel(TopkArgs a, int words) {
     }
 }
 
+// Exact selection of the fused indexer + top-k: one 256-thread workgroup per
+// query takes its parts' candidate lists in order (parts cover ascending key
+// ranges and each list is ascending, so their concatenation is too), finds
+// the k-th largest key T and how many entries equal to T to keep by an MSD
+// radix select with four 8-bit digits (one histogram bin per thread), then
+// writes, in list order, every entry above T and the first need_eq equal to
+// T. Rows with at most k keys keep them all.
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelUnroll = 8;
+
+__global__ __launch_bounds__(kSelThreads) void cand_select_kernel(CandSelectArgs a) {
+    __shared__ uint32_t hist[256];
+    __shared__ int s_w[kSelWaves];
+    __shared__ int s_sel[2];
+    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+    const int qi = a.batch.total_q - 1 - (int)blockIdx.x;
+    const int b = seq_of_row(a.batch.cu_q, a.batch.num_seqs, qi);
+    const int L = a.batch.cu_kv[b + 1] - a.batch.cu_kv[b];
+    const int pos = min(a.batch.q_pos[qi], L - 1);
+    const int k = a.topk;
+    int32_t *out = a.indices + (int64_t)qi * k;
+    if (pos + 1 <= k) {                                 // keep every earlier token
+        for (int e = tid; e < k; e += kSelThreads) out[e] = e <= pos ? e : -1;
+        return;
+    }
+    const uint2 *lists = a.cand + (int64_t)qi * a.n_parts * a.cand_cap;
+    const int32_t *counts = a.cand_n + (int64_t)qi * a.n_parts;
+    // every entry, kSelUnroll per thread and round, loads first
+    auto each = [&](auto f) {
+        for (int p = 0; p < a.n_parts; ++p) {
+            const uint2 *lp = lists + (int64_t)p * a.cand_cap;
+            const int n = counts[p];
+            for (int c = 0; c < n; c += kSelUnroll * kSelThreads) {
+                uint2 e[kSelUnroll];
+#pragma unroll
+                for (int u = 0; u < kSelUnroll; ++u) {
+                    const int i = c + u * kSelThreads + tid;
+                    e[u] = i < n ? lp[i] : make_uint2(0u, 0u);
+                }
+#pragma unroll
+                for (int u = 0; u < kSelUnroll; ++u) f(c + u * kSelThreads + tid < n, e[u]);
+            }
+        }
+    };
+    // ---- T: the k-th largest key; rem: entries equal to T in the top k
+    uint32_t prefix = 0u, pmask = 0u;
+    int rem = k;
+    for (int level = 0; level < 4; ++level) {
+        const int sh = 24 - 8 * level;
+        hist[tid] = 0u;
+        __syncthreads();
+        each([&](bool v, uint2 e) {
+            const uint32_t key = cand::key_of(e);
+            cand::hist_add(hist, v && (key & pmask) == prefix, (key >> sh) & 255u);
+        });
+        __syncthreads();
+        // bin tid: count above = entries in higher bins (a scan from the top)
+        const int h = (int)hist[255 - tid];               // thread t holds bin 255 - t
+        int inc = h;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int y = __shfl_up(inc, off);
+            if (lane >= off) inc += y;
+        }
+        if (lane == kWave - 1) s_w[wv] = inc;
+        __syncthreads();
+        int above = inc - h;
+        for (int w = 0; w < wv; ++w) above += s_w[w];
+        if (above < rem && rem <= above + h) {
+            s_sel[0] = 255 - tid;
+            s_sel[1] = above;
+        }
+        __syncthreads();
+        prefix |= (uint32_t)s_sel[0] << sh;
+        pmask |= 255u << sh;
+        rem -= s_sel[1];
+        __syncthreads();
+    }
+    const uint32_t T = prefix;
+    const int need_eq = rem;
+    // ---- ordered output, 256 entries per round: position = kept entries before it
+    int done = 0, eq_seen = 0;                           // block-uniform
+    for (int p = 0; p < a.n_parts; ++p) {
+        const uint2 *lp = lists + (int64_t)p * a.cand_cap;
+        const int n = counts[p];
+        for (int c = 0; c < n; c += kSelThreads) {
+            const int i = c + tid;
+            const uint2 e = i < n ? lp[i] : make_uint2(0u, 0u);
+            const uint32_t key = cand::key_of(e);
+            const bool gt = i < n && key > T, eq = i < n && key == T;
+            // ties: rank among the equal entries so far (in list order)
+            const uint64_t em = __ballot(eq);
+            if (lane == 0) {
+                s_w[wv] = __popcll(em);
+            }
+            __syncthreads();
+            int eq_before = eq_seen, eq_tot = 0;
+            for (int w = 0; w < kSelWaves; ++w) {
+                eq_before += w < wv ? s_w[w] : 0;
+                eq_tot += s_w[w];
+            }
+            eq_before += __popcll(em & ((1ull << lane) - 1ull));
+            const bool keep = gt || (eq && eq_before < need_eq);
+            const uint64_t km = __ballot(keep);
+            __syncthreads();
+            if (lane == 0) s_w[wv] = __popcll(km);
+            __syncthreads();
+            int at = done, kept_tot = 0;
+            for (int w = 0; w < kSelWaves; ++w) {
+                at += w < wv ? s_w[w] : 0;
+                kept_tot += s_w[w];
+            }
+            at += __popcll(km & ((1ull << lane) - 1ull));
+            if (keep && at < k) out[at] = (int32_t)e.y;
+            __syncthreads();
+            done += kept_tot;
+            eq_seen += eq_tot;
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_cand_select(const CandSelectArgs &a, hipStream_t s) {
+    if (a.batch.total_q <= 0) return hipSuccess;
+    hipLaunchKernelGGL(cand_select_kernel, dim3(a.batch.total_q), dim3(kSelThreads), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     if (a.batch.total_q <= 0) return hipSuccess;

@@ -228,6 +228,44 @@ def test_split_noalloc_argument_checks(lib):
     assert call(empty, out=None) == sm.MLA_OK
 
 
+def fused_call(lib, b, k=8, ws=FAKE * 16, ws_bytes=None, idx=FAKE, fp8=False, H=64, D=128):
+    if ws_bytes is None:
+        ws_bytes = lib.mla_topk_workspace_size(ctypes.byref(b), k)
+    if fp8:
+        return lib.mla_indexer_topk_fp8(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, FAKE, H, D, k, idx,
+                                        ws, ws_bytes, None)
+    return lib.mla_indexer_topk(ctypes.byref(b), FAKE, FAKE, FAKE, H, D, k, idx, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_indexer_topk_argument_checks(lib, fp8):
+    """mla_indexer_topk(_fp8) and mla_topk_workspace_size: k, the indices, the
+    workspace and the indexer's own checks, all on the host before any HIP call."""
+    b, keep = make_batch()
+    size = lib.mla_topk_workspace_size
+    # 4 queries, one key part (no device: one CU, so no key split): lists of
+    # cand_capacity(8) = 320 (key, j) entries, then the 4 list lengths
+    assert size(ctypes.byref(b), 8) == (4 * 320 * 8 + 255) // 256 * 256 + 4 * 4
+    assert size(ctypes.byref(b), 2048) == 4 * 4352 * 8 + 4 * 4
+    assert size(ctypes.byref(b), 0) == 0 and size(None, 8) == 0
+    bad, keep2 = make_batch(total_q=3)
+    assert size(ctypes.byref(bad), 8) == 0
+    assert fused_call(lib, b, fp8=fp8, k=0) == INVALID
+    assert fused_call(lib, b, fp8=fp8, k=-3, ws_bytes=1 << 20) == INVALID
+    assert fused_call(lib, b, fp8=fp8, k=4097, ws_bytes=1 << 30) == UNSUPPORTED
+    assert fused_call(lib, b, fp8=fp8, ws=None) == INVALID
+    assert fused_call(lib, b, fp8=fp8, ws=FAKE * 16 + 16) == INVALID       # not 256-byte aligned
+    assert fused_call(lib, b, fp8=fp8, ws_bytes=size(ctypes.byref(b), 8) - 1) == INVALID
+    assert b"mla_topk_workspace_size" in lib.mla_last_error()
+    assert fused_call(lib, b, fp8=fp8, idx=None) == INVALID
+    assert fused_call(lib, b, fp8=fp8, idx=FAKE + 2) == INVALID            # misaligned indices
+    assert fused_call(lib, b, fp8=fp8, H=65) == UNSUPPORTED                 # the indexer's checks
+    assert fused_call(lib, b, fp8=fp8, D=96) == UNSUPPORTED
+    assert fused_call(lib, bad, fp8=fp8, ws_bytes=1 << 20) == INVALID
+    empty, keep3 = make_batch(cu_q=(0, 0), cu_kv=(0, 10))
+    assert fused_call(lib, empty, fp8=fp8, ws=None, idx=None) == sm.MLA_OK
+
+
 def test_merge_argument_checks(lib):
     """mla_merge_attention validates on the host before any HIP call."""
     import ctypes

@@ -71,6 +71,22 @@ def test_counter_ingestion_scales_by_the_copy(tmp_path, monkeypatch):
     assert bench.measured_traffic("sparse32k", "fp8", "attention") == pytest.approx(a["bytes"])
     assert bench.measured_traffic("sparse32k", "bf16", "attention") is None
     assert bench.measured_traffic("sparse32k", "fp8", "indexer") is None
+    # fused path: the indexer and merge dispatches of a step add up
+    _write_csv(f_csv, [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 2 * 65536.0),
+                       ("mla::indexer_kernel<128, 2, false, true>(x)", "FETCH_SIZE", 100.0),
+                       ("mla::cand_merge_kernel(x)", "FETCH_SIZE", 8.0),
+                       ("mla::attn_f8_kernel<false>", "FETCH_SIZE", 1000.0)])
+    _write_csv(w_csv, [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 65536.0),
+                       ("mla::indexer_kernel<128, 2, false, true>(x)", "WRITE_SIZE", 4.0),
+                       ("mla::cand_merge_kernel(x)", "WRITE_SIZE", 2.0),
+                       ("mla::attn_f8_kernel<false>", "WRITE_SIZE", 10.0)])
+    rec = bench.ingest_counters(str(f_csv), str(w_csv), 64, "sparse32k", "fp8", "cmd", "bf16", "fused")
+    f = rec["kernels"]["indexer_topk"]
+    assert f["fetch_bytes"] == pytest.approx(108 * 1024 * 0.5)
+    assert f["write_bytes"] == pytest.approx(6 * 1024)
+    assert "indexer" not in rec["kernels"] and "topk" not in rec["kernels"]
+    assert bench.measured_traffic("sparse32k", "fp8", "indexer_topk", "bf16", "fused") == \
+        pytest.approx(f["bytes"])
     # a changed kernel source invalidates the stored figure
     table = json.load(open(bench.TRAFFIC_FILE))
     table["sparse32k/fp8"]["kernels"]["attention"]["source_hash"] = "stale"
@@ -98,6 +114,17 @@ def test_fp8_indexer_bytes_and_traffic_keys():
     assert bench.kernel_bytes(wl, "fp8")["attention"] == bench.kernel_bytes(wl, "fp8", "fp8")["attention"]
     assert bench.traffic_key("sparse32k", "fp8") == "sparse32k/fp8"
     assert bench.traffic_key("sparse32k", "fp8", "fp8") == "sparse32k/fp8/indexer-fp8"
+    assert bench.traffic_key("sparse32k", "fp8", "bf16", "fused") == "sparse32k/fp8/fused"
+
+
+def test_fused_path_bytes_and_traffic():
+    """The fused indexer + top-k moves the indexer's inputs and the indices,
+    not the score matrix; its traffic sums the indexer and merge dispatches
+    of a step and is stored under the fused key."""
+    wl = mla_inputs.WORKLOADS["sparse32k"]
+    pc = bench.pair_counts(wl)
+    b = bench.kernel_bytes(wl, "fp8")
+    assert b["indexer_topk"] == b["indexer"] - 4 * pc["causal"] + wl.total_q * wl.topk * 4
 
 
 def test_resume64_is_a_few_query_workload():

@@ -691,3 +691,143 @@ def test_dcp_key_shards_merge_to_full(sm, kv_dtype):
     rt = torch.as_tensor(rows, device="cuda")
     assert_close("dcp out vs oracle", m_o[rt].float().cpu().numpy(), r_out, tol, tol)
     assert_close("dcp lse vs oracle", m_l[rt].cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
+
+
+# ---------------------------------------------- fused indexer + top-k --
+def _fused_vs_unfused(sm, inp, label, oracle_rows=None):
+    """mla_indexer_topk(_fp8) against mla_topk_select on mla_indexer_score(_fp8)'s
+    scores for the same inputs: equal on every row, bit for bit (the fused
+    kernel computes the same scores with the same instructions and applies
+    the same selection rule). On oracle_rows, also the oracle's selection on
+    those GPU scores."""
+    wl = inp["workload"]
+    k = wl.topk
+    batch = sm.Batch.from_inputs(inp)
+    if inp.get("k_idx_scale") is not None:
+        args = (batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"], inp["k_idx_scale"], inp["w"])
+        sc = sm.indexer_score_fp8(*args)
+        fused = sm.indexer_topk_fp8(*args, k)
+    else:
+        args = (batch, inp["q_idx"], inp["k_idx"], inp["w"])
+        sc = sm.indexer_score(*args)
+        fused = sm.indexer_topk(*args, k)
+    ref = sm.topk_select(batch, sc, k)
+    torch.cuda.synchronize()
+    bad = (fused != ref).any(dim=1).nonzero().flatten()
+    assert bad.numel() == 0, "%s: fused top-k differs on %d rows, first %s" % (
+        label, bad.numel(), bad[:8].tolist())
+    say("[%s] fused indexer + top-k equals the unfused path on all %d rows" % (label, wl.total_q))
+    if oracle_rows is not None:
+        q_pos = inp["q_pos_host"]
+        rows = np.asarray(oracle_rows)
+        g_scores = [sc[int(r), : q_pos[r] + 1].cpu().numpy() for r in rows]
+        r_idx = oracle.topk_rows(g_scores, q_pos[rows], k)
+        got = fused[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+        assert np.array_equal(r_idx, got), label
+        say("[%s] fused indices equal the oracle's selection on the GPU scores of %d rows" %
+            (label, len(rows)))
+    return fused, sc
+
+
+@pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
+def test_fused_topk_tiny_and_ragged_all_rows(sm, idx_dtype):
+    """Tiny (k = 256 on 1,024 keys) and a ragged batch (an empty sequence, a
+    CP-style gap, a one-token sequence, rows shorter than k, k = 96): every
+    row against the unfused path and the oracle."""
+    wl = mla_inputs.WORKLOADS["tiny"]
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu", idx_dtype=idx_dtype))
+    _fused_vs_unfused(sm, inp, "fused-tiny-" + idx_dtype, np.arange(wl.total_q))
+    wl = mla_inputs.Workload("fused-ragged", (300, 0, 1000, 1, 130),
+                             (((0, 300),), (), ((0, 70), (930, 1000)), ((0, 1),), ((64, 130),)),
+                             n_heads=8, idx_heads=64, idx_dim=128, topk=96, kv_dtype="fp8", seed=101)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu", idx_dtype=idx_dtype))
+    _fused_vs_unfused(sm, inp, "fused-ragged-" + idx_dtype, np.arange(wl.total_q))
+
+
+def _indexer_only(nq, L, H, D, k, q, kI, w, q_lo):
+    """A one-sequence batch of nq queries at positions q_lo .. q_lo + nq - 1."""
+    wl = mla_inputs.Workload("fused-custom", (L,), (((q_lo, q_lo + nq),),), n_heads=8,
+                             idx_heads=H, idx_dim=D, topk=k, kv_dtype="bf16", seed=0)
+    return {"workload": wl, "q_idx": q.cuda(), "k_idx": kI.cuda(), "w": w.cuda(),
+            "cu_seqlens_q_host": wl.cu_seqlens_q(), "cu_seqlens_kv_host": wl.cu_seqlens_kv(),
+            "q_pos_host": wl.q_pos(), "q_pos": torch.from_numpy(wl.q_pos()).cuda(),
+            "q": torch.empty((nq, 1, 576), dtype=torch.bfloat16, device="cuda")}
+
+
+@pytest.mark.parametrize("kind", ["small_int", "all_zero", "rising", "falling"])
+def test_fused_topk_ties_and_order(sm, kind):
+    """Score patterns that stress the candidate list: small-integer inputs
+    (many exact ties), all scores zero (every key ties: the first k win),
+    scores rising with j in steps of 24 equal keys (every key beats the
+    threshold, so the list is compacted every few tiles, ties at each
+    compaction), and falling (nothing is appended after the first k)."""
+    g = torch.Generator().manual_seed(17)
+    nq, L, H, D, k = 64, 9000, 4, 64, 200
+    w = torch.randint(0, 3, (nq, H), generator=g).float()
+    if kind == "small_int":
+        q = torch.randint(-3, 4, (nq, H, D), generator=g).to(torch.bfloat16)
+        kI = torch.randint(-3, 4, (L, D), generator=g).to(torch.bfloat16)
+    elif kind == "all_zero":
+        q = torch.zeros((nq, H, D), dtype=torch.bfloat16)
+        kI = torch.randint(-3, 4, (L, D), generator=g).to(torch.bfloat16)
+    else:
+        q = torch.ones((nq, H, D), dtype=torch.bfloat16)
+        ramp = torch.arange(L) // 24 if kind == "rising" else (L - 1 - torch.arange(L)) // 24
+        kI = ramp[:, None].expand(L, D).to(torch.bfloat16)      # integers <= 374: exact in bf16
+        w = torch.ones((nq, H))
+    inp = _indexer_only(nq, L, H, D, k, q, kI, w, L - nq)
+    _fused_vs_unfused(sm, inp, "fused-" + kind, np.arange(nq))
+
+
+@pytest.mark.parametrize("k", [1, 4096])
+def test_fused_topk_k_limits(sm, k):
+    """k = 1 and the largest k (4,096) on rows of up to 20,000 keys, rows
+    around the keep-all boundary and p = 0."""
+    g = torch.Generator().manual_seed(k)
+    L, H, D = 20000, 8, 64
+    pos = np.array(sorted({0, max(k - 2, 0), max(k - 1, 0), k, k + 1, 9999, L - 2, L - 1}))
+    nq = len(pos)
+    q = torch.randn((nq, H, D), generator=g).to(torch.bfloat16)
+    kI = torch.randn((L, D), generator=g).to(torch.bfloat16)
+    w = torch.rand((nq, H), generator=g)
+    batch = sm.Batch([0, nq], [0, L], pos, "cuda")
+    sc = sm.indexer_score(batch, q.cuda(), kI.cuda(), w.cuda())
+    fused = sm.indexer_topk(batch, q.cuda(), kI.cuda(), w.cuda(), k)
+    ref = sm.topk_select(batch, sc, k)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, ref)
+    g_scores = [sc[i, : pos[i] + 1].cpu().numpy() for i in range(nq)]
+    assert np.array_equal(oracle.topk_rows(g_scores, pos, k), fused.cpu().numpy())
+
+
+@pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
+def test_fused_topk_key_split_merge(sm, idx_dtype):
+    """Few queries behind long prefixes (fewer eight-query blocks than twice
+    the CUs): every block's keys are split over many workgroups, each keeps
+    its own candidate list, and the merge kernel selects over their
+    concatenation. Every row against the unfused path and the oracle."""
+    wl = mla_inputs.Workload("fused-split", (30000, 5000), (((29970, 30000),), ((0, 3), (4990, 5000))),
+                             n_heads=8, idx_heads=64, idx_dim=128, topk=2048, kv_dtype="fp8", seed=103)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu", idx_dtype=idx_dtype))
+    batch = sm.Batch.from_inputs(inp)
+    need = sm.load_library().mla_topk_workspace_size(batch.c, wl.topk)
+    assert need > wl.total_q * 4352 * 8                 # more than one list per query: split
+    _fused_vs_unfused(sm, inp, "fused-split-" + idx_dtype, np.arange(wl.total_q))
+
+
+FUSED_FULL = [("sparse32k", "bf16"), ("cp131k", "bf16"), ("ragged", "bf16"), ("sparse32k", "fp8"),
+              ("ragged", "fp8"), ("resume64", "bf16")]
+
+
+@pytest.mark.parametrize("name,idx_dtype", FUSED_FULL)
+def test_fused_topk_full_size(sm, name, idx_dtype):
+    """The benchmark workloads: fused indices equal the unfused path's on
+    every row, and the oracle's selection on the GPU's scores on 64 sampled
+    rows (chunk edges, keep-all boundary, seeded picks)."""
+    wl = mla_inputs.WORKLOADS[name]
+    say("[fused %s/%s] generating inputs on the GPU" % (name, idx_dtype))
+    inp = mla_inputs.make_inputs(wl, "cuda", idx_dtype=idx_dtype)
+    rows = mla_inputs.sample_rows(wl, 64, per_seq=8)
+    _fused_vs_unfused(sm, inp, "fused-%s-%s" % (name, idx_dtype), rows)
+    del inp
+    torch.cuda.empty_cache()
