@@ -186,6 +186,41 @@ def fp8_kv(n_rows: int, seed: int, device="cpu", chunk_rows: int = 8192):
     return codes, sigma
 
 
+DS656_ROW = 656         # 512 E4M3 latent codes + 4 fp32 scales + 64 bf16 rope values
+
+
+def pack_ds656_rows(x: torch.Tensor) -> torch.Tensor:
+    """656-byte latent rows (a reading of FlashMLA's fp8_ds_mla row, which the
+    spke.com PCP/DCP article's footnote 1 names at 656 bytes per token) from
+    fp32 rows x [N, 576]: bytes 0..511 the E4M3 codes of the latent values,
+    each 128-value tile quantised with its own scale amax/448 (1 for an
+    all-zero tile, RNE, saturating); bytes 512..527 the four fp32 scales;
+    bytes 528..655 the 64 rope values rounded to bf16. uint8 [N, 656]."""
+    x = x.float()
+    n = x.shape[0]
+    lat = x[:, :D_LATENT].reshape(n, 4, 128)
+    amax = lat.abs().amax(dim=2)
+    sigma = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    codes = (lat / sigma[:, :, None]).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    rows = torch.empty((n, DS656_ROW), dtype=torch.uint8, device=x.device)
+    rows[:, :D_LATENT] = codes.view(torch.uint8).reshape(n, D_LATENT)
+    rows[:, D_LATENT:D_LATENT + 16] = sigma.contiguous().view(torch.uint8).reshape(n, 16)
+    rows[:, D_LATENT + 16:] = x[:, D_LATENT:].to(torch.bfloat16).contiguous().view(torch.uint8)
+    return rows
+
+
+def ds656_kv(n_rows: int, seed: int, device="cpu", chunk_rows: int = 8192) -> torch.Tensor:
+    """Latent KV rows: N(0,1) in fp32 (the same draw as fp8_kv and the bf16
+    rows), stored as 656-byte rows (pack_ds656_rows)."""
+    g = _gen(seed, T_KV, device)
+    rows = torch.empty((n_rows, DS656_ROW), dtype=torch.uint8, device=device)
+    for r in range(0, n_rows, chunk_rows):
+        n = min(chunk_rows, n_rows - r)
+        rows[r:r + n] = pack_ds656_rows(torch.randn((n, D_QK), generator=g, device=device,
+                                                    dtype=torch.float32))
+    return rows
+
+
 def quantize_e4m3_chunked(x: torch.Tensor, chunk_rows: int = 1 << 16):
     """quantize_e4m3_rows over the rows of x viewed as [-1, x.shape[-1]], in
     chunks (bounds the fp32 temporary). Returns (codes like x as uint8,
@@ -203,7 +238,8 @@ def make_inputs(wl: Workload, device="cpu", kv_dtype: Optional[str] = None,
     """All tensors of one workload on ``device``.
 
     q   [total_q, H, 576] bf16    absorbed query (512 latent + 64 rope)
-    kv  [total_kv, 576]   bf16, or uint8 E4M3 codes with kv_scale [total_kv] fp32
+    kv  [total_kv, 576]   bf16, or uint8 E4M3 codes with kv_scale [total_kv] fp32,
+                          or ("ds656") uint8 656-byte rows [total_kv, 656]
     q_idx [total_q, H_I, D_I] bf16, k_idx [total_kv, D_I] bf16, w [total_q, H_I] fp32
     (idx_dtype "fp8": q_idx and k_idx are the E4M3 codes of those same draws,
     one scale per (query, head) row in q_idx_scale [total_q, H_I] and per key
@@ -231,6 +267,9 @@ def make_inputs(wl: Workload, device="cpu", kv_dtype: Optional[str] = None,
         out["kv_scale"] = None
     elif kv_dtype == "fp8":
         out["kv"], out["kv_scale"] = fp8_kv(wl.total_kv, s, device)
+    elif kv_dtype == "ds656":
+        out["kv"] = ds656_kv(wl.total_kv, s, device)
+        out["kv_scale"] = None
     else:
         raise ValueError(kv_dtype)
     if with_indexer:

@@ -28,7 +28,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 _lock = threading.Lock()
 
-FMT_BF16, FMT_E4M3, FMT_F64 = 0, 1, 2
+FMT_BF16, FMT_E4M3, FMT_F64, FMT_DS656 = 0, 1, 2, 3
+DS656_ROW = 656
 QK_DIM, V_DIM = 576, 512
 
 
@@ -173,16 +174,18 @@ def attention_seq(q, kv, q_pos, sm_scale: float, kv_scale=None, indices=None,
                   q_fmt: int = FMT_BF16, kv_fmt: int = FMT_BF16):
     """Absorbed MLA attention of n queries of one sequence.
     q [n, H, 576] (uint16 bf16 bits, or float64 with q_fmt=FMT_F64);
-    kv [L, 576] (uint16 bf16 bits, uint8 e4m3 codes + kv_scale [L], or float64);
+    kv [L, 576] (uint16 bf16 bits, uint8 e4m3 codes + kv_scale [L], or float64),
+    or [L, 656] uint8 656-byte rows (kv_fmt=FMT_DS656: 512 E4M3 latent codes,
+    four fp32 scales of 128 values each, 64 bf16 rope values);
     indices [n, k] int32 or None (all earlier tokens).
     Returns (out [n, H, 512] float64, lse [n, H] float64)."""
-    dt = {FMT_BF16: np.uint16, FMT_E4M3: np.uint8, FMT_F64: np.float64}
+    dt = {FMT_BF16: np.uint16, FMT_E4M3: np.uint8, FMT_F64: np.float64, FMT_DS656: np.uint8}
     q = np.ascontiguousarray(q, dtype=dt[q_fmt])
     kv = np.ascontiguousarray(kv, dtype=dt[kv_fmt])
     q_pos = np.ascontiguousarray(q_pos, dtype=np.int32)
     n, H, dq = q.shape
     L = kv.shape[0]
-    assert dq == QK_DIM and kv.shape[1] == QK_DIM
+    assert dq == QK_DIM and kv.shape[1] == (DS656_ROW if kv_fmt == FMT_DS656 else QK_DIM)
     if kv_fmt == FMT_E4M3:
         kv_scale = np.ascontiguousarray(kv_scale, dtype=np.float32)
         assert kv_scale.shape == (L,)
@@ -286,6 +289,7 @@ def attention_rows(batch: dict, rows: Sequence[int], indices=None, sm_scale=None
     q = _take_rows(batch["q"], rows)
     kv = as_numpy(batch["kv"])
     fp8 = batch["kv_dtype"] == "fp8"
+    ds656 = batch["kv_dtype"] == "ds656"
     scale = as_numpy(batch["kv_scale"]) if fp8 else None
     seq = _seq_of_rows(cu_q, rows)
     H = q.shape[1]
@@ -298,7 +302,7 @@ def attention_rows(batch: dict, rows: Sequence[int], indices=None, sm_scale=None
         o, l = attention_seq(q[sel], kv[lo:hi], q_pos[r], sm_scale,
                              kv_scale=None if scale is None else scale[lo:hi],
                              indices=None if indices is None else np.asarray(indices)[sel],
-                             kv_fmt=FMT_E4M3 if fp8 else FMT_BF16)
+                             kv_fmt=FMT_E4M3 if fp8 else FMT_DS656 if ds656 else FMT_BF16)
         out[sel], lse[sel] = o, l
     return out, lse
 

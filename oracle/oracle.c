@@ -34,6 +34,12 @@
  * Decoders: bf16 = the 16 bits placed in the top half of an fp32.
  * OCP E4M3 (e4m3fn): byte s.eeee.mmm; e = 0 -> (-1)^s 2^-6 m/8; otherwise
  * (-1)^s 2^(e-7) (1 + m/8); e = 15 and m = 7 is NaN; no infinities.
+ * 656-byte latent row (article, footnote 1: 656 bytes of FP8 KV per token in
+ * FlashMLA's fp8_ds_mla format; the layout is this reading of it): bytes
+ * 0..511 the E4M3 codes of the 512 latent values, bytes 512..527 four
+ * little-endian fp32 scales (scale t covers latent values 128t .. 128t+127),
+ * bytes 528..655 the 64 rope values in bf16. Value d < 512 decodes as
+ * e4m3(code d) * scale[d / 128]; value 512 + r as bf16(rope r).
  */
 #include <math.h>
 #include <omp.h>
@@ -44,7 +50,8 @@
 #define QK_DIM 576
 #define V_DIM 512
 
-enum { FMT_BF16 = 0, FMT_E4M3 = 1, FMT_F64 = 2 };
+enum { FMT_BF16 = 0, FMT_E4M3 = 1, FMT_F64 = 2, FMT_DS656 = 3 };
+#define DS656_ROW 656
 
 /* Threads an OpenMP loop of the oracle uses (OMP_NUM_THREADS, else the cores). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
@@ -74,6 +81,17 @@ static double load_elem(int fmt, const void *base, int64_t row_elems, int64_t r,
     case FMT_BF16: return oracle_bf16_decode(((const uint16_t *)base)[r * row_elems + d]);
     case FMT_E4M3:
         return oracle_e4m3_decode(((const uint8_t *)base)[r * row_elems + d]) * (double)scale[r];
+    case FMT_DS656: {                 /* rows of DS656_ROW bytes; row_elems unused */
+        const uint8_t *row = (const uint8_t *)base + r * DS656_ROW;
+        if (d < V_DIM) {
+            float sc;
+            memcpy(&sc, row + V_DIM + 4 * (d / 128), sizeof sc);
+            return oracle_e4m3_decode(row[d]) * (double)sc;
+        }
+        uint16_t h;
+        memcpy(&h, row + V_DIM + 16 + 2 * (d - V_DIM), sizeof h);
+        return oracle_bf16_decode(h);
+    }
     default: return ((const double *)base)[r * row_elems + d];
     }
 }
@@ -179,7 +197,7 @@ void oracle_topk(int64_t n, const float *scores, int64_t ld, const int32_t *q_po
 
 /* ---- 3. absorbed MLA attention ---------------------------------------- */
 /* q [n, n_heads, 576] (bf16 or f64); kv [L, 576] (bf16, e4m3 + kv_scale[L], or
- * f64) for one sequence; indices [n, k] local rows (entries < 0 or > q_pos[i]
+ * f64), or [L, 656] bytes of 656-byte rows (FMT_DS656), for one sequence; indices [n, k] local rows (entries < 0 or > q_pos[i]
  * are skipped), or NULL for all j <= q_pos[i]; out [n, n_heads, 512] f64,
  * lse [n, n_heads] f64 (natural log).  An empty set gives O = 0, LSE = -inf. */
 void oracle_attention(int64_t n, int64_t n_heads, int64_t L, int q_fmt, const void *q,

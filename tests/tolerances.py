@@ -14,14 +14,24 @@ element test, so a gate cannot be loosened in one place only.
   row sum is fp32, and the log is fp32. The bound keeps a 10x margin over
   that and still rejects a query that loses one 32-key block of a
   2,048-key list (which moves its LSE by about 0.016 on average).
+* 656-byte rows (512 E4M3 latent codes with four fp32 tile scales, bf16
+  rope): the GPU path decodes each row to bf16, bf16(code * scale), as the
+  fp8_ds_mla decoder does, and attends over the bf16 rows; the oracle decodes
+  exactly. That rounding (up to 2^-9 of each latent value) moves a logit by
+  about 2.6e-3 (one standard deviation: 1/sqrt(192) times the rounding of
+  512 products), and the LSE by as much where one key dominates, so this
+  layout's LSE gate is 2e-2 + 1e-4 |r|, about 7.5 standard deviations; a
+  dropped 32-key block still moves the LSE past it on a good fraction of the
+  (query, head) pairs. Its outputs take the FP8-KV tolerance.
 * Indexer scores: |g - r| <= 1e-3 |r| + 1e-4 (fp32 sums of exact products).
 """
 from __future__ import annotations
 
 import numpy as np
 
-OUT_TOL = {"bf16": 2e-2, "fp8": 6e-2}
+OUT_TOL = {"bf16": 2e-2, "fp8": 6e-2, "ds656": 6e-2}
 LSE_ATOL, LSE_RTOL = 1e-3, 1e-4
+LSE_TOL = {"bf16": (LSE_ATOL, LSE_RTOL), "fp8": (LSE_ATOL, LSE_RTOL), "ds656": (2e-2, 1e-4)}
 IDX_ATOL, IDX_RTOL = 1e-4, 1e-3
 
 
@@ -63,7 +73,7 @@ def assert_attention(name, kv_dtype, out, lse, r_out, r_lse, say=None):
     """O at the KV type's output tolerance, LSE at the fp32 bound."""
     tol = OUT_TOL[kv_dtype]
     assert_close(name + " out", out, r_out, tol, tol)
-    assert_close(name + " lse", lse, r_lse, LSE_ATOL, LSE_RTOL)
+    assert_close(name + " lse", lse, r_lse, *LSE_TOL[kv_dtype])
     if say is not None:
         say("[%s] max |out err| %.3g, max |lse err| %.3g" % (name, max_err(out, r_out),
                                                             max_err(lse, r_lse)))
