@@ -26,6 +26,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 D_QK, D_V = 576, 512
+DS656_ROW = 656
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}     # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -73,9 +74,11 @@ def kernel_bytes(wl, kv_dtype: str, idx_dtype: str = "bf16") -> dict:
     outputs written once; gathered rows counted per selected pair). FP8
     indexer inputs are 1-byte codes plus an fp32 scale per row."""
     pc = pair_counts(wl)
-    row = D_QK + 4 if kv_dtype == "fp8" else 2 * D_QK
+    row = D_QK + 4 if kv_dtype == "fp8" else 2 * D_QK      # 656-byte rows: attention reads bf16
     q_bytes = wl.total_q * wl.n_heads * (2 * D_QK + 2 * D_V + 4)
     out = {"attention": pc["selected"] * (row + (0 if wl.dense else 4)) + q_bytes}
+    if kv_dtype == "ds656":
+        out["kv_decode"] = wl.total_kv * (DS656_ROW + 2 * D_QK)
     if not wl.dense:
         if idx_dtype == "fp8":
             out["indexer"] = pc["causal"] * 4 + wl.total_q * wl.idx_heads * (wl.idx_dim + 8) \
@@ -98,10 +101,13 @@ def kernel_bytes(wl, kv_dtype: str, idx_dtype: str = "bf16") -> dict:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"attention": ("attention.hip", "attention_f8.hip", "attn_common.h"),
                   "indexer": ("indexer.hip", "attn_common.h", "cand_select.h"), "topk": ("topk.hip",),
-                  "indexer_topk": ("indexer.hip", "attn_common.h", "cand_select.h", "topk.hip")}
+                  "indexer_topk": ("indexer.hip", "attn_common.h", "cand_select.h", "topk.hip"),
+                  "kv_decode": ("decode_ds656.hip",)}
 KERNEL_SYMBOLS = {"attention": ("attn_kernel", "attn_f8_kernel"), "indexer": ("indexer_kernel",),
-                  "topk": ("topk_kernel",), "indexer_topk": ("indexer_kernel", "cand_merge_kernel")}
-PATH_KERNELS = {"fused": ("indexer_topk", "attention"), "unfused": ("indexer", "topk", "attention")}
+                  "topk": ("topk_kernel",), "indexer_topk": ("indexer_kernel", "cand_select_kernel"),
+                  "kv_decode": ("ds656_decode_kernel",)}
+PATH_KERNELS = {"fused": ("indexer_topk", "kv_decode", "attention"),
+                "unfused": ("indexer", "topk", "kv_decode", "attention")}
 COPY_SYMBOL = "copyBuffer"
 
 
@@ -199,8 +205,12 @@ def path_dtype(kv_dtype: str, idx_dtype: str, dense: bool) -> tuple:
     """Arithmetic types of the path: (short label, description)."""
     attn = ("e4m3 MFMA (Q and P*sigma as exact / 8-bit hi+lo E4M3 pairs: bf16 precision), "
             "fp32 accumulate" if kv_dtype == "fp8" else "bf16 MFMA, fp32 accumulate")
+    if kv_dtype == "ds656":
+        attn += ", on rows decoded from 656-byte E4M3 rows (bf16(code * tile scale))"
     parts = {"attention": attn}
     kinds = {"e4m3" if kv_dtype == "fp8" else "bf16"}
+    if kv_dtype == "ds656":
+        kinds.add("e4m3")
     if not dense:
         parts["indexer"] = ("e4m3 MFMA on E4M3 codes with fp32 scales" if idx_dtype == "fp8"
                             else "bf16 MFMA") + ", fp32 accumulate"
@@ -257,7 +267,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sparse32k")
-    ap.add_argument("--kv-dtype", default=None, help="override the workload's KV dtype (bf16/fp8)")
+    ap.add_argument("--kv-dtype", default=None,
+                    help="override the workload's KV dtype: bf16, fp8 (576 E4M3 + one scale per "
+                         "row) or ds656 (656-byte rows, decoded to bf16 before attention)")
     ap.add_argument("--split", type=int, default=None,
                     help="attention through mla_sparse_prefill_split with this many parts per "
                          "query (0: chosen from the CU count)")
@@ -320,6 +332,10 @@ def main():
     lse = torch.empty((wl.total_q, wl.n_heads), dtype=torch.float32, device=dev)
     names = (["attention"] if wl.dense else ["indexer_topk", "attention"] if fused
              else ["indexer", "topk", "attention"])
+    kv_bf16 = None
+    if kv_dtype == "ds656":
+        names.insert(len(names) - 1, "kv_decode")
+        kv_bf16 = torch.empty((wl.total_kv, D_QK), dtype=torch.bfloat16, device=dev)
     split_ws = None
     if args.split is not None:
         need = sm.load_library().mla_sparse_prefill_split_workspace_size(wl.total_q, wl.n_heads,
@@ -330,11 +346,20 @@ def main():
         def mark(i):
             if ev is not None:
                 ev[i].record()
+        def attend(idx, at):
+            kv = inp["kv"]
+            if kv_bf16 is not None:
+                sm.kv_decode_ds656(inp["kv"], out=kv_bf16)
+                mark(at)
+                at += 1
+                kv = kv_bf16
+            sm.sparse_prefill(batch, inp["q"], kv, inp["kv_scale"], idx, wl.sm_scale,
+                              out=out, lse=lse, n_split=args.split, workspace=split_ws)
+            mark(at)
+
         if wl.dense:
             mark(0)
-            sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], None, wl.sm_scale,
-                              out=out, lse=lse, n_split=args.split, workspace=split_ws)
-            mark(1)
+            attend(None, 1)
             return
         mark(0)
         if fused:
@@ -355,9 +380,7 @@ def main():
             mark(1)
             sm.topk_select(batch, scores, wl.topk, indices=indices)
             mark(2)
-        sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], indices, wl.sm_scale,
-                          out=out, lse=lse, n_split=args.split, workspace=split_ws)
-        mark(len(names))
+        attend(indices, 2 if fused else 3)
 
     if args.copy_calibration_mib > 0:
         src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
@@ -454,7 +477,7 @@ def main():
     ms_step = elapsed / args.steps * 1e3
     dtype_label, dtype_detail = path_dtype(kv_dtype, idx_dtype, wl.dense)
     t_kernels = sum(per_kernel_ms.values()) * 1e-3
-    p_attn = PEAK_TFLOPS["fp8" if kv_dtype == "fp8" else "bf16"]
+    p_attn = PEAK_TFLOPS["fp8" if kv_dtype in ("fp8", "ds656") else "bf16"]
     mfma_frac = (fl["indexer"] / (PEAK_TFLOPS[idx_dtype] * 1e12) +
                  fl["attention"] / (p_attn * 1e12)) / (ms_step * 1e-3)
     res = {

@@ -27,6 +27,8 @@
  *                       their log-sum-exp.
  *   mla_sparse_prefill_split  split-KV attention: each query's keys in up to
  *                       16 parts run as separate work items, then merged.
+ *   mla_kv_decode_ds656 decodes 656-byte latent rows (E4M3 with four tile
+ *                       scales, bf16 rope) to the bf16 rows attention reads.
  *
  * Batches are packed: sequence b owns query rows [cu_q[b], cu_q[b+1]) and
  * latent-KV rows [cu_kv[b], cu_kv[b+1]); every query carries its true
@@ -280,6 +282,31 @@ mla_status_t mla_sparse_prefill_split_noalloc(const mla_batch_t *batch, const vo
                                               int64_t kv_scale_stride, const int32_t *indices,
                                               int32_t k, int32_t n_heads, float sm_scale,
                                               int32_t n_split, void *out, float *lse, void *stream);
+
+/* The 656-byte latent row (spke.com article, footnote 1: 656 bytes of FP8 KV
+ * per token, in FlashMLA's fp8_ds_mla format; this library reads it as):
+ *   bytes   0..511  E4M3 codes of the 512 latent values
+ *   bytes 512..527  four little-endian fp32 scales; scale t covers latent
+ *                   values 128t .. 128t+127
+ *   bytes 528..655  the 64 rope values, bf16
+ * Latent value d is e4m3(code d) * scale[d / 128]; rope value r is bf16. */
+#define MLA_DS656_ROW_BYTES 656
+
+/* Decodes n_rows 656-byte rows into the 576 bf16 values of a latent row that
+ * mla_sparse_prefill reads with MLA_KV_BF16: latent value d becomes
+ * bf16(fp32(e4m3(code) * scale)) (each rounding to nearest even), the rope
+ * values are copied. Attention over 656-byte rows is this call followed by
+ * the attention call on its output; decoding the product to bf16 before the
+ * contraction is what the fp8_ds_mla decoder does (up to 2^-9 of each latent
+ * value).
+ *   kv_ds656   device, row r at byte offset r * row_stride, 16-byte aligned
+ *   row_stride bytes between rows: >= 656 and a multiple of 16
+ *   kv_bf16    device [n_rows, 576] bf16, 16-byte aligned, owned by the caller
+ * Errors: MLA_ERR_INVALID_ARG (nothing enqueued) for n_rows < 0, a bad
+ * stride, a NULL or misaligned pointer. Codes 0x7f / 0xff (NaN) decode to
+ * NaN. */
+mla_status_t mla_kv_decode_ds656(const void *kv_ds656, int64_t row_stride, int64_t n_rows,
+                                 void *kv_bf16, void *stream);
 
 /* Merge of attention results over disjoint key sets by their log-sum-exp
  * (spke.com article, section "DCP": every GPU attends over its share of the

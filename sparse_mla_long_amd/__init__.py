@@ -10,6 +10,7 @@ Calls (same names as the C ABI, without the ``mla_`` prefix):
   indexer_score(batch, q_idx, k_idx, w, ...)   -> scores [total_q, ld] fp32
   indexer_score_fp8(batch, q_idx, q_scale, k_idx, k_scale, w, ...)
                                                -> scores from E4M3 codes with scales
+  kv_decode_ds656(kv)                          -> bf16 rows from 656-byte latent rows
   topk_select(batch, scores, k, ...)           -> indices [total_q, k] int32
   indexer_topk(batch, q_idx, k_idx, w, k, ...) -> indices, without the score matrix
   indexer_topk_fp8(batch, q_idx, q_scale, k_idx, k_scale, w, k, ...)
@@ -45,7 +46,7 @@ class MlaBatch(ctypes.Structure):
 EXPORTS = ("mla_indexer_score", "mla_indexer_score_fp8", "mla_topk_select", "mla_sparse_prefill",
            "mla_sparse_prefill_split", "mla_sparse_prefill_split_workspace_size",
            "mla_sparse_prefill_split_noalloc", "mla_topk_workspace_size", "mla_indexer_topk",
-           "mla_indexer_topk_fp8",
+           "mla_indexer_topk_fp8", "mla_kv_decode_ds656",
            "mla_merge_attention", "mla_status_string", "mla_last_error", "mla_abi_version")
 
 _lib = None
@@ -64,6 +65,7 @@ def load_library(path: str = LIB_PATH):
     L.mla_indexer_score.argtypes = [BP, P, P, P, I32, I32, P, I64, P]
     L.mla_indexer_score_fp8.argtypes = [BP, P, P, P, P, P, I32, I32, P, I64, P]
     L.mla_topk_select.argtypes = [BP, P, I64, I32, P, P]
+    L.mla_kv_decode_ds656.argtypes = [P, I64, I64, P, P]
     L.mla_topk_workspace_size.argtypes = [BP, I32]
     L.mla_topk_workspace_size.restype = ctypes.c_size_t
     L.mla_indexer_topk.argtypes = [BP, P, P, P, I32, I32, I32, P, P, ctypes.c_size_t, P]
@@ -79,7 +81,7 @@ def load_library(path: str = LIB_PATH):
     L.mla_merge_attention.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                       I32, I32, I32, P, P, P]
     for f in ("mla_indexer_score", "mla_indexer_score_fp8", "mla_topk_select", "mla_indexer_topk",
-              "mla_indexer_topk_fp8", "mla_sparse_prefill",
+              "mla_indexer_topk_fp8", "mla_kv_decode_ds656", "mla_sparse_prefill",
               "mla_sparse_prefill_split", "mla_sparse_prefill_split_noalloc", "mla_merge_attention"):
         getattr(L, f).restype = ctypes.c_int
     L.mla_status_string.argtypes = [ctypes.c_int]
@@ -220,6 +222,24 @@ def topk_select(batch: Batch, scores: torch.Tensor, k: int,
     _check(load_library().mla_topk_select(batch.c, _ptr(scores), scores.shape[1], int(k),
                                           _ptr(indices), _stream(scores)))
     return indices
+
+
+DS656_ROW = 656
+
+
+def kv_decode_ds656(kv: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mla_kv_decode_ds656: 656-byte latent rows (uint8 [n, 656], or a
+    row-strided uint8 view of wider rows) -> bf16 [n, 576]."""
+    if kv.dtype != torch.uint8 or kv.dim() != 2 or kv.shape[1] < DS656_ROW or kv.stride(1) != 1:
+        raise ValueError("kv must be uint8 [n, >= 656] with contiguous rows")
+    n = kv.shape[0]
+    if out is None:
+        out = torch.empty((n, QK_DIM), dtype=torch.bfloat16, device=kv.device)
+    else:
+        _need(out, "out", torch.bfloat16, kv.device, (n, QK_DIM))
+    _check(load_library().mla_kv_decode_ds656(_ptr(kv), int(kv.stride(0)), int(n), _ptr(out),
+                                              _stream(kv)))
+    return out
 
 
 def topk_workspace(batch: Batch, k: int) -> torch.Tensor:

@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla_sparse.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attention.hip", "attention_f8.hip", "merge.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attention.hip", "attention_f8.hip", "merge.hip",
+           "decode_ds656.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -498,6 +498,22 @@ mla_status_t mla_merge_attention(const void *const *o_parts, const float *const 
     return hip_status(mla::launch_merge(a, (hipStream_t)stream), "merge launch");
 }
 
+mla_status_t mla_kv_decode_ds656(const void *kv_ds656, int64_t row_stride, int64_t n_rows,
+                                 void *kv_bf16, void *stream) {
+    if (n_rows < 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be >= 0 (got %lld)", (long long)n_rows);
+    if (row_stride < MLA_DS656_ROW_BYTES || row_stride % 16 != 0)
+        return fail(MLA_ERR_INVALID_ARG, "row_stride %lld must be >= %d and a multiple of 16",
+                    (long long)row_stride, MLA_DS656_ROW_BYTES);
+    if (n_rows == 0) return ok();
+    if (!kv_ds656 || !kv_bf16) return fail(MLA_ERR_INVALID_ARG, "kv_ds656 / kv_bf16 is NULL");
+    if (!aligned(kv_ds656, 16) || !aligned(kv_bf16, 16))
+        return fail(MLA_ERR_INVALID_ARG, "kv_ds656 and kv_bf16 must be 16-byte aligned");
+    if (n_rows > (int64_t)INT32_MAX * 8)
+        return fail(MLA_ERR_UNSUPPORTED, "n_rows %lld too large", (long long)n_rows);
+    mla::Ds656Args a{(const uint8_t *)kv_ds656, row_stride, n_rows, (uint8_t *)kv_bf16};
+    return hip_status(mla::launch_ds656_decode(a, (hipStream_t)stream), "row decode launch");
+}
+
 const char *mla_status_string(mla_status_t s) {
     switch (s) {
     case MLA_OK: return "MLA_OK";

@@ -94,6 +94,16 @@ struct MergeArgs {
     float *lse_out;                         // [rows]
 };
 
+// Decode of 656-byte latent rows (512 E4M3 codes, four fp32 tile scales, 64
+// bf16 rope values) to bf16 rows of 576 values.
+struct Ds656Args {
+    const uint8_t *in;     // row r at in + r * in_stride
+    int64_t in_stride;
+    int64_t n_rows;
+    uint8_t *out;          // [n_rows, 576] bf16
+};
+hipError_t launch_ds656_decode(const Ds656Args &a, hipStream_t s);
+
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_cand_select(const CandSelectArgs &a, hipStream_t s);

@@ -266,6 +266,19 @@ def test_indexer_topk_argument_checks(lib, fp8):
     assert fused_call(lib, empty, fp8=fp8, ws=None, idx=None) == sm.MLA_OK
 
 
+def test_kv_decode_ds656_argument_checks(lib):
+    """mla_kv_decode_ds656 validates on the host before any HIP call."""
+    call = lib.mla_kv_decode_ds656
+    assert call(FAKE, 656, -1, FAKE, None) == INVALID
+    assert call(FAKE, 640, 4, FAKE, None) == INVALID            # shorter than a row
+    assert call(FAKE, 664, 4, FAKE, None) == INVALID            # not a multiple of 16
+    assert call(None, 656, 4, FAKE, None) == INVALID
+    assert call(FAKE, 656, 4, None, None) == INVALID
+    assert call(FAKE + 8, 656, 4, FAKE, None) == INVALID        # misaligned
+    assert call(FAKE, 656, 4, FAKE + 8, None) == INVALID
+    assert call(None, 656, 0, None, None) == sm.MLA_OK          # nothing to do
+
+
 def test_merge_argument_checks(lib):
     """mla_merge_attention validates on the host before any HIP call."""
     import ctypes

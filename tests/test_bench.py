@@ -74,11 +74,11 @@ def test_counter_ingestion_scales_by_the_copy(tmp_path, monkeypatch):
     # fused path: the indexer and merge dispatches of a step add up
     _write_csv(f_csv, [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 2 * 65536.0),
                        ("mla::indexer_kernel<128, 2, false, true>(x)", "FETCH_SIZE", 100.0),
-                       ("mla::cand_merge_kernel(x)", "FETCH_SIZE", 8.0),
+                       ("mla::cand_select_kernel(x)", "FETCH_SIZE", 8.0),
                        ("mla::attn_f8_kernel<false>", "FETCH_SIZE", 1000.0)])
     _write_csv(w_csv, [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 65536.0),
                        ("mla::indexer_kernel<128, 2, false, true>(x)", "WRITE_SIZE", 4.0),
-                       ("mla::cand_merge_kernel(x)", "WRITE_SIZE", 2.0),
+                       ("mla::cand_select_kernel(x)", "WRITE_SIZE", 2.0),
                        ("mla::attn_f8_kernel<false>", "WRITE_SIZE", 10.0)])
     rec = bench.ingest_counters(str(f_csv), str(w_csv), 64, "sparse32k", "fp8", "cmd", "bf16", "fused")
     f = rec["kernels"]["indexer_topk"]

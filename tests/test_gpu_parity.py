@@ -72,7 +72,8 @@ def fp8_score_magnitude(inp, rows):
 
 
 def run_path(sm, batch, inp):
-    """indexer (bf16 or FP8 inputs) -> top-k -> sparse attention on the GPU."""
+    """indexer (bf16 or FP8 inputs) -> top-k -> sparse attention on the GPU
+    (656-byte rows: decoded to bf16 rows first, then attended)."""
     wl = inp["workload"]
     if inp.get("k_idx_scale") is not None:
         scores = sm.indexer_score_fp8(batch, inp["q_idx"], inp["q_idx_scale"], inp["k_idx"],
@@ -80,7 +81,8 @@ def run_path(sm, batch, inp):
     else:
         scores = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
     idx = sm.topk_select(batch, scores, wl.topk)
-    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale)
+    kv = sm.kv_decode_ds656(inp["kv"]) if inp["kv_dtype"] == "ds656" else inp["kv"]
+    out, lse = sm.sparse_prefill(batch, inp["q"], kv, inp["kv_scale"], idx, wl.sm_scale)
     return out, lse, idx, scores
 
 
@@ -404,7 +406,7 @@ def test_inline_scale_row_layout(sm):
 # ------------------------------------------------------- full-size workloads --
 FULL = [("sparse32k", "fp8", "bf16"), ("sparse32k", "bf16", "bf16"), ("dense16k", "bf16", "bf16"),
         ("cp131k", "fp8", "bf16"), ("ragged", "fp8", "bf16"), ("sparse32k", "fp8", "fp8"),
-        ("ragged", "fp8", "fp8")]
+        ("ragged", "fp8", "fp8"), ("sparse32k", "ds656", "bf16")]
 
 
 @pytest.mark.parametrize("name,kv_dtype,idx_dtype", FULL)
@@ -831,3 +833,43 @@ def test_fused_topk_full_size(sm, name, idx_dtype):
     _fused_vs_unfused(sm, inp, "fused-%s-%s" % (name, idx_dtype), rows)
     del inp
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------ 656-byte latent rows --
+def test_ds656_decode_bit_exact(sm):
+    """mla_kv_decode_ds656 against torch's own float8 decode, fp32 multiply
+    and bf16 cast (each rounding to nearest even) on rows with tiles of very
+    different ranges, an all-zero tile, and a 672-byte row stride."""
+    g = torch.Generator().manual_seed(31)
+    n = 3001
+    x = torch.randn((n, 576), generator=g)
+    x[:, 128:256] *= 300.0
+    x[:, 384:512] *= 1e-3
+    x[7, :128] = 0.0
+    rows = mla_inputs.pack_ds656_rows(x)
+    wide = torch.zeros((n, 672), dtype=torch.uint8)
+    wide[:, :656] = rows
+    got = sm.kv_decode_ds656(wide.cuda()[:, :656])
+    codes = rows[:, :512].contiguous().view(torch.float8_e4m3fn).float().reshape(n, 4, 128)
+    scales = rows[:, 512:528].contiguous().view(torch.float32)
+    latent = (codes * scales[:, :, None]).reshape(n, 512).to(torch.bfloat16)
+    rope = rows[:, 528:656].contiguous().view(torch.bfloat16)
+    ref = torch.cat([latent, rope], dim=1)
+    torch.cuda.synchronize()
+    assert torch.equal(got.cpu().view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged-small"])
+def test_ds656_path_all_rows(sm, name):
+    """The whole path on 656-byte rows (indexer -> top-k -> decode -> bf16
+    attention), every row against the oracle's exact decode of the same
+    bytes, at the 656-byte row gates."""
+    if name == "tiny":
+        wl = mla_inputs.WORKLOADS["tiny"].scaled(n_heads=64)
+    else:
+        wl = mla_inputs.Workload("ds656-ragged", (300, 0, 1000, 1, 130),
+                                 (((0, 300),), (), ((0, 70), (930, 1000)), ((0, 1),), ((64, 130),)),
+                                 n_heads=64, idx_heads=64, idx_dim=128, topk=96, kv_dtype="ds656",
+                                 seed=33)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu", kv_dtype="ds656"))
+    check_path(sm, inp, np.arange(wl.total_q), "ds656-" + name)
