@@ -29,10 +29,13 @@ IMPLICIT_M0 = ("s_movrel", "v_movrel", "s_sendmsg", "ds_gws", "ds_append", "ds_c
 
 
 def _asm(src, tmp_path):
+    """The source's gfx950 assembly, compiled with the library's own flags."""
+    import sys
+    sys.path.insert(0, ROOT)
+    from sparse_mla_long_amd import build
     out = tmp_path / (os.path.basename(src) + ".s")
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
-                    "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                    "--cuda-device-only", "-S", src, "-o", str(out)],
+    flags = [f for f in build.compile_flags(os.path.basename(src)) if f != "-fPIC"]
+    subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", str(out)],
                    check=True, capture_output=True, text=True)
     return out.read_text().split("\n")
 
