@@ -459,17 +459,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             }
             return v;
         };
-        auto pv = [&](const uint8_t *kstep, int par, auto &&issue) {
-            // B: block 0's weights in bytes 0..15, block 1's in 16..31 (QK
-            // waves hg and hg + 2); lane half g carries block g's scale
+        // B operand of PV: block 0's weights in bytes 0..15, block 1's in
+        // 16..31 (QK waves hg and hg + 2); lane half g carries block g's scale
+        struct PvOps {
+            i32x8 ah, al, vn;
+            int sa;
+        };
+        auto pv_load = [&](const uint8_t *kstep, int par) -> PvOps {
             const u32x4 h0 = s_ph[par][hg][g][col], h1 = s_ph[par][hg + 2][g][col];
             const u32x4 l0 = s_pl[par][hg][g][col], l1 = s_pl[par][hg + 2][g][col];
-            const int sa = s_pe[par][hg + 2 * g][col];
-            const i32x8 ah = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3],
-                              (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-            const i32x8 al = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3],
-                              (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
-            i32x8 vn = v_ld(kstep, 0);
+            PvOps r;
+            r.sa = s_pe[par][hg + 2 * g][col];
+            r.ah = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+            r.al = i32x8{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+            r.vn = v_ld(kstep, 0);
+            return r;
+        };
+        auto pv = [&](const uint8_t *kstep, const PvOps &ops, auto &&issue) {
+            const i32x8 ah = ops.ah, al = ops.al;
+            const int sa = ops.sa;
+            i32x8 vn = ops.vn;
 #pragma unroll
             for (int nb = 0; nb < kOwn; ++nb) {
                 const i32x8 vb = vn;
@@ -555,30 +564,35 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                         const int sln = sl == kRingSteps - 1 ? 0 : sl + 1;    // step t + 1
                         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's gathers of step t landed
                         lds_barrier();       // step t everywhere; PV of t - 2 done; weights of t - 1 posted
+                        // QK waves: logit MFMAs of step t. PV waves: the rows of
+                        // this iteration's gathers, the PV operands of step t - 1,
+                        // then PV with one gather issued after each tile (two
+                        // after the first), so the gathers of step t + 1 spread
+                        // over the iteration.
                         f32x16 s = zero16();
+                        const bool keys = t + 1 < n_steps;       // gathers: key step t + 1, else the next Q
+                        const int qh_src = t + 1 - n_steps;
+                        int jn[kDmaStep];
+                        PvOps ops;
+                        auto issue_u = [&](int u) {
+                            if (keys) dma_go(kvq, sln, u, jn[u]);
+                            else if (q_next) q_one(qn_row, qh_src, sln, u);
+                        };
                         if constexpr (QK) {
                             if (t < n_steps) s = qk(ring + sl * kStepBytes + sub * kBlockBytes);
                         } else {
-                            // this iteration's gathers: rows read up front, one DMA
-                            // after each PV tile (two after the first)
-                            const bool keys = t + 1 < n_steps;
-                            const int qh_src = t + 1 - n_steps;
-                            int jn[kDmaStep];
                             if (keys) {
 #pragma unroll
                                 for (int u = 0; u < kDmaStep; ++u) jn[u] = dma_row(t + 1, u);
                             }
+                            if (t >= 1) ops = pv_load(ring + slp * kStepBytes, (t - 1) & 1);
                             auto issue = [&](int nb) {
 #pragma unroll
-                                for (int u = 0; u < kDmaStep; ++u) {
-                                    if (u == (nb == 0 ? 0 : nb + 1) || (nb == 0 && u == 1)) {
-                                        if (keys) dma_go(kvq, sln, u, jn[u]);
-                                        else if (q_next) q_one(qn_row, qh_src, sln, u);
-                                    }
-                                }
+                                for (int u = 0; u < kDmaStep; ++u)
+                                    if (nb == u * kOwn / kDmaStep) issue_u(u);
                             };
                             if (t >= 1) {
-                                pv(ring + slp * kStepBytes, (t - 1) & 1, issue);
+                                pv(ring + slp * kStepBytes, ops, issue);
                             } else {
 #pragma unroll
                                 for (int nb = 0; nb < kOwn; ++nb) issue(nb);
