@@ -127,7 +127,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     for (int u = 0; u < kDmaIns; ++u) {
         const int sidx = (wv + 4 * u) * 64 + lane;
         dma_r[u] = sidx / kChunks;
-        dma_lc[u] = 16 * ((sidx % kChunks) ^ swz<false>(dma_r[u]));
+        dma_lc[u] = 16 * ((sidx % kChunks) ^ bf16_swz(dma_r[u]));
     }
 
     // Softmax in base 2 against a reference max m_run per head. m_run is set
@@ -144,7 +144,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     f32x16 o[kVHalf / 32];
     // row this lane feeds into the QK A operand: accumulator row m = col
     const int qk_row = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
-    const int qk_swz = swz<false>(qk_row);
+    const int qk_swz = bf16_swz(qk_row);
     int parity = 0;
     auto voted = [&]() {                         // any wave's posted vote
         const int4 v = *(const int4 *)&s_vote[0];
@@ -181,7 +181,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         const uint8_t *vb0[2][2];
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
-            const int sw = (2 * v + (gi >> 3)) | (g << 2);
+            const int sw = v | (g << 1) | ((gi >> 3) << 2);    // bf16_swz of those rows
             const uint8_t *rb = kb + (16 * g + 4 * v + (gi >> 2)) * kRowBytes + 8 * (gi & 1);
             vb0[v][0] = rb + 16 * (L2 ^ sw);
             vb0[v][1] = rb + 16 * ((L2 + 4) ^ sw);

@@ -16,10 +16,17 @@ typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 *lds_bf16x4_ptr;
 typedef __attribute__((address_space(3))) v2i32 *lds_v2i32_ptr;
 
-// Chunk swizzle of LDS row r (XOR on the low chunk bits); rows 0..31 of a block.
-template <bool FP8> __device__ __forceinline__ int swz(int r) {
-    if (FP8) return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
-    return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
+// Chunk swizzle of a bf16 latent row in LDS (rows 0..31 of a block; the
+// 16-byte chunk c of row r sits at c ^ bf16_swz(r), within its group of 8).
+// A row is 1,152 bytes, so rows of equal parity start on the same bank and
+// the swizzle has to separate them: the QK reads (16 rows in 0..7 and 16..23,
+// one chunk each per 16-lane phase) need the 8 rows of each parity on 8
+// distinct chunk positions, which any one-to-one map of row bits 1, 2 and 4
+// gives; the transposed V reads (rows r0 .. r0 + 3 of a 4-row group, four
+// chunks each, per 32-lane phase) also need rows r0 and r0 + 2 on different
+// 64-byte halves of the bank space, so row bit 1 drives swizzle bit 2.
+__device__ __forceinline__ int bf16_swz(int r) {
+    return ((r >> 2) & 1) | (((r >> 4) & 1) << 1) | (((r >> 1) & 1) << 2);
 }
 
 __device__ __forceinline__ void lds_barrier() {
