@@ -162,14 +162,24 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         }
     }
 
+    // Chunk swizzle of key row r: 16-byte chunk c sits at c ^ kswz(r), which
+    // stays in 0 .. CPR-1. The 64 banks span 256 bytes, i.e. 16 / CPR rows, so
+    // rows r and r + 16 / CPR start on the same bank; a B-operand read phase
+    // touches 16 consecutive rows, one chunk each, and those rows land on 16
+    // distinct bank groups when the swizzle takes the row bits above the
+    // first log2(16 / CPR): r & 15 (256-byte rows), (r >> 1) & 7 (128-byte),
+    // (r >> 2) & 3 (64-byte).
+    static_assert(CPR == 4 || CPR == 8 || CPR == 16, "key row of 4, 8 or 16 chunks");
+    constexpr int kSwzShift = CPR == 16 ? 0 : (CPR == 8 ? 1 : 2);
+    auto kswz = [](int r) { return (r >> kSwzShift) & (CPR - 1); };
     // DMA slots: instruction wv + 8u of a tile; 16-byte slot sidx = ins*64 + lane
-    // holds logical chunk (sidx % CPR) ^ (row & (CPR-1)) of tile row sidx / CPR
+    // holds logical chunk (sidx % CPR) ^ kswz(row) of tile row sidx / CPR
     int dma_r[kDmaPerWave], dma_c[kDmaPerWave];
 #pragma unroll
     for (int u = 0; u < kDmaPerWave; ++u) {
         const int sidx = (wv + kIdxWaves * u) * 64 + lane;
         dma_r[u] = sidx / CPR;
-        dma_c[u] = (sidx % CPR) ^ (dma_r[u] & (CPR - 1));
+        dma_c[u] = (sidx % CPR) ^ kswz(dma_r[u]);
     }
     const uint8_t *kbytes = (const uint8_t *)a.k_idx;
     // rows past the block's last position read that row instead (results unused);
@@ -196,7 +206,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
 #pragma unroll
     for (int i = 0; i < (F8 ? 2 * KS : KS); ++i) {
         const int c = F8 ? 4 * (i >> 1) + 2 * g + (i & 1) : 2 * i + g;
-        boff[i] = (uint32_t)(col * RB + 16 * (c ^ (col & (CPR - 1))));
+        boff[i] = (uint32_t)(col * RB + 16 * (c ^ kswz(col)));
     }
     const int n_tiles = pmax / kKeyTile + 1;
     const int t_lo = attn::part_begin(n_tiles, a.key_split, kpart);
