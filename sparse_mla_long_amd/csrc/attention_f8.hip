@@ -316,24 +316,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         // PV role: O^T, 8 tiles of 32 dims x 32 heads
         f32x16 o[QK ? 1 : kOwn];
 
-        // Split of Q (QK waves). The query's Q landed by DMA ahead of it, head
-        // group h in ring slot (cb + 1 + h) % 3, 16-byte chunk (kb, pp, e) of
-        // lane (head col, g) at 1024 (4 kb + 2 pp + e) + 16 lane. The two QK
-        // waves of a head group split half of the k-blocks each (kKB0 and the
-        // rest; the block-1 wave's fifth block repeats block kKB - 1 and is
-        // dropped) in place, hi over chunk e = 0 and lo over e = 1, then both
-        // read all nine blocks back, so no register array is indexed by a
-        // wave-dependent value. Both roles take its two barriers.
-        constexpr int kKB0 = 5;
+        // Split of Q. The query's Q landed by DMA ahead of it, head group h in
+        // ring slot (cb + 1 + h) % 3, 16-byte chunk (kb, pp, e) of lane (head
+        // col, g) at 1024 (4 kb + 2 pp + e) + 16 lane. The four waves of a head
+        // group (both roles) split the nine k-blocks in place, part p =
+        // 2 (PV wave) + sub taking blocks 0-2, 3-4, 5-6, 7-8 (a shorter part
+        // repeats its last block and drops it), hi over chunk e = 0 and lo over
+        // e = 1; then the QK waves read all nine blocks back, so no register
+        // array is indexed by a wave-dependent value.
+        constexpr int kSplitMax = 3;
         auto trade_q = [&](int cb) {
             int ln = lane;                           // recomputed here, not held across the loop
             asm volatile("" : "+v"(ln));
             uint8_t *qs_hg = ring + ((cb + 1 + hg) % kRingSteps) * kStepBytes + 16 * ln;
-            if constexpr (QK) {
-                const int kbase = sub == 0 ? 0 : kKB0;
+            {
+                const int part = (QK ? 0 : 2) + sub;
+                const int kbase = part == 0 ? 0 : 2 * part + 1, kcnt = part == 0 ? 3 : 2;
 #pragma unroll
-                for (int kl = 0; kl < kKB0; ++kl) {
-                    const int kb = min(kbase + kl, kKB - 1);
+                for (int kl = 0; kl < kSplitMax; ++kl) {
+                    const int kb = kbase + min(kl, kcnt - 1);
                     bf16x8 raw[2][2];
 #pragma unroll
                     for (int pp = 0; pp < 2; ++pp)
@@ -372,7 +373,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                             hw[pp][d] = (uint32_t)hi;
                             lw[pp][d] = (uint32_t)lo;
                         }
-                    if (kl < kKB - kKB0 || sub == 0) {  // uniform
+                    if (kl < kcnt) {                   // uniform
 #pragma unroll
                         for (int pp = 0; pp < 2; ++pp) {
                             *(u32x4 *)(qs_hg + 1024 * (4 * kb + 2 * pp)) = hw[pp];
@@ -382,7 +383,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                     }
                 }
             }
-            lds_barrier();                           // both halves posted
+            lds_barrier();                           // every part posted
             if constexpr (QK) {
 #pragma unroll
                 for (int i = 0; i < (kKB + 3) / 4; ++i) qsc[i] = 0;
