@@ -103,7 +103,7 @@ KERNEL_SOURCES = {"attention": ("attention.hip", "attention_f8.hip", "attn_commo
                   "indexer": ("indexer.hip", "attn_common.h", "cand_select.h"), "topk": ("topk.hip",),
                   "indexer_topk": ("indexer.hip", "attn_common.h", "cand_select.h", "topk.hip"),
                   "kv_decode": ("decode_ds656.hip",)}
-KERNEL_SYMBOLS = {"attention": ("attn_kernel", "attn_f8_kernel"), "indexer": ("indexer_kernel",),
+KERNEL_SYMBOLS = {"attention": ("attn_bf16_kernel", "attn_f8_kernel"), "indexer": ("indexer_kernel",),
                   "topk": ("topk_kernel",), "indexer_topk": ("indexer_kernel", "cand_select_kernel"),
                   "kv_decode": ("ds656_decode_kernel",)}
 PATH_KERNELS = {"fused": ("indexer_topk", "kv_decode", "attention"),

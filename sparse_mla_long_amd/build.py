@@ -19,12 +19,13 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-# Per-source additions. The FP8 attention kernel runs two waves per SIMD whose
+# Per-source additions. The attention kernels run two waves per SIMD whose
 # roles hold their large arrays in different code paths; with MFMA
 # accumulators in VGPRs both paths share one 256-register allocation (in
 # accumulation registers the output tiles of one path and the operands of the
 # other would add up instead).
-FILE_FLAGS = {"attention_f8.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+FILE_FLAGS = {"attention.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+              "attention_f8.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 BUILD = os.path.join(PKG, "_build")
 
 

@@ -1,41 +1,47 @@
-// Absorbed (MQA-form) MLA attention over bf16 latent rows (FP8 rows use the
-// kernel of attention_f8.hip).
+// Absorbed (MQA-form) MLA attention over bf16 latent rows, with the waves of
+// a workgroup split into two roles that share each SIMD: logits and softmax
+// on one wave, PV and the gather on the other. Persistent workgroups prefetch
+// the next query. (FP8 rows: attention_f8.hip, the same scheme on the E4M3
+// matrix unit; launch_attention below picks the kernel.)
 //
 // Every token has one latent row of 576 values (512 latent + 64 rope) shared
 // by all heads; a query's heads attend with QK over all 576 dims and PV over
-// the first 512 (spke.com GLM-5.3 PCP/DCP article, footnote 1). One gathered
-// row therefore serves every head (section "PCP"): the kernel lands each
-// block of 32 gathered rows in LDS once and runs QK and PV of all 64 heads on
-// it.
+// the first 512 (spke.com GLM-5.3 PCP/DCP article, footnote 1), so one
+// gathered row serves every head (section "PCP"). Each 32-key block of
+// gathered rows lands in LDS once and feeds QK and PV of all 64 heads.
 //
-// Work split: one query per 256-thread workgroup, four waves; wave w owns
-// heads 32*(w>>1).. (its head group) and one half of the dims: QK over dims
-// 288*(w&1).. and PV into output dims 256*(w&1)... The two waves of a head
-// group exchange their partial logits through LDS and add them in the same
-// order, so both hold identical logits and run the same softmax.
-//
-//  * Gather: rows move HBM -> LDS with global_load_lds_dwordx4 (each lane's
-//    16 bytes land at LDS base + 16*lane) through a ring of 3 blocks. No
-//    registers hold rows in flight; completion is tracked with explicit vmcnt
-//    waits. Key indices and mask biases of a listed query are copied to LDS
-//    per chunk of the index list before its blocks.
-//  * 16-byte chunks are XOR-swizzled per row so both read patterns below are
-//    bank-conflict-free.
-//  * QK: S^T[key x head] = K[key x dims] . Q^T[dims x head] on 32x32x16 bf16
-//    MFMA; the wave's Q^T fragments stay in registers for the whole query.
-//    Accumulator row m reads LDS row 16*((m>>2)&1) + 4*(m>>3) + (m&3), so
-//    lane half g of the 32x32 accumulator holds LDS rows 16g..16g+15 of the
-//    block, in order.
-//  * PV: O[head x dim] += P[head x key] . V[key x dim]: the accumulator above
-//    already is P in the A-operand layout (k-step t = LDS rows 16g+8t..+7), so
-//    P never leaves registers. V is read key-major from the same LDS rows with
-//    the gfx950 transpose read ds_read_b64_tr_b16 (a lane receives 4 rows of
-//    one column).
-//  * Software pipeline, one barrier per block: iteration b computes the
-//    partial logits of block b+1 while it runs the softmax and PV of block b;
-//    the partial logits cross to the partner wave behind the next barrier.
-//  * Softmax in base 2 against a fixed reference max per head (see below), so
-//    the fp32 output accumulators are never rescaled inside the loop.
+// Work split: one persistent 512-thread workgroup per CU, two waves per SIMD.
+// A step is one 32-key block (36,864 bytes of bf16 rows: three steps fit the
+// LDS next to the tables).
+//  * QK waves (0..3): wave w owns head group hg = w & 1 (32 heads) and dim
+//    half dh = w >> 1: partial logits S^T[key x head] over dims 288 dh ..
+//    +287 on 32x32x16 bf16 MFMA, K from LDS, Q^T in registers. The two waves
+//    of a head group post their partial tiles, meet at a second barrier, and
+//    add the partner's in the same order, so both hold bit-identical logits
+//    and run the same softmax; the dh = 0 wave posts the probabilities (bf16)
+//    for PV.
+//  * PV waves (4..7): wave 4 + v owns head group v & 1 and output dims
+//    256 (v >> 1) .. +255: O^T[dim x head] += V^T[dim x key] P^T[key x head]
+//    of the previous step, with P from LDS and V read key-major with
+//    ds_read_b64_tr_b16; they also issue every gather (the rows of the next
+//    step, or the next query's Q).
+//  * Registers: a QK wave holds its Q^T half (72 VGPRs), a PV wave O^T (128).
+//    The roles run in separate code paths and the file is built with MFMA
+//    accumulators in VGPRs, so both fit one allocation (about 165).
+//  * Softmax in base 2 against a fixed reference max per head (the first
+//    block with a valid key); probabilities may exceed 1 by up to
+//    2^kHeadroom, so O is never rescaled in the loop, and a block that
+//    overshoots makes the workgroup redo the query with the larger reference.
+//  * Accumulator row m = col of the QK A operand reads LDS row
+//    16((m >> 2) & 1) + 4(m >> 3) + (m & 3), so lane half g of the 32x32
+//    tile holds LDS rows 16g .. 16g+15 in element order: P in the A-operand
+//    layout of PV (k-step t = rows 16g + 8t .. +7).
+//  * Next query: the gathers of a chunk's last iteration and the one after
+//    it (where only the last step's PV runs) bring the next query's Q, one
+//    head group per ring slot, in the layout of the K rows; its index list
+//    goes into its own LDS buffer.
+//  * LDS rows: 1,152 bytes, 16-byte chunk c of row r at c ^ bf16_swz(r)
+//    (conflict-free QK and transposed V reads).
 // Entries of the index list outside 0..p_i are masked (probability 0).
 #include "attn_common.h"
 #include "common.h"
@@ -46,344 +52,518 @@ namespace {
 
 using namespace attn;
 
-constexpr int kThreads = 256;              // 4 waves: (head group, dim half)
-constexpr int kQKHalf = kQK / 2, kVHalf = kV / 2;
-constexpr int O_LD = kVHalf + 8;            // epilogue staging pitch (bf16)
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;                   // 512
+constexpr int kRole = 4;                                   // waves per role
+constexpr int kRowBytes = 1152, kChunks = 72;              // bf16 rows: 72 chunks of 8 dims
+constexpr int kStepBytes = kBlk * kRowBytes;               // 36,864: one block per step
+constexpr int kDmaStep = kStepBytes / 1024 / kRole;        // 9 DMA instructions per PV wave and step
+constexpr int kRingSteps = 3;
+constexpr int kIdx = 2048;                                 // index-list entries per chunk
+constexpr int kEnt = kIdx / kThreads;                      // table entries per thread
+constexpr int kQKHalf = kQK / 2;                           // 288 dims per QK wave
+constexpr int kKS = kQKHalf / 16;                          // 18 k-steps
+constexpr int kVHalf = kV / 2;                             // 256 output dims per PV wave
+constexpr int kNT = kVHalf / 32;                           // 8 output tiles
+constexpr int O_LD = kVHalf / 2 + 8;                       // epilogue staging pitch (bf16): 128 dims a pass
+// the PV waves take the mid-step barrier after this many PV tiles
+constexpr int kMidTile = 4;
 
-constexpr int kRowBytes = 1152, kChunks = 72;   // bf16 rows: 72 chunks of 8 dims
-constexpr int kRing = 3, kIdx = 2048;
-constexpr int kXchgBytes = 2 * 4 * 64 * 16 * 4;   // [parity][wave][4][64 lanes] x f32x4
+constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
+constexpr size_t kStaticBytes = (size_t)kIdx * 8 + 2 * 2 * 4 * 64 * 16 + 2 * 2 * 2 * 64 * 16 + 2 * 32 * 4 +
+                                 kWaves * 4;
+static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
+static_assert(kDmaStep * kRole * 1024 == kStepBytes, "DMA split");
+static_assert(kEnt * kThreads == kIdx, "table split");
+static_assert((size_t)kRole * 32 * O_LD * 2 <= kStepBytes, "staging fits a ring slot");
+static_assert(kDmaStep == 9 && kNT == 8 && kKS == 18, "schedule");
 
-constexpr size_t kLdsBytes = (size_t)kRing * kBlk * kRowBytes + kXchgBytes;  // ring + exchange
-constexpr size_t kStaticBytes = (size_t)kIdx * 8 + 16;                        // entry table + votes
+template <int N> using IC = std::integral_constant<int, N>;
 
-// DENSE: no index list (keys 0..p_i); otherwise an entry table (row and mask
-// bias) is built per chunk of the list.
 template <bool DENSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1))) void attn_kernel(AttnArgs a) {
-    constexpr bool TABLE = !DENSE;
-    constexpr int R = kRing;
-    constexpr int kBlockBytes = kBlk * kRowBytes;
-    constexpr int kDma = kBlockBytes / 1024;                    // 16 B x 64 lanes per DMA
-    static_assert(kDma * 1024 == kBlockBytes && kDma >= 16, "DMA split");
-    static_assert(R >= 3, "the pipeline needs three ring slots");
+                          amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t *ring = smem;                                            // R blocks
-    f32x4 *xchg = (f32x4 *)(smem + R * kBlockBytes);                 // partial S^T exchange
-    // entry table in its own LDS objects, so LDS reads of it are not ordered
-    // behind the in-flight ring DMA
-    constexpr int kTab = TABLE ? kIdx : 4;
-    __shared__ __attribute__((aligned(16))) int32_t s_row[kTab];             // row, or -1
-    __shared__ __attribute__((aligned(16))) float s_bias[kTab];              // 0, or -inf if masked
-    __shared__ __attribute__((aligned(16))) int s_vote[4];                   // restart votes per wave
+    uint8_t *ring = smem;
+    __shared__ __attribute__((aligned(16))) int32_t s_row[kIdx];   // row, or -1 if masked
+    __shared__ __attribute__((aligned(16))) int32_t s_next[kIdx];  // index list of the next query (raw)
+    __shared__ f32x4 s_xch[2][2][4][64];        // partial logits [hg][dh][quad][lane]
+    __shared__ bf16x8 s_p[2][2][2][64];         // PV A operands [step parity][hg][k-step][lane]
+    __shared__ float s_l[2][32];                // row sums [hg][head]
+    __shared__ __attribute__((aligned(16))) int s_vote[kWaves];
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
-    const int hg = wv >> 1, dh = wv & 1;                             // head group, dim half
+    const int rw = wv & (kRole - 1);            // index within the role
+    const int hg = rw & 1, sub = rw >> 1;       // head group; dim half (QK) or output half (PV)
     const int tid = threadIdx.x;
-    // virtual query v: part v % S of query row v / S (S = 1 without split-KV)
-    const int S = a.n_split;
-    const int vq = a.batch.total_q * S - 1 - (int)blockIdx.x;
-    const int qi = vq / S, part = vq - qi * S;
-    const int64_t orow = (int64_t)part * a.batch.total_q + qi;      // output row
-    const int b = seq_of_row(a.batch.cu_q, a.batch.num_seqs, qi);
-    const int64_t kv0 = a.batch.cu_kv[b];
-    const int L = a.batch.cu_kv[b + 1] - (int)kv0;
-    const int pos = min(a.batch.q_pos[qi], L - 1);
     const int H = a.n_heads;
-    // dense: keys [key_lo, key_lo + n_valid) of 0..pos (an empty part runs one
-    // masked entry); listed: entries [lo, hi) of the row (never empty: S <= k)
-    const int key_lo = DENSE ? part_begin(pos + 1, S, part) : part_begin(a.k, S, part);
-    const int n_valid = (DENSE ? part_begin(pos + 1, S, part + 1) : part_begin(a.k, S, part + 1)) - key_lo;
-    const int n_keys = max(n_valid, 1);
-    const int32_t *idx_row = DENSE ? nullptr : a.indices + (int64_t)qi * a.idx_ld + key_lo;
-    const uint8_t *kvq = a.kv + kv0 * a.kv_stride;                   // row 0 of this sequence
-    const int chunk_len = TABLE ? kIdx : n_keys;
-
-    // Q^T fragments (B operand) of head 32*hg + col over this wave's 288 dims.
-    // k-step 2t+u uses dims 288*dh + 16*(2t+g) + 8u .. +7.
     const int head = 32 * hg + col;
-    bf16x8 qf[kQKHalf / 16];
-    {
-        const bool hv = head < H;
-        const __bf16 *qrow = a.q + ((int64_t)qi * H + (hv ? head : 0)) * kQK + kQKHalf * dh;
-#pragma unroll
-        for (int t = 0; t < kQKHalf / 32; ++t)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bf16x8 v = *(const bf16x8 *)(qrow + 16 * (2 * t + g) + 8 * u);
-                qf[2 * t + u] = hv ? v : zero_bf16x8();
-            }
-        // settle the fragment loads here, so no wait on them lands inside the
-        // block loop (where it would also drain the KV ring)
-#pragma unroll
-        for (int t = 0; t < kQKHalf / 16; ++t) asm volatile("" ::"v"(qf[t]));
-    }
+    const bool hv = head < H;
+    const int total_q = a.batch.total_q;
+    const int S = a.n_split;                    // parts per query (virtual queries per row)
+    const int total_v = total_q * S;
 
-    // per-lane DMA slot constants (same for every block)
-    constexpr int kDmaIns = (kDma + 3) / 4;
-    int dma_r[kDmaIns], dma_lc[kDmaIns];
-#pragma unroll
-    for (int u = 0; u < kDmaIns; ++u) {
-        const int sidx = (wv + 4 * u) * 64 + lane;
-        dma_r[u] = sidx / kChunks;
-        dma_lc[u] = 16 * ((sidx % kChunks) ^ bf16_swz(dma_r[u]));
-    }
-
-    // Softmax in base 2 against a reference max m_run per head. m_run is set
-    // by the first block with a valid key and only ever raised by a restart:
-    // probabilities exp2(t - m_run) may exceed 1 by up to 2^kHeadroom, which
-    // bf16 P and the fp32 sums hold exactly enough, so the 128 fp32
-    // accumulators per lane are never rescaled inside the loop. A block that
-    // overshoots by more makes the workgroup redo the query with the larger
-    // reference. Each wave ORs its votes in a register and posts them to
-    // s_vote at the end of a chunk of the index list; until then exponents
-    // are clamped to 2^kClampLog2, which keeps every sum finite.
-    float m_run = -INFINITY, l_run = 0.f;       // head `col`, this lane's keys
-    float m_seen = -INFINITY;                   // largest block max of head `col` seen
-    f32x16 o[kVHalf / 32];
-    // row this lane feeds into the QK A operand: accumulator row m = col
-    const int qk_row = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
-    const int qk_swz = bf16_swz(qk_row);
-    int parity = 0;
-    auto voted = [&]() {                         // any wave's posted vote
-        const int4 v = *(const int4 *)&s_vote[0];
-        return (v.x | v.y | v.z | v.w) != 0;
+    // Persistent workgroup: its k-th virtual query in snake order over the
+    // rows, last rows first (they have the most keys in causal batches), so
+    // the workgroups' totals stay even. -1 past the end. Virtual query v is
+    // part v % S of query row v / S.
+    auto query_of = [&](int k) -> int {
+        const int G = (int)gridDim.x, bx = (int)blockIdx.x;
+        const int r = k * G + ((k & 1) ? G - 1 - bx : bx);
+        return r < total_v ? total_v - 1 - r : -1;
+    };
+    // thread index as a value the compiler cannot hoist
+    auto tid_opq = [&]() {
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        return t;
     };
 
-    // ---- partial S^T = K Q^T of one ring slot over this wave's 288 dims. The
-    // XOR swizzle only touches the low chunk bits, so (L + 8m) ^ sw ==
-    // (L ^ sw) + 8m: four per-lane bases plus immediate offsets address every
-    // k-step.
-    auto qk = [&](const uint8_t *kb) -> f32x16 {
-        f32x16 s = zero16();
-        const uint8_t *krow = kb + qk_row * kRowBytes;
-        const int L0 = 36 * dh + 2 * g;
-        const uint8_t *e0 = krow + 16 * (L0 ^ qk_swz), *e1 = krow + 16 * ((L0 + 1) ^ qk_swz);
-        const uint8_t *o0 = krow + 16 * ((L0 + 4) ^ qk_swz), *o1 = krow + 16 * ((L0 + 5) ^ qk_swz);
-#pragma unroll
-        for (int t = 0; t < kQKHalf / 32; ++t) {
-            const bf16x8 k0 = *(const bf16x8 *)(((t & 1) ? o0 : e0) + 128 * (t >> 1));
-            const bf16x8 k1 = *(const bf16x8 *)(((t & 1) ? o1 : e1) + 128 * (t >> 1));
-            s = mfma32x32x16(k0, qf[2 * t], s);
-            s = mfma32x32x16(k1, qf[2 * t + 1], s);
-        }
-        return s;
+    // ---- gathers (issued by the PV waves): instruction ins = rw + 4u of a
+    // step moves the 16-byte slots sidx = 64 ins + lane, i.e. logical chunk
+    // (sidx % 72) ^ bf16_swz(row) of block row sidx / 72. Lane terms are
+    // recomputed at each use (held, they would be spilled across the loop).
+    auto dma_rc = [&](int u, int &r, uint32_t &lc) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int sidx = (rw + kRole * u) * 64 + ln;
+        r = sidx / kChunks;
+        lc = 16u * (uint32_t)((sidx % kChunks) ^ bf16_swz(r));
     };
-    // ---- O[:, 256*dh ..] += P V from one ring slot; k-step t = LDS rows 16g + 8t
-    // .. +7. The chunk swizzle of the rows a lane addresses does not depend on
-    // t or on the N-block, so per-lane bases plus immediates address them all.
-    auto pv = [&](const uint8_t *kb, const bf16x8 *pa) {
-        const int gi = lane & 15, hh = (lane >> 4) & 1;
-        // lane supplies row 16g + 8t + 4v + (gi >> 2), dims 4*(gi & 3).. of the
-        // N-block's 16-dim group; logical chunk 32*dh + 4*nb + 2*hh + ((gi&3)>>1)
-        const int L2 = 32 * dh + 2 * hh + ((gi & 3) >> 1);
-        const uint8_t *vb0[2][2];
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            const int sw = v | (g << 1) | ((gi >> 3) << 2);    // bf16_swz of those rows
-            const uint8_t *rb = kb + (16 * g + 4 * v + (gi >> 2)) * kRowBytes + 8 * (gi & 1);
-            vb0[v][0] = rb + 16 * (L2 ^ sw);
-            vb0[v][1] = rb + 16 * ((L2 + 4) ^ sw);
-        }
-#pragma unroll
-        for (int nb = 0; nb < kVHalf / 32; ++nb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                bf16x4 w16[2];
-#pragma unroll
-                for (int v = 0; v < 2; ++v)
-                    w16[v] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lds_bf16x4_ptr)(vb0[v][nb & 1] + 128 * (nb >> 1) + 8 * kRowBytes * t));
-                bf16x8 vb;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vb[e] = w16[0][e];
-                    vb[4 + e] = w16[1][e];
-                }
-                o[nb] = mfma32x32x16(pa[t], vb, o[nb]);
-            }
+    auto slot_dst = [&](int slot, int u) {
+        return lds_addr(smem) + (uint32_t)(slot * kStepBytes + (rw + kRole * u) * 1024);
     };
-    f32x4 *xmine = xchg + (wv * 4) * 64 + lane;           // + parity * 16 * 64
-    const f32x4 *xother = xchg + ((wv ^ 1) * 4) * 64 + lane;
-    auto put_partial = [&](const f32x16 &s, int par) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            xmine[(par * 16 + q4) * 64] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+    // row j of this query's sequence for instruction u (entries past the chunk
+    // hold -1: row 0, fetched and never used)
+    auto dma_row = [&](int st, int u) -> int {
+        int r;
+        uint32_t lc;
+        dma_rc(u, r, lc);
+        return max(s_row[kBlk * st + r], 0);
     };
-    auto add_partial = [&](f32x16 &s, int par) {
+    // row j (of `pitch` bytes) of `src` for instruction u into ring slot `slot`
+    auto dma_go = [&](const uint8_t *src, uint32_t pitch, int slot, int u, int j) {
+        int r;
+        uint32_t lc;
+        dma_rc(u, r, lc);
+        dma16_lds(src, (uint32_t)j * pitch + lc, slot_dst(slot, u));
+    };
+    // Q rows go to a ring slot in the layout of the K rows: head 32 h + r of
+    // head group h as row r (heads past n_heads fetch head 0)
+    auto q_head = [&](int h, int u) -> int {
+        int r;
+        uint32_t lc;
+        dma_rc(u, r, lc);
+        const int hq = 32 * h + r;
+        return hq < H ? hq : 0;
+    };
+    auto q_one = [&](const uint8_t *qb, int h, int slot, int u) {
+        dma_go(qb, (uint32_t)kRowBytes, slot, u, q_head(h, u));
+    };
+    // index list of virtual query v into s_next (entries past the list repeat its last)
+    auto fetch_idx = [&](int v) {
+        const int row = v / S, part = v - row * S;
+        const int lo = part_begin(a.k, S, part);
+        const int cn0 = min(kIdx, part_begin(a.k, S, part + 1) - lo), t = tid_opq();
+        const int32_t *ib = a.indices + (int64_t)row * a.idx_ld + lo;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 v = xother[(par * 16 + q4) * 64];
-            // same sum order in both waves (dim half 0 first) -> identical S
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                s[4 * q4 + j] = dh == 0 ? s[4 * q4 + j] + v[j] : v[j] + s[4 * q4 + j];
-        }
+        for (int i = 0; i < kEnt; ++i)
+            dma4_lds(ib, 4u * (uint32_t)min(t + kThreads * i, cn0 - 1),
+                     lds_addr(s_next) + 4u * (uint32_t)(kThreads * i + kWave * wv));
     };
 
-    for (;;) {                                   // attempts: one unless a block overshoots
-#pragma unroll
-    for (int nb = 0; nb < kVHalf / 32; ++nb) o[nb] = zero16();
-    l_run = 0.f;
-    bool redo = false;
-    bool my_vote = false;                        // wave-uniform
-    for (int c0 = 0; c0 < n_keys && !redo; c0 += chunk_len) {
-        const int cn = min(chunk_len, n_keys - c0);               // entries in this chunk
-        const int cv = min(chunk_len, n_valid - c0);              // dense: the valid ones
-        const int n_blk = (cn + kBlk - 1) / kBlk;
-        const int n_ent = n_blk * kBlk;
-        if (TABLE) {
-            // entry table of the chunk: row (or -1 when masked) and mask bias
-            for (int e = tid; e < n_ent; e += kThreads) {
-                const int ge = c0 + e;
-                int j = -1;
-                if (e < cn) j = DENSE ? ge : idx_row[ge];
-                const bool v = j >= 0 && j <= pos;
-                s_row[e] = v ? j : -1;
-                s_bias[e] = v ? 0.f : -INFINITY;
-            }
-            __syncthreads();
+    // ---- per-query state, computed alike by every wave
+    int qi = 0;
+    int64_t orow = 0;                            // output row: part * total_q + qi
+    int key_lo = 0, lim = 0;                     // dense: first key of the part; keys above lim are masked
+    int n_keys = 0;
+    int64_t kv0 = 0;
+    const int32_t *idx_row = nullptr;
+    auto set_query = [&](int v) {
+        qi = v / S;
+        const int part = v - qi * S;
+        orow = (int64_t)part * total_q + qi;
+        const int b = seq_of_row(a.batch.cu_q, a.batch.num_seqs, qi);
+        kv0 = a.batch.cu_kv[b];
+        const int L = a.batch.cu_kv[b + 1] - (int)kv0;
+        const int pos = min(a.batch.q_pos[qi], L - 1);
+        if (DENSE) {             // keys [lo, hi) of 0..pos; an empty part runs one masked entry
+            key_lo = part_begin(pos + 1, S, part);
+            const int hi = part_begin(pos + 1, S, part + 1);
+            lim = hi - 1;
+            n_keys = hi - key_lo + (hi == key_lo ? 1 : 0);
+        } else {                 // entries [lo, hi) of the list (never empty: S <= k)
+            const int lo = part_begin(a.k, S, part);
+            lim = pos;
+            n_keys = part_begin(a.k, S, part + 1) - lo;
+            idx_row = a.indices + (int64_t)qi * a.idx_ld + lo;
         }
-        // row of entry e of the chunk; entries past the chunk (the pipeline's
-        // tail) read row 0, which is always present and whose result is unused
-        auto row_of = [&](int e) -> int {
-            if (TABLE) {
-                const int r = s_row[min(e, kTab - 1)];   // unconditional: no branch, one wait
-                return e < n_ent ? r : -1;
-            }
-            return e < cn ? key_lo + c0 + e : -1;
-        };
-        // DMA one block into ring slot `slot`: this wave issues instructions
-        // wv, wv+4, ... (16-byte slot sidx = ins*64 + lane holds logical chunk
-        // dma_lc[u] of block row dma_r[u]); row offsets stay 32-bit.
-        // The rows of all of this wave's instructions are looked up first (one
-        // LDS wait); only the last instruction may be skipped, on SCC.
-        auto issue = [&](int blk, int slot) {
-            uint8_t *dst = ring + slot * kBlockBytes;
-            int j[kDmaIns];
-#pragma unroll
-            for (int u = 0; u < kDmaIns; ++u) j[u] = max(row_of(blk * kBlk + dma_r[u]), 0);
-#pragma unroll
-            for (int u = 0; u < kDmaIns; ++u) {
-                if (4 * u + 3 < kDma || wv + 4 * u < kDma) {      // compile-time true but for the last
-                    const uint32_t off = (uint32_t)j[u] * (uint32_t)a.kv_stride + (uint32_t)dma_lc[u];
-                    dma16(kvq + off, dst + (wv + 4 * u) * 1024);
-                }
-            }
-        };
+    };
+    auto chunk_steps = [&](int c0) { return (min(kIdx, n_keys - c0) + kBlk - 1) / kBlk; };
 
-        // prologue: blocks 0..R-2 in flight; partial logits of block 0
+    // Row table of the chunk starting at entry c0 (jv: this thread's raw
+    // entries): rows posted (-1 where masked), then the PV waves' gather of
+    // step 0 into ring slot cb.
+    auto post_rows = [&](int c0, int *jv, int cb, bool pv_wave) {
+        const int cn = min(kIdx, n_keys - c0), t = tid_opq();
 #pragma unroll
-        for (int p = 0; p < R - 1; ++p) issue(p, p);
-        wait_vm_blocks<kDma / 4>(R - 2);
-        lds_barrier();
-        f32x16 s_own = qk(ring);
-        put_partial(s_own, parity);
-
-        for (int blk = 0; blk < n_blk; ++blk) {
-            // R-1 blocks were issued ahead; block blk+1 must have landed
-            wait_vm_blocks<kDma / 4>(R - 3);
-            lds_barrier();               // blk+1 landed everywhere; partials of blk written
-            issue(blk + R - 1, (blk + R - 1) % R);        // into the slot of block blk-1
-            f32x16 s = s_own;
-            add_partial(s, parity);
-            // partial logits of the next block (on the last block: of a tail
-            // slot, unused)
-            s_own = qk(ring + ((blk + 1) % R) * kBlockBytes);
-
-            // ---- softmax (base 2) of block blk for head `col`; element e <->
-            // LDS row 16g + e
-            const int e0 = blk * kBlk + 16 * g;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                float bi[4];
-                if (TABLE) {
-                    *(f32x4 *)bi = *(const f32x4 *)&s_bias[e0 + 4 * q4];
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) bi[j] = e0 + 4 * q4 + j < cv ? 0.f : -INFINITY;
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int e = 4 * q4 + j;
-                    s[e] = fmaf(s[e], a.scale_log2, bi[j]);
-                    mx = fmaxf(mx, s[e]);
-                }
-            }
-            mx = fmaxf(mx, xor32(mx));
-            m_seen = fmaxf(m_seen, mx);
-            if (m_run == -INFINITY) m_run = mx;          // first valid keys: nothing to rescale
-            my_vote |= __any(mx > m_run + kHeadroom);
-            const float msub = m_run == -INFINITY ? 0.f : m_run;
-            bf16x8 pa[2];
-            float psum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fminf(s[e] - msub, kClampLog2));
-                psum += p;
-                pa[e >> 3][e & 7] = (__bf16)p;
-            }
-            l_run += psum;
-
-            pv(ring + (blk % R) * kBlockBytes, pa);
-            parity ^= 1;
-            put_partial(s_own, parity);
+        for (int i = 0; i < kEnt; ++i) {
+            const int e = t + kThreads * i;
+            jv[i] = e < cn && jv[i] >= 0 && jv[i] <= lim ? jv[i] : -1;
+            s_row[e] = jv[i];
         }
-        // the tail DMA must land before the ring is reused
+        lds_barrier();                                   // rows posted
+        const uint8_t *kvq = a.kv + kv0 * a.kv_stride;
+        if (pv_wave) {                                   // uniform
+#pragma unroll
+            for (int u = 0; u < kDmaStep; ++u) dma_go(kvq, (uint32_t)a.kv_stride, cb, u, dma_row(0, u));
+        }
+    };
+
+    for (int e = tid; e < kIdx; e += kThreads) s_row[e] = -1;
+    // the first query's index list and Q, as a previous query would have left them
+    if (query_of(0) >= 0) {                       // uniform
+        const int q0 = query_of(0);
+        if (!DENSE) fetch_idx(q0);
+        if (wv >= kRole) {
+#pragma unroll
+            for (int u = 0; u < kDmaStep; ++u) {
+                q_one((const uint8_t *)(a.q + (int64_t)(q0 / S) * H * kQK), 0, 1, u);
+                q_one((const uint8_t *)(a.q + (int64_t)(q0 / S) * H * kQK), 1, 2, u);
+            }
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        s_vote[wv] = my_vote ? 1 : 0;                 // same value from every lane
-        lds_barrier();        // every wave is done with the ring and the table; votes posted
-        redo = voted();
-        lds_barrier();        // votes read before the next chunk posts again
-    }
-    if (!redo) break;
-    // redo the query with a larger reference max
-    lds_barrier();
-    m_run = fmaxf(m_run, m_seen);
-    parity = 0;
-    lds_barrier();
+        lds_barrier();
     }
 
-    // ---- epilogue: l over both lane halves; LSE; O / l staged through LDS as bf16
-    const float lt = l_run + xor32(l_run);
-    if (dh == 0 && g == 0 && head < H)
-        a.lse[orow * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    __bf16 *stage = (__bf16 *)smem + wv * 32 * O_LD;          // 32 heads x 256 bf16 per wave
+    // The two roles run the same control flow (queries, redo attempts,
+    // chunks, steps) with the same barriers in the same order; only the work
+    // between barriers differs, and every condition around a barrier is
+    // uniform over the workgroup.
+    auto run = [&](auto ROLE) {
+        constexpr bool QK = decltype(ROLE)::value != 0;
+
+        // QK role: Q^T fragments (B operand) of head `head` over dims
+        // 288 sub .. +287; fragment 2t + u holds dims 288 sub + 16 (2t + g) +
+        // 8u .. +7 (LDS chunk 36 sub + 4t + 2g + u of the head's row)
+        bf16x8 qf[QK ? kKS : 1];
+        float m_run = -INFINITY, l_run = 0.f, m_seen = -INFINITY;   // head `col`
+        // PV role: O^T[dim x head], 8 tiles of 32 dims x 32 heads (lane (head
+        // col, g) holds dims 32 nb + 8 i + 4 g + j in element 4 i + j)
+        f32x16 o[QK ? 1 : kNT];
+
+        // K rows: accumulator row m = col reads LDS row qk_row; chunk
+        // 36 sub + 4t + 2g + u, and (L + 8m) ^ sw == (L ^ sw) + 8m
+        const int qk_row = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
+        // partial S^T of one ring slot over this wave's 288 dims
+        auto qk = [&](const uint8_t *kb) -> f32x16 {
+            f32x16 s = zero16();
+            const int sw = bf16_swz(qk_row);
+            const uint8_t *krow = kb + qk_row * kRowBytes;
+            const int L0 = 36 * sub + 2 * g;
+            const uint8_t *e0 = krow + 16 * (L0 ^ sw), *e1 = krow + 16 * ((L0 + 1) ^ sw);
+            const uint8_t *o0 = krow + 16 * ((L0 + 4) ^ sw), *o1 = krow + 16 * ((L0 + 5) ^ sw);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+            for (int t = 0; t < kKS / 2; ++t) {
+                const bf16x8 k0 = *(const bf16x8 *)(((t & 1) ? o0 : e0) + 128 * (t >> 1));
+                const bf16x8 k1 = *(const bf16x8 *)(((t & 1) ? o1 : e1) + 128 * (t >> 1));
+                if constexpr (QK) {
+                    s = mfma32x32x16(k0, qf[2 * t], s);
+                    s = mfma32x32x16(k1, qf[2 * t + 1], s);
+                }
+            }
+            return s;
+        };
+        // the query's Q^T from ring slot (cb + 1 + hg) % 3 (head rows in the
+        // K-row layout)
+        auto read_q = [&](int cb) {
+            if constexpr (QK) {
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const int c = ln & 31, gg = ln >> 5;
+                const int sw = bf16_swz(c);
+                const uint8_t *qr = ring + ((cb + 1 + hg) % kRingSteps) * kStepBytes + c * kRowBytes;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int hr = 8 * i + 4 * g + j;
-            const float ir = __shfl(inv, hr);
+                for (int t = 0; t < kKS / 2; ++t)
 #pragma unroll
-            for (int nb = 0; nb < kVHalf / 32; ++nb)
-                stage[hr * O_LD + 32 * nb + col] = (__bf16)(o[nb][4 * i + j] * ir);
+                    for (int u = 0; u < 2; ++u)
+                        qf[2 * t + u] = *(const bf16x8 *)(qr + 16 * ((36 * sub + 4 * t + 2 * gg + u) ^ sw));
+            }
+        };
+
+        // PV of one ring slot: O^T[256 sub .., :] += V^T P^T; k-step t = LDS
+        // rows 16g + 8t .. +7. For the 32x32x16 MFMA a lane's 8 values of V^T
+        // as the A operand (row = dim) are those of V as a B operand (column =
+        // dim), and P^T as B those of P as A, so the operands are read as for
+        // O = P V and only their order is swapped; O^T puts one head in each
+        // lane column. A lane supplies row 16g + 8t + 4v + (gi >> 2), dims
+        // 4 (gi & 3) .. of the tile's 16-dim group: logical chunk
+        // 32 sub + 4 nb + 2 hh + ((gi & 3) >> 1), swizzled by those rows'
+        // bf16_swz (which does not depend on t). mid() runs after tile
+        // kMidTile - 1, issue(nb) after tile nb.
+        auto pv = [&](const uint8_t *kb, const bf16x8 *pa, auto &&issue, auto &&mid) {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int gi = ln & 15, hh = (ln >> 4) & 1, gg = ln >> 5;
+            const int L2 = 32 * sub + 2 * hh + ((gi & 3) >> 1);
+            const uint8_t *vb0[2][2];
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const int sw = v | (gg << 1) | ((gi >> 3) << 2);    // bf16_swz of those rows
+                const uint8_t *rb = kb + (16 * gg + 4 * v + (gi >> 2)) * kRowBytes + 8 * (gi & 1);
+                vb0[v][0] = rb + 16 * (L2 ^ sw);
+                vb0[v][1] = rb + 16 * ((L2 + 4) ^ sw);
+            }
+#pragma unroll
+            for (int nb = 0; nb < kNT; ++nb) {
+                if (nb == kMidTile) mid();
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    bf16x4 w16[2];
+#pragma unroll
+                    for (int v = 0; v < 2; ++v)
+                        w16[v] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                            (lds_bf16x4_ptr)(vb0[v][nb & 1] + 128 * (nb >> 1) + 8 * kRowBytes * t));
+                    bf16x8 vb;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        vb[e] = w16[0][e];
+                        vb[4 + e] = w16[1][e];
+                    }
+                    if constexpr (!QK) o[nb] = mfma32x32x16(vb, pa[t], o[nb]);
+                }
+                issue(nb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (kNT == kMidTile) mid();
+        };
+
+        int cb = 0;                                  // ring slot of the chunk's step 0
+        for (int k = 0;; ++k) {
+            const int q = query_of(k);
+            if (q < 0) break;                         // uniform
+            set_query(q);
+            const int qn = query_of(k + 1);
+            const uint8_t *qn_base = (const uint8_t *)(a.q + (int64_t)(qn >= 0 ? qn / S : 0) * H * kQK);
+            {
+                int jv[kEnt];
+                const int t = tid_opq();
+#pragma unroll
+                for (int i = 0; i < kEnt; ++i) jv[i] = DENSE ? key_lo + t + kThreads * i : s_next[t + kThreads * i];
+                post_rows(0, jv, cb, !QK);
+            }
+            if (!DENSE && qn >= 0) fetch_idx(qn);     // s_next is read; refill it
+            read_q(cb);                               // (the first barrier below frees the Q slots)
+            bool staged = true;
+            m_run = -INFINITY;
+            m_seen = -INFINITY;
+            for (;;) {                                // attempts: one unless a block overshoots
+                if constexpr (!QK) {
+#pragma unroll
+                    for (int nb = 0; nb < kNT; ++nb) o[nb] = zero16();
+                }
+                l_run = 0.f;
+                bool redo = false;
+                bool my_vote = false;                 // wave-uniform
+                for (int c0 = 0; c0 < n_keys && !redo; c0 += kIdx) {
+                    const int n_steps = chunk_steps(c0);
+                    if (!staged) {           // uniform: later chunks and redo attempts
+                        const int cn = min(kIdx, n_keys - c0), t = tid_opq();
+                        int jv[kEnt];
+#pragma unroll
+                        for (int i = 0; i < kEnt; ++i) {
+                            const int e = t + kThreads * i;
+                            jv[i] = DENSE ? key_lo + c0 + e : idx_row[c0 + min(e, cn - 1)];   // unconditional loads
+                        }
+                        post_rows(c0, jv, cb, !QK);
+                    }
+                    staged = false;
+                    const uint8_t *kvq = a.kv + kv0 * a.kv_stride;
+                    // Iteration t: QK waves compute the logits, softmax and P of
+                    // step t (two barriers: the partial tiles cross between
+                    // them); PV waves run PV of step t - 1 and gather step t + 1,
+                    // or past the chunk's last step the next query's Q (head
+                    // group t + 1 - n_steps) when this chunk ends the query.
+                    // Step v sits in ring slot (cb + v) % 3: step t + 1 takes
+                    // the slot of step t - 2, whose PV ended before this
+                    // iteration's first barrier.
+                    // (iteration 0, which has no PV, is peeled off, so the
+                    // loop has one path for O)
+                    int sl = cb;
+                    auto step = [&](int t, auto WITH_PV) {
+                        constexpr bool kPV = decltype(WITH_PV)::value != 0;
+                        const int slp = sl == 0 ? kRingSteps - 1 : sl - 1;
+                        const int sln = sl == kRingSteps - 1 ? 0 : sl + 1;
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's gathers of step t landed
+                        lds_barrier();       // step t everywhere; PV of t - 2 done; P of t - 1 posted
+                        if constexpr (QK) {
+                            f32x16 s = zero16();
+                            if (t < n_steps) {
+                                s = qk(ring + sl * kStepBytes);
+#pragma unroll
+                                for (int q4 = 0; q4 < 4; ++q4)
+                                    s_xch[hg][sub][q4][lane] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+                            }
+                            lds_barrier();   // mid-step: both halves' partial logits posted
+                            if (t < n_steps) {
+                                // logits of head `col`, keys (LDS rows) 16g .. 16g+15
+                                // (entries e0 ..): own half plus the partner's
+#pragma unroll
+                                for (int q4 = 0; q4 < 4; ++q4) {
+                                    const f32x4 v = s_xch[hg][sub ^ 1][q4][lane];
+#pragma unroll
+                                    for (int j = 0; j < 4; ++j) s[4 * q4 + j] += v[j];
+                                }
+                                const int e0 = kBlk * t + 16 * g;
+                                float mx = -INFINITY;
+#pragma unroll
+                                for (int q4 = 0; q4 < 4; ++q4) {
+                                    const int4 rv = *(const int4 *)&s_row[e0 + 4 * q4];
+#pragma unroll
+                                    for (int j = 0; j < 4; ++j) {
+                                        const int e = 4 * q4 + j;
+                                        s[e] = rv[j] >= 0 ? s[e] * a.scale_log2 : -INFINITY;
+                                        mx = fmaxf(mx, s[e]);
+                                    }
+                                }
+                                mx = fmaxf(mx, xor32(mx));
+                                m_seen = fmaxf(m_seen, mx);
+                                if (m_run == -INFINITY) m_run = mx;          // first valid keys
+                                my_vote |= __any(mx > m_run + kHeadroom);
+                                const float msub = m_run == -INFINITY ? 0.f : m_run;
+                                bf16x8 pa[2];
+                                float psum = 0.f;
+#pragma unroll
+                                for (int e = 0; e < 16; ++e) {
+                                    const float p = __builtin_amdgcn_exp2f(fminf(s[e] - msub, kClampLog2));
+                                    psum += p;
+                                    pa[e >> 3][e & 7] = (__bf16)p;
+                                }
+                                l_run += psum;
+                                if (sub == 0) {
+                                    s_p[t & 1][hg][0][lane] = pa[0];
+                                    s_p[t & 1][hg][1][lane] = pa[1];
+                                }
+                            }
+                        } else {
+                            // this iteration's gathers: rows read up front, one
+                            // after each PV tile (two after the first)
+                            // (past the last step of a chunk that does not end
+                            // the query, or with no next query, the Q fetch
+                            // still runs, of query row 0 if there is none, into
+                            // slots nobody reads before the chunk's last wait)
+                            const bool keys = t + 1 < n_steps;
+                            int jn[kDmaStep];
+                            if (keys) {
+#pragma unroll
+                                for (int u = 0; u < kDmaStep; ++u) jn[u] = dma_row(t + 1, u);
+                            } else {
+#pragma unroll
+                                for (int u = 0; u < kDmaStep; ++u) jn[u] = q_head(t + 1 - n_steps, u);
+                            }
+                            const uint8_t *src = keys ? kvq : qn_base;
+                            const uint32_t pitch = keys ? (uint32_t)a.kv_stride : (uint32_t)kRowBytes;
+                            auto issue = [&](int nb) {
+#pragma unroll
+                                for (int u = 0; u < kDmaStep; ++u)
+                                    if (nb == u * kNT / kDmaStep) dma_go(src, pitch, sln, u, jn[u]);
+                            };
+                            auto mid = [&]() { lds_barrier(); };   // the QK waves' mid-step barrier
+                            if constexpr (kPV) {
+                                bf16x8 pa[2];
+                                pa[0] = s_p[(t - 1) & 1][hg][0][lane];
+                                pa[1] = s_p[(t - 1) & 1][hg][1][lane];
+                                pv(ring + slp * kStepBytes, pa, issue, mid);
+                            } else {
+#pragma unroll
+                                for (int nb = 0; nb < kNT; ++nb) {
+                                    if (nb == kMidTile) mid();
+                                    issue(nb);
+                                }
+                                if (kNT == kMidTile) mid();
+                            }
+                        }
+                        sl = sln;
+                    };
+                    step(0, IC<0>{});
+                    for (int t = 1; t <= n_steps; ++t) step(t, IC<1>{});
+                    // the tail DMA must land before the ring is reused
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    s_vote[wv] = QK && my_vote ? 1 : 0;          // same value from every lane
+                    lds_barrier();        // votes posted; every wave is done with the ring and the table
+                    {
+                        const int4 v0 = *(const int4 *)&s_vote[0], v1 = *(const int4 *)&s_vote[4];
+                        redo = ((v0.x | v0.y | v0.z | v0.w) | (v1.x | v1.y | v1.z | v1.w)) != 0;
+                    }
+                    lds_barrier();        // votes read before the next chunk posts again
+                    cb = (cb + n_steps - 1) % kRingSteps;        // the next chunk's step 0: the last step's slot
+                }
+                if (!redo) break;
+                m_run = fmaxf(m_run, m_seen);                    // redo with the largest block max seen
+            }
+
+            // ---- epilogue: the row sums (identical in both QK waves of a head
+            // group); LSE (QK waves); O / l (PV waves)
+            if constexpr (QK) {
+                const float lt = l_run + xor32(l_run);
+                if (sub == 0 && g == 0) s_l[hg][col] = lt;
+                if (sub == 0 && g == 0 && hv)
+                    a.lse[orow * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+            }
+            lds_barrier();
+            if constexpr (!QK) {
+                // O^T / l as bf16, staged through the last step's slot (the next
+                // query's step 0: its first barrier comes before the gathers into
+                // it), 32 heads x 128 dims per wave and pass; each wave reads back
+                // only its own rows. Lane terms come from an opaque copy of the
+                // lane id, so they are computed here rather than held across the
+                // query loop.
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const float lt = s_l[hg][ln & 31];
+                const float inv = lt > 0.f ? 1.f / lt : 0.f;
+                __bf16 *stage = (__bf16 *)(ring + cb * kStepBytes) + rw * 32 * O_LD;
+                __bf16 *st_w = stage + (ln & 31) * O_LD + 4 * (ln >> 5);
+                const __bf16 *st_r = stage + (ln >> 4) * O_LD + 8 * (ln & 15);
+                __bf16 *orow_p = a.out + (orow * H + 32 * hg + (ln >> 4)) * kV + kVHalf * sub + 8 * (ln & 15);
+                const int h_lane = 32 * hg + (ln >> 4);
+#pragma unroll
+                for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+                    for (int nb = 0; nb < kNT / 2; ++nb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            bf16x4 v;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[kNT / 2 * ps + nb][4 * i + j] * inv);
+                            *(bf16x4 *)(st_w + 32 * nb + 8 * i) = v;
+                        }
+                    // 32 rows x 256 B: four rows per pass, 16 B per lane
+#pragma unroll
+                    for (int it = 0; it < 8; ++it) {
+                        const u32x4 v = *(const u32x4 *)(st_r + 4 * it * O_LD);
+                        if (h_lane + 4 * it < H)
+                            *(u32x4 *)(orow_p + (int64_t)4 * it * kV + (kVHalf / 2) * ps) = v;
+                    }
+                }
+            }
         }
-    lds_barrier();
-    // 32 rows x 512 B per wave: two rows per pass, 16 B per lane
-#pragma unroll
-    for (int pr = 0; pr < 16; ++pr) {
-        const int hr = 2 * pr + (lane >> 5);
-        const int h = 32 * hg + hr;
-        if (h < H) {
-            const u32x4 v = *(const u32x4 *)(stage + hr * O_LD + 8 * col);
-            *(u32x4 *)(a.out + (orow * H + h) * kV + kVHalf * dh + 8 * col) = v;
-        }
-    }
+    };
+    if (wv < kRole) run(IC<1>{});
+    else run(IC<0>{});
 }
 
-static_assert(kLdsBytes >= 4 * 32 * O_LD * 2, "epilogue staging must fit");
-static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
-
+// One persistent workgroup per compute unit (the LDS allows one), each
+// running its share of the queries.
 template <bool DENSE> hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
-    hipError_t e = hipFuncSetAttribute((const void *)attn_kernel<DENSE>,
+    hipError_t e = hipFuncSetAttribute((const void *)attn_bf16_kernel<DENSE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_kernel<DENSE>), dim3((unsigned)((int64_t)a.batch.total_q * a.n_split)), dim3(kThreads),
-                       kLdsBytes, s, a);
+    int dev = 0, n_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int grid = (int)std::min<int64_t>((int64_t)a.batch.total_q * a.n_split, std::max(n_cu, 1));
+    hipLaunchKernelGGL((attn_bf16_kernel<DENSE>), dim3(grid), dim3(kThreads), kLdsBytes, s, a);
     return hipGetLastError();
 }
 

@@ -323,7 +323,6 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
             for (int ks = 0; ks < KS; ++ks) {
                 if constexpr (F8) {
                     // chunks 4 ks + 2 g and the next: the dims the A operand holds
-                    const int c0 = 4 * ks + 2 * g;
                     const i32x8 bk = cat(*(const i32x4 *)(krow + boff[2 * ks]), *(const i32x4 *)(krow + boff[2 * ks + 1]));
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_e4m3(qf[mb][ks], bk, acc[mb]);
