@@ -121,40 +121,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 
     // ---- gathers (issued by the PV waves): instruction ins = rw + 4u of a
     // step moves the 16-byte slots sidx = 64 ins + lane, i.e. logical chunk
-    // (sidx % 72) ^ bf16_swz(row) of block row sidx / 72. Lane terms are
-    // recomputed at each use (held, they would be spilled across the loop).
-    auto dma_rc = [&](int u, int &r, uint32_t &lc) {
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int sidx = (rw + kRole * u) * 64 + ln;
-        r = sidx / kChunks;
-        lc = 16u * (uint32_t)((sidx % kChunks) ^ bf16_swz(r));
-    };
+    // (sidx % 72) ^ bf16_swz(row) of block row sidx / 72. The lane terms
+    // (that row, and the chunk's byte offset in it) are computed once.
+    int dma_r[kDmaStep];
+    uint32_t dma_lc[kDmaStep];
+#pragma unroll
+    for (int u = 0; u < kDmaStep; ++u) {
+        const int sidx = (rw + kRole * u) * 64 + lane;
+        dma_r[u] = sidx / kChunks;
+        dma_lc[u] = 16u * (uint32_t)((sidx % kChunks) ^ bf16_swz(dma_r[u]));
+    }
     auto slot_dst = [&](int slot, int u) {
         return lds_addr(smem) + (uint32_t)(slot * kStepBytes + (rw + kRole * u) * 1024);
     };
     // row j of this query's sequence for instruction u (entries past the chunk
     // hold -1: row 0, fetched and never used)
-    auto dma_row = [&](int st, int u) -> int {
-        int r;
-        uint32_t lc;
-        dma_rc(u, r, lc);
-        return max(s_row[kBlk * st + r], 0);
-    };
+    auto dma_row = [&](int st, int u) -> int { return max(s_row[kBlk * st + dma_r[u]], 0); };
     // row j (of `pitch` bytes) of `src` for instruction u into ring slot `slot`
     auto dma_go = [&](const uint8_t *src, uint32_t pitch, int slot, int u, int j) {
-        int r;
-        uint32_t lc;
-        dma_rc(u, r, lc);
-        dma16_lds(src, (uint32_t)j * pitch + lc, slot_dst(slot, u));
+        dma16_lds(src, (uint32_t)j * pitch + dma_lc[u], slot_dst(slot, u));
     };
     // Q rows go to a ring slot in the layout of the K rows: head 32 h + r of
     // head group h as row r (heads past n_heads fetch head 0)
     auto q_head = [&](int h, int u) -> int {
-        int r;
-        uint32_t lc;
-        dma_rc(u, r, lc);
-        const int hq = 32 * h + r;
+        const int hq = 32 * h + dma_r[u];
         return hq < H ? hq : 0;
     };
     auto q_one = [&](const uint8_t *qb, int h, int slot, int u) {
