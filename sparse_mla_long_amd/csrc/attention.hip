@@ -15,11 +15,11 @@
 // LDS next to the tables).
 //  * QK waves (0..3): wave w owns head group hg = w & 1 (32 heads) and dim
 //    half dh = w >> 1: partial logits S^T[key x head] over dims 288 dh ..
-//    +287 on 32x32x16 bf16 MFMA, K from LDS, Q^T in registers. The two waves
-//    of a head group post their partial tiles, meet at a second barrier, and
-//    add the partner's in the same order, so both hold bit-identical logits
-//    and run the same softmax; the dh = 0 wave posts the probabilities (bf16)
-//    for PV.
+//    +287 on 32x32x16 bf16 MFMA, K from LDS, Q^T in registers. Each wave of
+//    a head group's pair finalizes half of the block's keys (k-step dh of
+//    PV): it posts the partner's half of its partial tile, meets it at a
+//    second barrier, adds the partner's partials to its own half, and runs
+//    the softmax there, posting those probabilities (bf16) for PV.
 //  * PV waves (4..7): wave 4 + v owns head group v & 1 and output dims
 //    256 (v >> 1) .. +255: O^T[dim x head] += V^T[dim x key] P^T[key x head]
 //    of the previous step, with P from LDS and V read key-major with
@@ -27,11 +27,13 @@
 //    step, or the next query's Q).
 //  * Registers: a QK wave holds its Q^T half (72 VGPRs), a PV wave O^T (128).
 //    The roles run in separate code paths and the file is built with MFMA
-//    accumulators in VGPRs, so both fit one allocation (about 165).
-//  * Softmax in base 2 against a fixed reference max per head (the first
-//    block with a valid key); probabilities may exceed 1 by up to
-//    2^kHeadroom, so O is never rescaled in the loop, and a block that
-//    overshoots makes the workgroup redo the query with the larger reference.
+//    accumulators in VGPRs, so both fit one allocation (about 220).
+//  * Softmax in base 2 against a fixed reference max per head (the largest
+//    valid logit of the query's first block, agreed by the pair through LDS);
+//    probabilities may exceed 1 by up to 2^kHeadroom, so O is never rescaled
+//    in the loop, and a block that overshoots (or has valid keys while the
+//    reference is unset) makes the workgroup redo the query with the pair's
+//    largest block max.
 //  * Accumulator row m = col of the QK A operand reads LDS row
 //    16((m >> 2) & 1) + 4(m >> 3) + (m & 3), so lane half g of the 32x32
 //    tile holds LDS rows 16g .. 16g+15 in element order: P in the A-operand
@@ -70,8 +72,8 @@ constexpr int O_LD = kVHalf / 2 + 8;                       // epilogue staging p
 constexpr int kMidTile = 4;
 
 constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
-constexpr size_t kStaticBytes = (size_t)kIdx * 8 + 2 * 2 * 4 * 64 * 16 + 2 * 2 * 2 * 64 * 16 + 2 * 32 * 4 +
-                                 kWaves * 4;
+constexpr size_t kStaticBytes = (size_t)kIdx * 8 + 2 * 2 * 2 * 64 * 16 + 2 * 2 * 2 * 64 * 16 + 2 * 2 * 32 * 4 +
+                                 2 * 32 * 4 + 2 * 2 * 32 * 4 + kWaves * 4;
 static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
 static_assert(kDmaStep * kRole * 1024 == kStepBytes, "DMA split");
 static_assert(kEnt * kThreads == kIdx, "table split");
@@ -87,9 +89,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     uint8_t *ring = smem;
     __shared__ __attribute__((aligned(16))) int32_t s_row[kIdx];   // row, or -1 if masked
     __shared__ __attribute__((aligned(16))) int32_t s_next[kIdx];  // index list of the next query (raw)
-    __shared__ f32x4 s_xch[2][2][4][64];        // partial logits [hg][dh][quad][lane]
+    __shared__ f32x4 s_xch[2][2][2][64];        // partial logits for the partner [hg][dh][quad][lane]
     __shared__ bf16x8 s_p[2][2][2][64];         // PV A operands [step parity][hg][k-step][lane]
-    __shared__ float s_l[2][32];                // row sums [hg][head]
+    __shared__ float s_l[2][2][32];             // row sums [hg][k-step half][head]
+    __shared__ float s_m[2][32];                // reference max [hg][head]
+    __shared__ float s_x[2][2][32];             // group max exchange [hg][dh][head]
     __shared__ __attribute__((aligned(16))) int s_vote[kWaves];
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
@@ -97,8 +101,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const int hg = rw & 1, sub = rw >> 1;       // head group; dim half (QK) or output half (PV)
     const int tid = threadIdx.x;
     const int H = a.n_heads;
-    const int head = 32 * hg + col;
-    const bool hv = head < H;
     const int total_q = a.batch.total_q;
     const int S = a.n_split;                    // parts per query (virtual queries per row)
     const int total_v = total_q * S;
@@ -264,6 +266,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             }
             return s;
         };
+        // largest value of a head over both QK waves of its head group; the
+        // PV waves take the barriers and get a value they do not use
+        auto group_max = [&](float v) -> float {
+            if constexpr (QK) {
+                if (g == 0) s_x[hg][sub][col] = v;
+            }
+            lds_barrier();
+            const float r = fmaxf(s_x[hg][0][col], s_x[hg][1][col]);
+            lds_barrier();
+            return r;
+        };
         // the query's Q^T from ring slot (cb + 1 + hg) % 3 (head rows in the
         // K-row layout)
         auto read_q = [&](int cb) {
@@ -347,6 +360,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             bool staged = true;
             m_run = -INFINITY;
             m_seen = -INFINITY;
+            bool need_init = true;                    // reference max not yet set (uniform)
             for (;;) {                                // attempts: one unless a block overshoots
                 if constexpr (!QK) {
 #pragma unroll
@@ -387,53 +401,57 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's gathers of step t landed
                         lds_barrier();       // step t everywhere; PV of t - 2 done; P of t - 1 posted
                         if constexpr (QK) {
+                            // Each wave of the pair finalizes half of the keys:
+                            // keys 16g + 8 dh .. +7 of lane (col, g), i.e.
+                            // elements 8 dh .. +7 of the tile (k-step dh of PV);
+                            // the partner's partial logits for them cross
+                            // through LDS.
+                            const int m8 = 8 * sub, o8 = 8 * (sub ^ 1);
                             f32x16 s = zero16();
                             if (t < n_steps) {
                                 s = qk(ring + sl * kStepBytes);
-#pragma unroll
-                                for (int q4 = 0; q4 < 4; ++q4)
-                                    s_xch[hg][sub][q4][lane] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+                                s_xch[hg][sub][0][lane] = f32x4{s[o8], s[o8 + 1], s[o8 + 2], s[o8 + 3]};
+                                s_xch[hg][sub][1][lane] = f32x4{s[o8 + 4], s[o8 + 5], s[o8 + 6], s[o8 + 7]};
                             }
                             lds_barrier();   // mid-step: both halves' partial logits posted
+                            float x[8];
+                            float mx = -INFINITY;
                             if (t < n_steps) {
-                                // logits of head `col`, keys (LDS rows) 16g .. 16g+15
-                                // (entries e0 ..): own half plus the partner's
+                                // base-2 logits of head `col` (own partial plus the
+                                // partner's), -inf where masked
+                                const int e0 = kBlk * t + 16 * g + m8;
 #pragma unroll
-                                for (int q4 = 0; q4 < 4; ++q4) {
+                                for (int q4 = 0; q4 < 2; ++q4) {
                                     const f32x4 v = s_xch[hg][sub ^ 1][q4][lane];
-#pragma unroll
-                                    for (int j = 0; j < 4; ++j) s[4 * q4 + j] += v[j];
-                                }
-                                const int e0 = kBlk * t + 16 * g;
-                                float mx = -INFINITY;
-#pragma unroll
-                                for (int q4 = 0; q4 < 4; ++q4) {
                                     const int4 rv = *(const int4 *)&s_row[e0 + 4 * q4];
 #pragma unroll
                                     for (int j = 0; j < 4; ++j) {
                                         const int e = 4 * q4 + j;
-                                        s[e] = rv[j] >= 0 ? s[e] * a.scale_log2 : -INFINITY;
-                                        mx = fmaxf(mx, s[e]);
+                                        x[e] = rv[j] >= 0 ? (s[m8 + e] + v[j]) * a.scale_log2 : -INFINITY;
+                                        mx = fmaxf(mx, x[e]);
                                     }
                                 }
                                 mx = fmaxf(mx, xor32(mx));
+                            }
+                            if (!kPV && need_init) {     // uniform: the first step of the query
+                                m_run = group_max(mx);
+                                need_init = false;
+                            }
+                            if (t < n_steps) {
                                 m_seen = fmaxf(m_seen, mx);
-                                if (m_run == -INFINITY) m_run = mx;          // first valid keys
+                                // also catches valid keys while the reference is unset (-inf)
                                 my_vote |= __any(mx > m_run + kHeadroom);
                                 const float msub = m_run == -INFINITY ? 0.f : m_run;
-                                bf16x8 pa[2];
+                                bf16x8 pa;
                                 float psum = 0.f;
 #pragma unroll
-                                for (int e = 0; e < 16; ++e) {
-                                    const float p = __builtin_amdgcn_exp2f(fminf(s[e] - msub, kClampLog2));
+                                for (int e = 0; e < 8; ++e) {
+                                    const float p = __builtin_amdgcn_exp2f(fminf(x[e] - msub, kClampLog2));
                                     psum += p;
-                                    pa[e >> 3][e & 7] = (__bf16)p;
+                                    pa[e] = (__bf16)p;
                                 }
                                 l_run += psum;
-                                if (sub == 0) {
-                                    s_p[t & 1][hg][0][lane] = pa[0];
-                                    s_p[t & 1][hg][1][lane] = pa[1];
-                                }
+                                s_p[t & 1][hg][sub][lane] = pa;
                             }
                         } else {
                             // this iteration's gathers: rows read up front, one
@@ -471,6 +489,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                     issue(nb);
                                 }
                                 if (kNT == kMidTile) mid();
+                                if (need_init) {         // the QK waves' group max
+                                    group_max(0.f);
+                                    need_init = false;
+                                }
                             }
                         }
                         sl = sln;
@@ -489,16 +511,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                     cb = (cb + n_steps - 1) % kRingSteps;        // the next chunk's step 0: the last step's slot
                 }
                 if (!redo) break;
-                m_run = fmaxf(m_run, m_seen);                    // redo with the largest block max seen
+                // redo the query with a larger reference: the head group's largest block max
+                m_run = fmaxf(m_run, group_max(m_seen));
             }
 
-            // ---- epilogue: the row sums (identical in both QK waves of a head
-            // group); LSE (QK waves); O / l (PV waves)
+            // ---- epilogue: the QK waves post their halves of the row sums and
+            // the reference max; the PV waves write O / l and the LSE
             if constexpr (QK) {
-                const float lt = l_run + xor32(l_run);
-                if (sub == 0 && g == 0) s_l[hg][col] = lt;
-                if (sub == 0 && g == 0 && hv)
-                    a.lse[orow * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+                const float lh = l_run + xor32(l_run);
+                if (g == 0) s_l[hg][sub][col] = lh;
+                if (sub == 0 && g == 0) s_m[hg][col] = m_run;
             }
             lds_barrier();
             if constexpr (!QK) {
@@ -510,8 +532,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 // query loop.
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
-                const float lt = s_l[hg][ln & 31];
+                const float lt = s_l[hg][0][ln & 31] + s_l[hg][1][ln & 31];
                 const float inv = lt > 0.f ? 1.f / lt : 0.f;
+                if (sub == 0 && ln < 32 && 32 * hg + ln < H)
+                    a.lse[orow * H + 32 * hg + ln] = lt > 0.f ? (s_m[hg][ln] + __log2f(lt)) * kLn2 : -INFINITY;
                 __bf16 *stage = (__bf16 *)(ring + cb * kStepBytes) + rw * 32 * O_LD;
                 __bf16 *st_w = stage + (ln & 31) * O_LD + 4 * (ln >> 5);
                 const __bf16 *st_r = stage + (ln >> 4) * O_LD + 8 * (ln & 15);
