@@ -20,11 +20,12 @@
 //    PV): it posts the partner's half of its partial tile, meets it at a
 //    second barrier, adds the partner's partials to its own half, and runs
 //    the softmax there, posting those probabilities (bf16) for PV.
-//  * PV waves (4..7): wave 4 + v owns head group v & 1 and output dims
-//    256 (v >> 1) .. +255: O^T[dim x head] += V^T[dim x key] P^T[key x head]
-//    of the previous step, with P from LDS and V read key-major with
-//    ds_read_b64_tr_b16; they also issue every gather (the rows of the next
-//    step, or the next query's Q).
+//  * PV waves (4..7): wave 4 + v owns output dims 128 v .. +127 of all 64
+//    heads: O^T[dim x head] += V^T[dim x key] P^T[key x head] of the previous
+//    step, with P from LDS and V read key-major with ds_read_b64_tr_b16, each
+//    V fragment once per step for both head groups (the transposed reads are
+//    the slowest LDS traffic of the step); they also issue every gather (the
+//    rows of the next step, or the next query's Q).
 //  * Registers: a QK wave holds its Q^T half (72 VGPRs), a PV wave O^T (128).
 //    The roles run in separate code paths and the file is built with MFMA
 //    accumulators in VGPRs, so both fit one allocation (about 220).
@@ -65,9 +66,10 @@ constexpr int kIdx = 2048;                                 // index-list entries
 constexpr int kEnt = kIdx / kThreads;                      // table entries per thread
 constexpr int kQKHalf = kQK / 2;                           // 288 dims per QK wave
 constexpr int kKS = kQKHalf / 16;                          // 18 k-steps
-constexpr int kVHalf = kV / 2;                             // 256 output dims per PV wave
-constexpr int kNT = kVHalf / 32;                           // 8 output tiles
-constexpr int O_LD = kVHalf / 2 + 8;                       // epilogue staging pitch (bf16): 128 dims a pass
+constexpr int kVQ = kV / kRole;                            // 128 output dims per PV wave
+constexpr int kDT = kVQ / 32;                              // 4 dim tiles
+constexpr int kNT = 2 * kDT;                               // 8 output tiles (dim tile x head group)
+constexpr int O_LD = kVQ + 8;                              // epilogue staging pitch (bf16): 128 dims a pass
 // the PV waves take the mid-step barrier after this many PV tiles
 constexpr int kMidTile = 4;
 
@@ -78,7 +80,7 @@ static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
 static_assert(kDmaStep * kRole * 1024 == kStepBytes, "DMA split");
 static_assert(kEnt * kThreads == kIdx, "table split");
 static_assert((size_t)kRole * 32 * O_LD * 2 <= kStepBytes, "staging fits a ring slot");
-static_assert(kDmaStep == 9 && kNT == 8 && kKS == 18, "schedule");
+static_assert(kDmaStep == 9 && kNT == 8 && kDT == 4 && kKS == 18, "schedule");
 
 template <int N> using IC = std::integral_constant<int, N>;
 
@@ -98,7 +100,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
     const int rw = wv & (kRole - 1);            // index within the role
-    const int hg = rw & 1, sub = rw >> 1;       // head group; dim half (QK) or output half (PV)
+    const int hg = rw & 1, sub = rw >> 1;       // QK: head group and dim half; PV: rw is the dim quarter
     const int tid = threadIdx.x;
     const int H = a.n_heads;
     const int total_q = a.batch.total_q;
@@ -240,8 +242,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         // 8u .. +7 (LDS chunk 36 sub + 4t + 2g + u of the head's row)
         bf16x8 qf[QK ? kKS : 1];
         float m_run = -INFINITY, l_run = 0.f, m_seen = -INFINITY;   // head `col`
-        // PV role: O^T[dim x head], 8 tiles of 32 dims x 32 heads (lane (head
-        // col, g) holds dims 32 nb + 8 i + 4 g + j in element 4 i + j)
+        // PV role: O^T[dim x head], 8 tiles of 32 dims x 32 heads, tile
+        // nb = 2 dt + h for dims 128 rw + 32 dt .. and head group h (lane (head
+        // col, g) holds dims 32 dt + 8 i + 4 g + j in element 4 i + j)
         f32x16 o[QK ? 1 : kNT];
 
         // K rows: accumulator row m = col reads LDS row qk_row; chunk
@@ -294,21 +297,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             }
         };
 
-        // PV of one ring slot: O^T[256 sub .., :] += V^T P^T; k-step t = LDS
+        // PV of one ring slot: O^T[128 rw .., :] += V^T P^T; k-step t = LDS
         // rows 16g + 8t .. +7. For the 32x32x16 MFMA a lane's 8 values of V^T
         // as the A operand (row = dim) are those of V as a B operand (column =
         // dim), and P^T as B those of P as A, so the operands are read as for
         // O = P V and only their order is swapped; O^T puts one head in each
         // lane column. A lane supplies row 16g + 8t + 4v + (gi >> 2), dims
         // 4 (gi & 3) .. of the tile's 16-dim group: logical chunk
-        // 32 sub + 4 nb + 2 hh + ((gi & 3) >> 1), swizzled by those rows'
-        // bf16_swz (which does not depend on t). mid() runs after tile
-        // kMidTile - 1, issue(nb) after tile nb.
-        auto pv = [&](const uint8_t *kb, const bf16x8 *pa, auto &&issue, auto &&mid) {
+        // 16 rw + 4 dt + 2 hh + ((gi & 3) >> 1), swizzled by those rows'
+        // bf16_swz (which does not depend on t). pa[h][t] is head group h's P
+        // of k-step t. mid() runs before tile kMidTile, issue(nb) after tile nb.
+        auto pv = [&](const uint8_t *kb, const bf16x8 (*pa)[2], auto &&issue, auto &&mid) {
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const int gi = ln & 15, hh = (ln >> 4) & 1, gg = ln >> 5;
-            const int L2 = 32 * sub + 2 * hh + ((gi & 3) >> 1);
+            const int L2 = 16 * rw + 2 * hh + ((gi & 3) >> 1);
             const uint8_t *vb0[2][2];
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
@@ -318,25 +321,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 vb0[v][1] = rb + 16 * ((L2 + 4) ^ sw);
             }
 #pragma unroll
-            for (int nb = 0; nb < kNT; ++nb) {
-                if (nb == kMidTile) mid();
+            for (int dt = 0; dt < kDT; ++dt) {
+                bf16x8 vb[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     bf16x4 w16[2];
 #pragma unroll
                     for (int v = 0; v < 2; ++v)
                         w16[v] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                            (lds_bf16x4_ptr)(vb0[v][nb & 1] + 128 * (nb >> 1) + 8 * kRowBytes * t));
-                    bf16x8 vb;
+                            (lds_bf16x4_ptr)(vb0[v][dt & 1] + 128 * (dt >> 1) + 8 * kRowBytes * t));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        vb[e] = w16[0][e];
-                        vb[4 + e] = w16[1][e];
+                        vb[t][e] = w16[0][e];
+                        vb[t][4 + e] = w16[1][e];
                     }
-                    if constexpr (!QK) o[nb] = mfma32x32x16(vb, pa[t], o[nb]);
                 }
-                issue(nb);
-                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int nb = 2 * dt + h;
+                    if (nb == kMidTile) mid();
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        if constexpr (!QK) o[nb] = mfma32x32x16(vb[t], pa[h][t], o[nb]);
+                    issue(nb);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             if (kNT == kMidTile) mid();
         };
@@ -478,9 +487,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                             };
                             auto mid = [&]() { lds_barrier(); };   // the QK waves' mid-step barrier
                             if constexpr (kPV) {
-                                bf16x8 pa[2];
-                                pa[0] = s_p[(t - 1) & 1][hg][0][lane];
-                                pa[1] = s_p[(t - 1) & 1][hg][1][lane];
+                                bf16x8 pa[2][2];
+#pragma unroll
+                                for (int h = 0; h < 2; ++h) {
+                                    pa[h][0] = s_p[(t - 1) & 1][h][0][lane];
+                                    pa[h][1] = s_p[(t - 1) & 1][h][1][lane];
+                                }
                                 pv(ring + slp * kStepBytes, pa, issue, mid);
                             } else {
 #pragma unroll
@@ -526,38 +538,40 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             if constexpr (!QK) {
                 // O^T / l as bf16, staged through the last step's slot (the next
                 // query's step 0: its first barrier comes before the gathers into
-                // it), 32 heads x 128 dims per wave and pass; each wave reads back
-                // only its own rows. Lane terms come from an opaque copy of the
-                // lane id, so they are computed here rather than held across the
-                // query loop.
+                // it), 32 heads x 128 dims per wave and pass (pass h: head group
+                // h); each wave reads back only its own rows. Lane terms come
+                // from an opaque copy of the lane id, so they are computed here
+                // rather than held across the query loop. Waves 4 and 5 write
+                // the LSE of head groups 0 and 1.
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
-                const float lt = s_l[hg][0][ln & 31] + s_l[hg][1][ln & 31];
-                const float inv = lt > 0.f ? 1.f / lt : 0.f;
-                if (sub == 0 && ln < 32 && 32 * hg + ln < H)
-                    a.lse[orow * H + 32 * hg + ln] = lt > 0.f ? (s_m[hg][ln] + __log2f(lt)) * kLn2 : -INFINITY;
+                if (rw < 2 && ln < 32 && 32 * rw + ln < H) {
+                    const float lr = s_l[rw][0][ln] + s_l[rw][1][ln];
+                    a.lse[orow * H + 32 * rw + ln] = lr > 0.f ? (s_m[rw][ln] + __log2f(lr)) * kLn2 : -INFINITY;
+                }
                 __bf16 *stage = (__bf16 *)(ring + cb * kStepBytes) + rw * 32 * O_LD;
                 __bf16 *st_w = stage + (ln & 31) * O_LD + 4 * (ln >> 5);
                 const __bf16 *st_r = stage + (ln >> 4) * O_LD + 8 * (ln & 15);
-                __bf16 *orow_p = a.out + (orow * H + 32 * hg + (ln >> 4)) * kV + kVHalf * sub + 8 * (ln & 15);
-                const int h_lane = 32 * hg + (ln >> 4);
+                __bf16 *orow_p = a.out + (orow * H + (ln >> 4)) * kV + kVQ * rw + 8 * (ln & 15);
 #pragma unroll
-                for (int ps = 0; ps < 2; ++ps) {
+                for (int h = 0; h < 2; ++h) {
+                    const float lt = s_l[h][0][ln & 31] + s_l[h][1][ln & 31];
+                    const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
-                    for (int nb = 0; nb < kNT / 2; ++nb)
+                    for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             bf16x4 v;
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[kNT / 2 * ps + nb][4 * i + j] * inv);
-                            *(bf16x4 *)(st_w + 32 * nb + 8 * i) = v;
+                            for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[2 * dt + h][4 * i + j] * inv);
+                            *(bf16x4 *)(st_w + 32 * dt + 8 * i) = v;
                         }
                     // 32 rows x 256 B: four rows per pass, 16 B per lane
 #pragma unroll
                     for (int it = 0; it < 8; ++it) {
                         const u32x4 v = *(const u32x4 *)(st_r + 4 * it * O_LD);
-                        if (h_lane + 4 * it < H)
-                            *(u32x4 *)(orow_p + (int64_t)4 * it * kV + (kVHalf / 2) * ps) = v;
+                        if (32 * h + (ln >> 4) + 4 * it < H)
+                            *(u32x4 *)(orow_p + (int64_t)(32 * h + 4 * it) * kV) = v;
                     }
                 }
             }
