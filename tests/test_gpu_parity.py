@@ -222,6 +222,39 @@ def test_wide_logit_range(sm, kv_dtype, listed):
     assert_close("wide lse", lse.cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("lead", [70, 2100])
+def test_masked_leading_entries(sm, kv_dtype, lead):
+    """Index lists whose first `lead` entries are all masked (-1, or keys past
+    the query's position): the query's first step (70: more than one 64-key
+    FP8 step) or its whole first 2,048-entry chunk (2,100) holds no valid key,
+    so the kernels start the query with no reference max and must redo it
+    once valid keys appear. One row is masked throughout (O = 0, LSE = -inf).
+    Every row against the oracle on the same lists."""
+    inp = _few_queries(kv_dtype, 70 + lead)
+    wl = inp["workload"]
+    batch = sm.Batch.from_inputs(inp)
+    q_pos = inp["q_pos_host"]
+    g = np.random.default_rng(71 + lead)
+    n_valid = 300
+    lists = np.full((wl.total_q, lead + n_valid), -1, np.int32)
+    for i, p in enumerate(q_pos):
+        past = p + 1 + g.integers(0, 50, lead)          # keys after the query's position
+        lists[i, :lead] = np.where(g.random(lead) < 0.5, -1, past)
+        m = min(p + 1, n_valid)
+        lists[i, lead:lead + m] = g.permutation(p + 1)[:m]
+    lists[wl.total_q // 2] = -1
+    idx = torch.from_numpy(lists).cuda()
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.total_q)
+    r_out, r_lse = oracle.attention_rows(inp, rows, lists)
+    assert np.isneginf(r_lse[wl.total_q // 2]).all()
+    tol = TOL[kv_dtype]
+    assert_close("masked-lead out", out.float().cpu().numpy(), r_out, tol, tol)
+    assert_close("masked-lead lse", lse.cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
+
+
 # --------------------------------------------------------------- indexer --
 @pytest.mark.parametrize("H,D", [(64, 128), (4, 64), (33, 128)])
 def test_indexer_small_integers_bit_exact(sm, H, D):
