@@ -37,8 +37,9 @@
 //    largest block max.
 //  * Accumulator row m = col of the QK A operand reads LDS row
 //    16((m >> 2) & 1) + 4(m >> 3) + (m & 3), so lane half g of the 32x32
-//    tile holds LDS rows 16g .. 16g+15 in element order: P in the A-operand
-//    layout of PV (k-step t = rows 16g + 8t .. +7).
+//    tile holds LDS rows 16g .. 16g+15 in element order: P^T in the B-operand
+//    layout of PV (the registers of P as an A operand; k-step t = rows
+//    16g + 8t .. +7).
 //  * Next query: the gathers of a chunk's last iteration and the one after
 //    it (where only the last step's PV runs) bring the next query's Q, one
 //    head group per ring slot, in the layout of the K rows; its index list
