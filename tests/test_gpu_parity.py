@@ -255,6 +255,66 @@ def test_masked_leading_entries(sm, kv_dtype, lead):
     assert_close("masked-lead lse", lse.cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
 
 
+def _random_batch(seed):
+    """A seeded random ragged batch: 1-4 sequences of 1..3,000 KV rows, each
+    with one or two runs of query positions (a CP-style gap when two)."""
+    g = np.random.default_rng(seed)
+    n_seq = int(g.integers(1, 5))
+    kv_lens, ranges = [], []
+    for _ in range(n_seq):
+        L = int(g.integers(1, 3001))
+        kv_lens.append(L)
+        a = int(g.integers(0, L))
+        b = int(min(L, a + g.integers(1, 40)))
+        r = [(a, b)]
+        if L - b > 2 and g.random() < 0.5:           # a second run after a gap
+            c = int(g.integers(b + 1, L))
+            r.append((c, int(min(L, c + g.integers(1, 20)))))
+        ranges.append(tuple(r))
+    return tuple(kv_lens), tuple(ranges), g
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_attention_random_batches(sm, seed):
+    """Seeded random ragged batches, head counts, k, KV types, list shapes
+    (the GPU's own top-k lists, or shuffled lists with masked entries mixed
+    in) and split counts: every row of every case against the oracle."""
+    kv_lens, ranges, g = _random_batch(1000 + seed)
+    n_heads = int(g.choice([8, 16, 32, 64]))
+    kv_dtype = ["bf16", "fp8"][seed % 2]
+    k = int(g.choice([1, 17, 256, 2048]))
+    wl = mla_inputs.Workload("rand%d" % seed, kv_lens, ranges, n_heads=n_heads, idx_heads=4,
+                             idx_dim=64, topk=k, kv_dtype=kv_dtype, seed=2000 + seed)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu"))
+    batch = sm.Batch.from_inputs(inp)
+    q_pos = inp["q_pos_host"]
+    if seed % 4 < 2:                                 # the GPU's own selection
+        sc = sm.indexer_score(batch, inp["q_idx"], inp["k_idx"], inp["w"])
+        idx = sm.topk_select(batch, sc, k)
+        lists = idx.cpu().numpy()
+    else:                                            # shuffled lists, masked entries mixed in
+        lists = np.full((wl.total_q, k), -1, np.int32)
+        for i, p in enumerate(q_pos):
+            m = min(p + 1, k)
+            sel = g.permutation(p + 1)[:m].astype(np.int32)
+            junk = g.random(m) < 0.2                 # some entries past the position
+            sel[junk] = p + 1 + g.integers(0, 30, int(junk.sum()))
+            lists[i, :m] = sel
+            lists[i] = lists[i][g.permutation(k)]
+        idx = torch.from_numpy(lists).cuda()
+    n_split = int(g.choice([1, 1, 2, 3]))
+    n_split = min(n_split, k)
+    say("[rand%d] %d seqs, %d queries, H=%d, k=%d, kv=%s, split=%d" %
+        (seed, len(kv_lens), wl.total_q, n_heads, k, kv_dtype, n_split))
+    kw = {} if n_split == 1 else {"n_split": n_split}
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale, **kw)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.total_q)
+    r_out, r_lse = oracle.attention_rows(inp, rows, lists)
+    tl.assert_attention("rand%d" % seed, kv_dtype, out.float().cpu().numpy(), lse.cpu().numpy(),
+                        r_out, r_lse, say)
+
+
 # --------------------------------------------------------------- indexer --
 @pytest.mark.parametrize("H,D", [(64, 128), (4, 64), (33, 128)])
 def test_indexer_small_integers_bit_exact(sm, H, D):
