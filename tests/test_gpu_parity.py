@@ -839,6 +839,29 @@ def test_fused_topk_tiny_and_ragged_all_rows(sm, idx_dtype):
     _fused_vs_unfused(sm, inp, "fused-ragged-" + idx_dtype, np.arange(wl.total_q))
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_path_random_batches(sm, seed):
+    """Seeded random ragged batches through the whole path: the indexer (bf16
+    or FP8 inputs; 4, 33 or 64 heads of 64 or 128 dims) against the oracle on
+    every row, top-k bit-exact against the oracle's selection on the GPU's
+    scores, attention (FP8 or bf16 rows) on every row, and the fused indexer +
+    top-k equal to the unfused pair, bit for bit."""
+    kv_lens, ranges, g = _random_batch(3000 + seed)
+    idx_heads = int(g.choice([4, 33, 64]))
+    idx_dim = int(g.choice([64, 128]))
+    k = int(g.choice([1, 17, 256, 2048]))
+    n_heads = int(g.choice([8, 16, 32, 64]))
+    kv_dtype = ["fp8", "bf16"][seed % 2]
+    idx_dtype = ["bf16", "fp8"][(seed // 2) % 2]
+    wl = mla_inputs.Workload("path%d" % seed, kv_lens, ranges, n_heads=n_heads, idx_heads=idx_heads,
+                             idx_dim=idx_dim, topk=k, kv_dtype=kv_dtype, seed=4000 + seed)
+    inp = to_gpu(mla_inputs.make_inputs(wl, "cpu", idx_dtype=idx_dtype))
+    say("[path%d] %d seqs, %d queries, indexer %dx%d %s, k=%d, H=%d, kv=%s" %
+        (seed, len(kv_lens), wl.total_q, idx_heads, idx_dim, idx_dtype, k, n_heads, kv_dtype))
+    check_path(sm, inp, np.arange(wl.total_q), "path%d" % seed)
+    _fused_vs_unfused(sm, inp, "path%d-fused" % seed)
+
+
 def _indexer_only(nq, L, H, D, k, q, kI, w, q_lo):
     """A one-sequence batch of nq queries at positions q_lo .. q_lo + nq - 1."""
     wl = mla_inputs.Workload("fused-custom", (L,), (((q_lo, q_lo + nq),),), n_heads=8,
