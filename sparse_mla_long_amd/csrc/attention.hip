@@ -76,10 +76,11 @@ constexpr int kMidTile = 4;
 
 constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
 constexpr size_t kStaticBytes = (size_t)kIdx * 8 + 2 * 2 * 2 * 64 * 16 + 2 * 2 * 2 * 64 * 16 + 2 * 2 * 32 * 4 +
-                                 2 * 32 * 4 + 2 * 2 * 32 * 4 + kWaves * 4;
+                                 2 * 32 * 4 + 2 * 2 * 32 * 4 + kWaves * 4 + (kIdx / kBlk) * 4;
 static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
 static_assert(kDmaStep * kRole * 1024 == kStepBytes, "DMA split");
 static_assert(kEnt * kThreads == kIdx, "table split");
+static_assert(2 * kBlk == kWave && kIdx % (4 * kBlk) == 0, "two table steps per wave and pass");
 static_assert((size_t)kRole * 32 * O_LD * 2 <= kStepBytes, "staging fits a ring slot");
 static_assert(kDmaStep == 9 && kNT == 8 && kDT == 4 && kKS == 18, "schedule");
 
@@ -98,6 +99,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     __shared__ float s_m[2][32];                // reference max [hg][head]
     __shared__ float s_x[2][2][32];             // group max exchange [hg][dh][head]
     __shared__ __attribute__((aligned(16))) int s_vote[kWaves];
+    // per step of the posted table: v + 1 if step v has an unmasked entry, else 0
+    __shared__ __attribute__((aligned(16))) int s_live[kIdx / kBlk];
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
     const int rw = wv & (kRole - 1);            // index within the role
@@ -195,6 +198,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         }
     };
     auto chunk_steps = [&](int c0) { return (min(kIdx, n_keys - c0) + kBlk - 1) / kBlk; };
+    // steps of the posted chunk up to its last one with an unmasked entry (at
+    // least one): trailing steps of masked entries (the -1 tail of a short
+    // index list) add nothing to l or O and are not run. Read after the
+    // table's barrier; the same value in every thread.
+    auto live_steps = [&]() -> int {
+        int last = 1;
+#pragma unroll
+        for (int i = 0; i < kIdx / kBlk / 4; ++i) {
+            const int4 v = *(const int4 *)&s_live[4 * i];
+            last = max(last, max(max(v.x, v.y), max(v.z, v.w)));
+        }
+        return __builtin_amdgcn_readfirstlane(last);
+    };
 
     // Row table of the chunk starting at entry c0 (jv: this thread's raw
     // entries): rows posted (-1 where masked), then the PV waves' gather of
@@ -206,6 +222,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             const int e = t + kThreads * i;
             jv[i] = e < cn && jv[i] >= 0 && jv[i] <= lim ? jv[i] : -1;
             s_row[e] = jv[i];
+            // a wave's 64 entries of pass i are two steps, one per lane half
+            const uint64_t live = __ballot(jv[i] >= 0);
+            if (lane == 0) {
+                const int st = e >> 5;
+                s_live[st] = (uint32_t)live != 0 ? st + 1 : 0;
+                s_live[st + 1] = (uint32_t)(live >> 32) != 0 ? st + 2 : 0;
+            }
         }
         lds_barrier();                                   // rows posted
         const uint8_t *kvq = a.kv + kv0 * a.kv_stride;
@@ -380,7 +403,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 bool redo = false;
                 bool my_vote = false;                 // wave-uniform
                 for (int c0 = 0; c0 < n_keys && !redo; c0 += kIdx) {
-                    const int n_steps = chunk_steps(c0);
                     if (!staged) {           // uniform: later chunks and redo attempts
                         const int cn = min(kIdx, n_keys - c0), t = tid_opq();
                         int jv[kEnt];
@@ -392,6 +414,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                         post_rows(c0, jv, cb, !QK);
                     }
                     staged = false;
+                    const int n_steps = DENSE ? chunk_steps(c0) : live_steps();
                     const uint8_t *kvq = a.kv + kv0 * a.kv_stride;
                     // Iteration t: QK waves compute the logits, softmax and P of
                     // step t (two barriers: the partial tiles cross between

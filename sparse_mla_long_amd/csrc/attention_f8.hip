@@ -82,11 +82,12 @@ constexpr int O_LD = 16 * kOwn + 8;                        // epilogue staging p
 
 constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
 constexpr size_t kStaticBytes = (size_t)kIdx * 12 + 2 * 2 * kRole * 2 * 32 * 16 + 2 * kRole * 32 * 4 +
-                                 2 * 2 * 32 * 4 + kWaves * 4 + 2 * kKB * 32;
+                                 2 * 2 * 32 * 4 + kWaves * 4 + 2 * kKB * 32 + (kIdx / 64) * 4;
 static_assert(kLdsBytes + kStaticBytes <= 160 * 1024, "LDS budget");
 static_assert(kDmaStep * kRole * 1024 == kStepBytes, "DMA split");
 static_assert(kTailBase + kBlk * kTailPitch == kBlockBytes, "block layout");
 static_assert(kEnt * kThreads == kIdx, "table split");
+static_assert(kStepBlocks * kBlk == kWave && kIdx % (4 * kWave) == 0, "one table step per wave and pass");
 static_assert((size_t)kRole * 32 * O_LD * 2 <= kStepBytes, "staging fits a ring slot");
 static_assert(kKB * kRole * 1024 == kStepBytes, "a head group's Q fills a ring slot");
 static_assert(kDmaStep == 9 && kOwn == 8 && kKB == 9, "gather issue schedule");
@@ -130,6 +131,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     __shared__ float s_x[2][2][32];             // [hg][block][head] exchange
     __shared__ __attribute__((aligned(16))) int s_vote[kWaves];
     __shared__ uint8_t s_qcode[2][kKB][32];     // Q scale codes [hg][k-block][head]
+    // per step of the posted table: v + 1 if step v has an unmasked entry, else 0
+    __shared__ __attribute__((aligned(16))) int s_live[kIdx / 64];
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
     const int rw = wv & (kRole - 1);            // index within the role
@@ -249,6 +252,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         }
     };
     auto chunk_steps = [&](int c0) { return (min(kIdx, n_keys - c0) + kStepBlocks * kBlk - 1) / (kStepBlocks * kBlk); };
+    // steps of the posted chunk up to its last one with an unmasked entry (at
+    // least one): trailing steps of masked entries (the -1 tail of a short
+    // index list) add nothing to l or O and are not run. Read after the
+    // table's barrier; the same value in every thread.
+    auto live_steps = [&]() -> int {
+        int last = 1;
+#pragma unroll
+        for (int i = 0; i < kIdx / 256; ++i) {
+            const int4 v = *(const int4 *)&s_live[4 * i];
+            last = max(last, max(max(v.x, v.y), max(v.z, v.w)));
+        }
+        return __builtin_amdgcn_readfirstlane(last);
+    };
 
     // Row table of the chunk starting at entry c0 (jv: its raw entries of this
     // thread): rows posted (-1 where masked), then the PV waves' gather of
@@ -261,6 +277,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             const int e = t + kThreads * i;
             jv[i] = e < cn && jv[i] >= 0 && jv[i] <= lim ? jv[i] : -1;
             s_row[e] = jv[i];
+            // a wave's 64 entries of pass i are one step
+            const bool live = __any(jv[i] >= 0);
+            if (lane == 0) s_live[e >> 6] = live ? (e >> 6) + 1 : 0;
         }
         lds_barrier();                                   // rows posted
         const uint8_t *kvq = a.kv + kv0 * a.kv_stride;
@@ -538,7 +557,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 bool redo = false;
                 bool my_vote = false;                     // wave-uniform
                 for (int c0 = 0; c0 < n_keys && !redo; c0 += kIdx) {
-                    const int n_steps = chunk_steps(c0);
                     const bool q_next = qn >= 0 && c0 + kIdx >= n_keys;
                     if (!staged) {           // uniform: later chunks and redo attempts
                         const int cn = min(kIdx, n_keys - c0), t = tid_opq();
@@ -551,6 +569,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                         post_rows(c0, jv, cb, !QK);
                     }
                     staged = false;
+                    const int n_steps = DENSE ? chunk_steps(c0) : live_steps();
                     const uint8_t *kvq = a.kv + kv0 * a.kv_stride;
                     // Iteration t: QK waves compute logits, softmax and weights
                     // of step t; PV waves run PV of step t - 1 and gather step

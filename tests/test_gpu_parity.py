@@ -255,6 +255,51 @@ def test_masked_leading_entries(sm, kv_dtype, lead):
     assert_close("masked-lead lse", lse.cpu().numpy(), r_lse, LSE_ATOL, LSE_RTOL)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("n_split", [1, 3])
+def test_masked_trailing_entries(sm, kv_dtype, n_split):
+    """Index lists of 4,200 entries whose valid keys stop early, the rest
+    masked (-1, or keys past the query's position): the valid prefix ends on
+    a 32- or 64-key step boundary, one entry after it, or in the first
+    2,048-entry chunk (later chunks and split parts then hold no valid key);
+    one row keeps a lone valid entry at 4,000 after a masked gap. Every row
+    against the oracle, and bit-identical to the same lists cut to 2,600
+    entries (trailing masked entries contribute nothing)."""
+    inp = _few_queries(kv_dtype, 90 + n_split)
+    wl = inp["workload"]
+    batch = sm.Batch.from_inputs(inp)
+    q_pos = inp["q_pos_host"]
+    g = np.random.default_rng(91 + n_split)
+    n_list = 4200
+    ends = [64, 65, 128, 2048, 2049, 31, 1, 0, 2600]
+    lists = np.full((wl.total_q, n_list), -1, np.int32)
+    for i, p in enumerate(q_pos):
+        m = min(ends[i % len(ends)], p + 1)
+        lists[i, :m] = g.permutation(p + 1)[:m]
+        tail = np.arange(m, n_list)
+        past = g.random(len(tail)) < 0.3                 # keys after the position
+        lists[i, tail[past]] = p + 1 + g.integers(0, 40, int(past.sum()))
+    lone = wl.total_q - 1
+    lists[lone] = -1
+    lists[lone, 4000] = q_pos[lone] // 2
+    kw = {} if n_split == 1 else {"n_split": n_split}
+    idx = torch.from_numpy(lists).cuda()
+    out, lse = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], idx, wl.sm_scale, **kw)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.total_q)
+    r_out, r_lse = oracle.attention_rows(inp, rows, lists)
+    tl.assert_attention("masked-tail split%d" % n_split, kv_dtype, out.float().cpu().numpy(),
+                        lse.cpu().numpy(), r_out, r_lse, say)
+    if n_split == 1:
+        cut = idx[:, :2600].contiguous()
+        keep = np.ones(wl.total_q, bool)
+        keep[lone] = False
+        o2, l2 = sm.sparse_prefill(batch, inp["q"], inp["kv"], inp["kv_scale"], cut, wl.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o2[torch.from_numpy(keep).cuda()], out[torch.from_numpy(keep).cuda()])
+        assert torch.equal(l2[torch.from_numpy(keep).cuda()], lse[torch.from_numpy(keep).cuda()])
+
+
 def _random_batch(seed):
     """A seeded random ragged batch: 1-4 sequences of 1..3,000 KV rows, each
     with one or two runs of query positions (a CP-style gap when two)."""
