@@ -15,8 +15,8 @@
 //    w >> 1 of every step. It computes the block's whole 576-dim logits on the
 //    FP8 MFMA, the softmax, and the PV weights P*sigma as an E4M3 hi + lo pair
 //    under a per-head E8M0 scale, which it posts to LDS.
-//  * PV waves (4..7): wave 4 + v owns head group v & 1 and output dims
-//    256 (v >> 1) .. +255. Step s's PV (both blocks, one 64-deep contraction)
+//  * PV waves (4..7): wave 4 + v owns output dims 128 v .. +127 of both head
+//    groups. Step s's PV (both blocks, one 64-deep contraction)
 //    runs while the QK waves work on step s + 1, with the weights the QK waves
 //    posted. The PV waves also issue every gather (rows of step s + 2, or the
 //    next query's Q), so a gather issue that waits for the memory pipeline
@@ -25,7 +25,7 @@
 //  PV MFMAs while the QK wave runs its softmax and weight split, and QK MFMAs
 //  while the PV wave waits on a gather issue. One barrier per step.
 //  * Registers: a QK wave holds Q^T as E4M3 hi + lo operands (144 VGPRs) for
-//    the whole query; a PV wave holds O^T (256 dims x 32 heads, fp32, 128
+//    the whole query; a PV wave holds O^T (128 dims x 64 heads, fp32, 128
 //    VGPRs). The roles run in separate code paths, so neither pays for the
 //    other's arrays, and the file is built with MFMA accumulators in VGPRs so
 //    both fit one 256-register allocation.
@@ -35,10 +35,11 @@
 //  * Softmax: accumulator element (i, j) of lane half g is LDS row
 //    16g + 4i + j of the block (the QK A operand reads rows in that order),
 //    which is the k order PV's operand wants.
-//  * PV: O^T[dim x head] += V^T[dim x key] P^T[key x head] over the wave's 256
+//  * PV: O^T[dim x head] += V^T[dim x key] P^T[key x head] over the wave's 128
 //    dims and the step's 64 keys (k 0..31 block 0, k 32..63 block 1, each
 //    under its own per-head scale); V is read key-major with
-//    ds_read_b64_tr_b8 (8 rows of one column per lane).
+//    ds_read_b64_tr_b8 (8 rows of one column per lane), once per step for
+//    both head groups.
 //  * Reference max per head shared by both QK waves of a head group (the max
 //    of the first step's two blocks), so their probabilities and row sums
 //    share one scale; blocks exceeding it by more than 2^kHeadroom vote for a
@@ -77,8 +78,9 @@ constexpr int kRingSteps = 3;                              // steps resident in 
 constexpr int kIdx = 2048;                                 // index-list entries per chunk
 constexpr int kEnt = kIdx / kThreads;                      // table entries per thread
 constexpr int kKB = kQK / 64;                              // QK k-blocks of the FP8 MFMA
-constexpr int kOwn = kV / 64;                              // output tiles (32 dims) per PV wave
-constexpr int O_LD = 16 * kOwn + 8;                        // epilogue staging pitch (bf16): 128 dims a pass
+constexpr int kDT = kV / kRole / 32;                       // dim tiles (32 dims) per PV wave
+constexpr int kOwn = 2 * kDT;                              // output tiles per PV wave: dim tile x head group
+constexpr int O_LD = 32 * kDT + 8;                         // epilogue staging pitch (bf16): 128 dims a pass
 
 constexpr size_t kLdsBytes = (size_t)kRingSteps * kStepBytes;                 // 110,592
 constexpr size_t kStaticBytes = (size_t)kIdx * 12 + 2 * 2 * kRole * 2 * 32 * 16 + 2 * kRole * 32 * 4 +
@@ -136,7 +138,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
     const int rw = wv & (kRole - 1);            // index within the role
-    const int hg = rw & 1, sub = rw >> 1;       // head group; block (QK) or dim half (PV)
+    const int hg = rw & 1, sub = rw >> 1;       // head group and block (QK); Q split part (both roles)
     const int tid = threadIdx.x;
     const int H = a.n_heads;
     const int head = 32 * hg + col;
@@ -454,21 +456,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             return s;
         };
 
-        // PV of one step (PV waves): O^T += V^T P^T over the wave's 256 dims,
-        // both blocks in one 64-deep contraction. Operand bytes 0..15 of lane
-        // half g are k 16g .. 16g+15, bytes 16..31 are k 32 + 16g .. ; the
-        // E8M0 scale of lane half g covers k 32g .. 32g+31. So k 0..31 are
-        // block 0's keys (LDS rows 16g .. 16g+15 for lane half g) and k 32..63
-        // block 1's. A lane (dim col, g) reads rows 16g + 8t + (gi >> 1),
-        // bytes 8 (gi & 1).. of chunk 2nb + hh of the wave's 256 dims;
-        // ds_read_b64_tr_b8 hands it rows 16g + 8t .. +7 of column col. Those
-        // rows share sm = 2 (gi >> 1) + g: logical chunk 2nb + hh sits at
-        // chunk 2nb ^ v_x. issue(nb) runs after tile nb's MFMAs.
+        // PV of one step (PV waves): O^T += V^T P^T over the wave's 128 dims
+        // and both head groups, both blocks in one 64-deep contraction.
+        // Operand bytes 0..15 of lane half g are k 16g .. 16g+15, bytes 16..31
+        // are k 32 + 16g .. ; the E8M0 scale of lane half g covers k 32g ..
+        // 32g+31. So k 0..31 are block 0's keys (LDS rows 16g .. 16g+15 for
+        // lane half g) and k 32..63 block 1's. For dim tile nb (dims 128 rw +
+        // 32 nb ..) a lane (dim col, g) reads rows 16g + 8t + (gi >> 1), bytes
+        // 8 (gi & 1).. of logical chunk 8 rw + 2nb + hh; ds_read_b64_tr_b8
+        // hands it rows 16g + 8t .. +7 of column col. Those rows share sm =
+        // 2 (gi >> 1) + g, so the chunk sits at (8 rw + 2nb) ^ v_x. The V
+        // operand of a dim tile feeds the MFMAs of both head groups (output
+        // tiles 2nb and 2nb + 1); issue(tile) runs after each tile's MFMAs.
         auto v_ld = [&](const uint8_t *kstep, int nb) -> i32x8 {
             const int gi = lane & 15;
             const int v_x = ((lane >> 4) & 1) ^ (2 * (gi >> 1) + g);
-            const uint8_t *rb = kstep + 256 * sub + (16 * g + (gi >> 1)) * kMainPitch + 8 * (gi & 1) +
-                                16 * ((2 * nb) ^ v_x);
+            const uint8_t *rb = kstep + (16 * g + (gi >> 1)) * kMainPitch + 8 * (gi & 1) +
+                                16 * ((8 * rw + 2 * nb) ^ v_x);
             i32x8 v;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -479,36 +483,42 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
             }
             return v;
         };
-        // B operand of PV: block 0's weights in bytes 0..15, block 1's in
-        // 16..31 (QK waves hg and hg + 2); lane half g carries block g's scale
+        // B operands of PV, one per head group h: block 0's weights in bytes
+        // 0..15, block 1's in 16..31 (QK waves h and h + 2); lane half g
+        // carries block g's scale
         struct PvOps {
-            i32x8 ah, al, vn;
-            int sa;
+            i32x8 ah[2], al[2], vn;
+            int sa[2];
         };
         auto pv_load = [&](const uint8_t *kstep, int par) -> PvOps {
-            const u32x4 h0 = s_ph[par][hg][g][col], h1 = s_ph[par][hg + 2][g][col];
-            const u32x4 l0 = s_pl[par][hg][g][col], l1 = s_pl[par][hg + 2][g][col];
             PvOps r;
-            r.sa = s_pe[par][hg + 2 * g][col];
-            r.ah = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-            r.al = i32x8{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 h0 = s_ph[par][h][g][col], h1 = s_ph[par][h + 2][g][col];
+                const u32x4 l0 = s_pl[par][h][g][col], l1 = s_pl[par][h + 2][g][col];
+                r.sa[h] = s_pe[par][h + 2 * g][col];
+                r.ah[h] = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+                r.al[h] = i32x8{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+            }
             r.vn = v_ld(kstep, 0);
             return r;
         };
         auto pv = [&](const uint8_t *kstep, const PvOps &ops, auto &&issue) {
-            const i32x8 ah = ops.ah, al = ops.al;
-            const int sa = ops.sa;
             i32x8 vn = ops.vn;
 #pragma unroll
-            for (int nb = 0; nb < kOwn; ++nb) {
+            for (int dt = 0; dt < kDT; ++dt) {
                 const i32x8 vb = vn;
-                if (nb + 1 < kOwn) vn = v_ld(kstep, nb + 1);
-                if constexpr (!QK) {
-                    o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, ah, o[nb], 0, 0, 0, 127, 0, sa);
-                    o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, al, o[nb], 0, 0, 0, 127, 0, sa);
+                if (dt + 1 < kDT) vn = v_ld(kstep, dt + 1);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int nb = 2 * dt + h;
+                    if constexpr (!QK) {
+                        o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, ops.ah[h], o[nb], 0, 0, 0, 127, 0, ops.sa[h]);
+                        o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, ops.al[h], o[nb], 0, 0, 0, 127, 0, ops.sa[h]);
+                    }
+                    issue(nb);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                issue(nb);
-                __builtin_amdgcn_sched_barrier(0);
             }
         };
 
@@ -716,39 +726,39 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 if (sub == 0 && g == 0 && hv)
                     a.lse[orow * H + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
             } else {
-                const float inv = lt > 0.f ? 1.f / lt : 0.f;
-                // O staged through the last step's slot (the next query's step
-                // 0), 32 heads x 128 dims per wave and pass; each wave reads back
-                // only its own rows. Lane (head col, g) holds dims 32 nb + 8 i +
-                // 4 g .. +3 of its head in accumulator elements 4 i .. 4 i + 3 of
-                // tile nb. (The next query's first barrier comes before the
-                // gathers into this slot.) Lane terms come from an opaque copy
-                // of the lane id, so they are computed here rather than held
-                // across the query loop.
+                // O^T / l as bf16, staged through the last step's slot (the next
+                // query's step 0), 32 heads x 128 dims per wave and pass (pass h:
+                // head group h); each wave reads back only its own rows. Lane
+                // (head col, g) holds dims 32 dt + 8 i + 4 g .. +3 of its head in
+                // accumulator elements 4 i .. 4 i + 3 of tile 2 dt + h. (The next
+                // query's first barrier comes before the gathers into this slot.)
+                // Lane terms come from an opaque copy of the lane id, so they are
+                // computed here rather than held across the query loop.
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
                 __bf16 *stage = (__bf16 *)(ring + cb * kStepBytes) + rw * 32 * O_LD;
                 __bf16 *st_w = stage + (ln & 31) * O_LD + 4 * (ln >> 5);
                 const __bf16 *st_r = stage + (ln >> 4) * O_LD + 8 * (ln & 15);
-                __bf16 *orow_p = a.out + (orow * H + 32 * hg + (ln >> 4)) * kV + 32 * kOwn * sub + 8 * (ln & 15);
-                const int h_lane = 32 * hg + (ln >> 4);
+                __bf16 *orow_p = a.out + (orow * H + (ln >> 4)) * kV + 32 * kDT * rw + 8 * (ln & 15);
 #pragma unroll
-                for (int ps = 0; ps < 2; ++ps) {
+                for (int h = 0; h < 2; ++h) {
+                    const float lh = s_x[h][0][ln & 31] + s_x[h][1][ln & 31];
+                    const float inv = lh > 0.f ? 1.f / lh : 0.f;
 #pragma unroll
-                    for (int nb = 0; nb < kOwn / 2; ++nb)
+                    for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             bf16x4 v;
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[kOwn / 2 * ps + nb][4 * i + j] * inv);
-                            *(bf16x4 *)(st_w + 32 * nb + 8 * i) = v;
+                            for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[2 * dt + h][4 * i + j] * inv);
+                            *(bf16x4 *)(st_w + 32 * dt + 8 * i) = v;
                         }
                     // 32 rows x 256 B: four rows per pass, 16 B per lane
 #pragma unroll
                     for (int it = 0; it < 8; ++it) {
                         const u32x4 v = *(const u32x4 *)(st_r + 4 * it * O_LD);
-                        if (h_lane + 4 * it < H)
-                            *(u32x4 *)(orow_p + (int64_t)4 * it * kV + 16 * kOwn * ps) = v;
+                        if (32 * h + (ln >> 4) + 4 * it < H)
+                            *(u32x4 *)(orow_p + (int64_t)(32 * h + 4 * it) * kV) = v;
                     }
                 }
             }
