@@ -183,6 +183,8 @@ void topk_kernel(TopkArgs a, int words) {
         kmin = min(kmin, s_mm[w]);
         kmax = max(kmax, s_mm[kWaves + w]);
     }
+    kmin = __builtin_amdgcn_readfirstlane(kmin);       // the same in every lane: keep it scalar
+    kmax = __builtin_amdgcn_readfirstlane(kmax);
     const uint32_t range = kmax - kmin;
 
     // ---- radix select on v = key - kmin: T (as v) and the number of ties needed
@@ -257,7 +259,7 @@ void topk_kernel(TopkArgs a, int words) {
             __syncthreads();
             if (level == 0) {
                 // classify: above T's first digit -> selected; in its bin -> candidate
-                const bool fits = in_bin <= kCandCap;
+                const bool fits = __builtin_amdgcn_readfirstlane(in_bin) <= kCandCap;
                 for (int base = 0; base < n; base += kThreads * kBatch) {
                   uint32_t kb[kBatch];
                   load_keys(base, kb);
@@ -265,23 +267,35 @@ void topk_kernel(TopkArgs a, int words) {
                   for (int u = 0; u < kBatch; ++u) {
                     const int j = base + u * kThreads + tid;
                     const int c = j >> 6;                        // 64-key chunk of this wave
-                    const uint32_t v = kb[u] - kmin;
-                    const uint32_t dj = v >> s;
-                    const bool above = j < n && dj > d;
-                    const bool inb = j < n && dj == d;
-                    const uint64_t ma = __ballot(above);
+                    const uint32_t dj = (kb[u] - kmin) >> s;
+                    const uint64_t ma = __ballot(j < n && dj > d);
                     if (lane == 0 && 2 * c < W) {
                         bm_sel[2 * c] = (uint32_t)ma;
                         if (2 * c + 1 < W) bm_sel[2 * c + 1] = (uint32_t)(ma >> 32);
                     }
-                    if (fits) {
-                        const uint64_t mc = __ballot(inb);
+                  }
+                  if (fits) {
+                    // the batch's bin members: one list reservation per wave
+                    uint64_t mc[kBatch];
+                    int tot = 0;
+#pragma unroll
+                    for (int u = 0; u < kBatch; ++u) {
+                        const int j = base + u * kThreads + tid;
+                        mc[u] = __ballot(j < n && ((kb[u] - kmin) >> s) == d);
+                        tot += __popcll(mc[u]);
+                    }
+                    if (tot != 0) {                              // uniform
                         int cb = 0;
-                        if (lane == 0 && mc) cb = atomicAdd(&s_cand_n, __popcll(mc));
-                        cb = __shfl(cb, 0);
-                        if (inb)
-                            cand[cb + __popcll(mc & ((1ull << lane) - 1ull))] =
-                                make_uint2(v + kmin, (uint32_t)j);
+                        if (lane == 0) cb = atomicAdd(&s_cand_n, tot);
+                        cb = __builtin_amdgcn_readfirstlane(cb);
+#pragma unroll
+                        for (int u = 0; u < kBatch; ++u) {
+                            const int j = base + u * kThreads + tid;
+                            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc[u] >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mc[u], 0u));
+                            if ((mc[u] >> lane) & 1ull) cand[cb + below] = make_uint2(kb[u], (uint32_t)j);
+                            cb += __popcll(mc[u]);
+                        }
                     }
                   }
                 }
