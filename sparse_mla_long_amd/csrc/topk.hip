@@ -10,10 +10,12 @@
 // range, so it already splits typical score distributions finely. A classify
 // pass marks every key whose first digit is above T's in a bitmap and
 // collects the keys of T's bin (usually a few dozen) into an LDS candidate
-// list; the remaining digits are resolved on that list alone. Candidates
-// above T join the bitmap, candidates equal to T go to a tie bitmap, and the
-// output is the selected bits in index order -- the first (k - #above) ties
-// by index -- written with two block scans.
+// list; the remaining digits are resolved on that list alone (a list of up
+// to kRankMax entries by ranking each entry against all of them, a longer
+// one by more radix digits). Candidates above T join the bitmap, candidates
+// equal to T go to a tie bitmap, and the output is the selected bits in index
+// order -- the first (k - #above) ties by index -- written with two block
+// scans.
 //
 // The row is read from global memory three times (range, first-digit
 // histogram, classify); the re-reads hit L2/MALL. Nothing but the bitmaps,
@@ -33,6 +35,7 @@ constexpr int kBins = 2048;                  // 11-bit digits
 constexpr int kDigit = 11;
 constexpr int kBatch = 8;                    // keys per thread per pass iteration
 constexpr int kVecBatch = 4;                 // 16-byte loads per thread in the first pass
+constexpr int kRankMax = 256;                // candidate lists up to this long are resolved by ranking
 constexpr int kCandCap = 1024;               // candidate list entries (a bin this size or more: one more pass)
 // longest rows: two bitmaps of kTopkMaxRow bits plus the candidate list beside the static LDS
 static_assert(2 * (kTopkMaxRow / 32) * 4 + kCandCap * 8 + 16 * 1024 <= 160 * 1024, "top-k LDS");
@@ -301,6 +304,29 @@ void topk_kernel(TopkArgs a, int words) {
                 }
                 __syncthreads();
                 use_list = fits;
+                const int cn = s_cand_n;
+                if (fits && s != 0 && cn <= kRankMax) {           // uniform
+                    // a short list: rank every candidate against all of them;
+                    // T is the key with (#larger) < rem <= (#larger) + (#equal)
+                    uint32_t key = 0u;
+                    int gt = 0, eq = 0;
+                    if (tid < cn) key = cand[tid].x;
+                    const uint32_t *ck = (const uint32_t *)cand;
+#pragma unroll 8
+                    for (int m = 0; m < cn; ++m) {
+                        const uint32_t km = ck[2 * m];
+                        gt += km > key ? 1 : 0;
+                        eq += km == key ? 1 : 0;
+                    }
+                    if (tid < cn && gt < rem && rem <= gt + eq) {
+                        s_sel[0] = (int)(key - kmin);
+                        s_sel[1] = rem - gt;
+                    }
+                    __syncthreads();
+                    prefix = (uint32_t)s_sel[0];
+                    rem = s_sel[1];
+                    break;
+                }
             }
             if (s == 0) break;
             const int s_next = max(0, s - kDigit);
