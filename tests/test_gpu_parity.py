@@ -460,8 +460,16 @@ def test_indexer_writes_only_causal_entries(sm, fp8, n_queries):
 
 # ----------------------------------------------------------------- top-k --
 @pytest.mark.parametrize("kind", ["all_equal", "relu_zeros", "small_int", "signed_zero", "normal",
-                                  "coarse", "sample_low", "sample_high"])
+                                  "coarse", "sample_low", "sample_high", "short_bin_ties",
+                                  "short_bin_few_ties"])
 def test_topk_ties_bit_exact(sm, kind):
+    """Selection bit-exact against the oracle's on score rows built to reach
+    each path of the kernel: one key value (no radix level), a threshold bin
+    too large for the candidate list (an extra pass: 12 of the 20 rows of
+    "normal"), a few dozen candidates resolved by ranking (positive scores on
+    a 1/256 or 1/1,024 grid: every row; up to 28 or 9 keys tie with the k-th
+    and in most rows only some of them are kept), and sampled or periodic
+    structure."""
     g = torch.Generator().manual_seed(3)
     n, L, k = 24, 70000, 2048
     pos = torch.tensor([0, 1, 2046, 2047, 2048, 2049, 5000, 32767, 32768, 32769, 40000, 69999] +
@@ -477,6 +485,9 @@ def test_topk_ties_bit_exact(sm, kind):
         s[:, ::97] = 1.0
     elif kind == "coarse":                 # many exact ties inside the threshold bin
         s = torch.round(torch.randn(n, L, generator=g) * 4) * 2.5
+    elif kind in ("short_bin_ties", "short_bin_few_ties"):
+        q = 256.0 if kind == "short_bin_ties" else 1024.0
+        s = torch.round((torch.randn(n, L, generator=g) + 8) * q) / q
     elif kind in ("sample_low", "sample_high"):
         # periodic structure: one 128-byte line in 16 holds the row's lowest
         # (or highest) scores, far from the rest
