@@ -285,9 +285,30 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         if constexpr (TOPK) append(sc, j, g == 0);
         else if (g == 0 && j <= pos) srow[j] = sc;
     };
+    // Stored scores (no fused top-k): a buffer store through a descriptor whose
+    // range is this query's row up to its position (zero bytes for an idle
+    // wave). The hardware drops a store whose offset falls outside the range,
+    // so keys past the position (and, in bf16, lane half 1, which holds the
+    // same scores) need no branch, and the store sits among the next
+    // sub-tile's MFMAs.
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t srsrc =
+        __builtin_amdgcn_make_buffer_rsrc(TOPK ? (void *)a.scores : (void *)srow, (short)0,
+                                          (pos + 1) * 4, 0x00020000);
+    auto store_nb = [&](float sc, int j0) {
+        const int off = g == 0 && j0 >= 0 ? 4 * (j0 + col) : 0x7ffffff0;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srsrc, off, 0, 0);
+    };
+    // FP8: store_pair's form of it (lanes 0-31 finish sub-tile a, 32-63 b)
+    auto store_pair_nb = [&](float a, int ja, float ska, float b, int jb, float skb) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        const float sc = (__uint_as_float(r[0]) + __uint_as_float(r[1])) * (g ? skb : ska);
+        const int j0 = g ? jb : ja;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srsrc, j0 >= 0 ? 4 * (j0 + col) : 0x7ffffff0, 0, 0);
+    };
     // FP8: lane-half sums of two sub-tiles, a (keys ja + col, key scale ska)
     // and b (jb, skb): one swap gives lanes 0-31 both halves of a and lanes
-    // 32-63 both halves of b, so every lane finishes and stores one score.
+    // 32-63 both halves of b, so every lane finishes and stores (or, fused,
+    // appends) one score.
     // (The bf16 form, at higher register pressure, finishes each sub-tile in
     // the epilogue: holding the halves spilled it.)
     auto store_pair = [&](float a, int ja, float ska, float b, int jb, float skb) {
@@ -308,9 +329,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         const uint8_t *kt = ktile[(t - t_lo) % kTileRing];
         // Software pipeline over 32-key sub-tiles: the MFMAs of sub-tile u share
         // a scheduling region (closed by a scheduling barrier) with the
-        // epilogue of sub-tile u-1; the scores are stored after the tile's
-        // MFMAs, so no branch splits that region. Sub-tiles past this query's
-        // position compute on later or repeated keys and are not stored.
+        // epilogue of sub-tile u-1 and its score store, a range-checked buffer
+        // store with no branch (FP8: a pair of sub-tiles at every odd u). The
+        // fused top-k appends after the tile's MFMAs, so its branches do not
+        // split those regions. Sub-tiles past this query's position compute on
+        // later or repeated keys and are not stored.
         float sc[kKeyTile / 32], sk[kKeyTile / 32];
         int sj[kKeyTile / 32];
 #pragma unroll
@@ -332,16 +355,27 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
                     for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(qf[mb][ks], bk, acc[mb]);
                 }
             }
-            sc[s] = epilogue(prev);                      // garbage before the first sub-tile: not stored
-            if constexpr (F8) sk[s] = prev_sk;
-            sj[s] = prev_j0;
+            if constexpr (!TOPK) {
+                if constexpr (F8) {                      // pairs of sub-tiles, finished at odd s
+                    sc[s] = epilogue(prev);
+                    sk[s] = prev_sk;
+                    sj[s] = prev_j0;
+                    if (s & 1) store_pair_nb(sc[s - 1], sj[s - 1], sk[s - 1], sc[s], sj[s], sk[s]);
+                } else {
+                    store_nb(epilogue(prev), prev_j0);   // none before the first sub-tile
+                }
+            } else {
+                sc[s] = epilogue(prev);                  // garbage before the first sub-tile: not stored
+                if constexpr (F8) sk[s] = prev_sk;
+                sj[s] = prev_j0;
+            }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) prev[mb] = acc[mb];
             if constexpr (F8) prev_sk = ((const float *)(kt + kTileBytes + 128 * s))[col];
             prev_j0 = t0 + 32 * s;
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (F8) {
+        if constexpr (F8 && TOPK) {
 #pragma unroll
             for (int s = 0; s < kKeyTile / 32; s += 2) store_pair(sc[s], sj[s], sk[s], sc[s + 1], sj[s + 1], sk[s + 1]);
         } else if constexpr (TOPK) {
@@ -352,17 +386,15 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
                 const int j0 = g ? sj[s + 1] : sj[s];
                 append(g ? sc[s + 1] : sc[s], j0 + col, j0 >= 0);
             }
-        } else {
-#pragma unroll
-            for (int s = 0; s < kKeyTile / 32; ++s)
-                if (sj[s] >= 0) store(sc[s], sj[s]);
         }
         if constexpr (TOPK) {
             if (__builtin_amdgcn_readfirstlane(nc) > a.cand_cap - kKeyTile) compact();
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail DMA lands before the LDS is freed
-    if constexpr (F8) store_pair(epilogue(prev), prev_j0, prev_sk, 0.f, -1, 0.f);
+    if constexpr (F8 && TOPK) store_pair(epilogue(prev), prev_j0, prev_sk, 0.f, -1, 0.f);
+    else if constexpr (F8) store_pair_nb(epilogue(prev), prev_j0, prev_sk, 0.f, -1, 0.f);
+    else if constexpr (!TOPK) store_nb(epilogue(prev), prev_j0);
     else store(epilogue(prev), prev_j0);
     if constexpr (TOPK) {
         // the list's length for cand_select_kernel (its entries land before
