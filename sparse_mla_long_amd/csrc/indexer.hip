@@ -226,18 +226,22 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         return;
     }
     float *srow = TOPK ? nullptr : a.scores + (int64_t)qi * a.ld;
-    // fused top-k: append this lane's score of key j (if ok) to the list
+    // fused top-k: append this lane's score of key j (if ok) to the list, with
+    // no branch: a buffer store through a descriptor over the list, where
+    // lanes that do not append get an offset outside it (the hardware drops
+    // such a store), so the append sits among the MFMAs
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t lrsrc =
+        __builtin_amdgcn_make_buffer_rsrc(clist, (short)0, TOPK && active ? a.cand_cap * 8 : 0, 0x00020000);
     auto append = [&](float sc, int j, bool ok) {
         const uint32_t key = cand::order_key(sc);
         const bool app = collect && ok && j <= pos && key > tau;
         const uint64_t m = __ballot(app);
-        if (app) {
-            const int at = nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            clist[at] = make_uint2(key, (uint32_t)j);
-            lmin = min(lmin, key);
-            lmax = max(lmax, key);
-        }
+        const int at = nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{key, (uint32_t)j}, lrsrc, app ? 8 * at : 0x7ffffff0, 0, 0);
+        lmin = app ? min(lmin, key) : lmin;
+        lmax = app ? max(lmax, key) : lmax;
         nc += __popcll(m);
     };
     // fused top-k: drop the entries that can no longer reach the top k
@@ -280,11 +284,6 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         }
         return sc;
     };
-    auto store = [&](float sc, int j0) {
-        const int j = j0 + col;
-        if constexpr (TOPK) append(sc, j, g == 0);
-        else if (g == 0 && j <= pos) srow[j] = sc;
-    };
     // Stored scores (no fused top-k): a buffer store through a descriptor whose
     // range is this query's row up to its position (zero bytes for an idle
     // wave). The hardware drops a store whose offset falls outside the range,
@@ -294,30 +293,23 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     [[maybe_unused]] const __amdgpu_buffer_rsrc_t srsrc =
         __builtin_amdgcn_make_buffer_rsrc(TOPK ? (void *)a.scores : (void *)srow, (short)0,
                                           (pos + 1) * 4, 0x00020000);
-    auto store_nb = [&](float sc, int j0) {
+    auto store = [&](float sc, int j0) {           // bf16: sub-tile at key j0 (lane half 0 stores)
         const int off = g == 0 && j0 >= 0 ? 4 * (j0 + col) : 0x7ffffff0;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srsrc, off, 0, 0);
     };
-    // FP8: store_pair's form of it (lanes 0-31 finish sub-tile a, 32-63 b)
-    auto store_pair_nb = [&](float a, int ja, float ska, float b, int jb, float skb) {
+    // FP8: lane-half sums of two sub-tiles, a (key scale ska) and b (skb): one
+    // swap gives lanes 0-31 both halves of a and lanes 32-63 both halves of b,
+    // so every lane finishes one score. (The bf16 form, at higher register
+    // pressure, finishes each sub-tile in the epilogue: holding the halves
+    // spilled it.)
+    auto finish_pair = [&](float a, float ska, float b, float skb) -> float {
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-        const float sc = (__uint_as_float(r[0]) + __uint_as_float(r[1])) * (g ? skb : ska);
+        return (__uint_as_float(r[0]) + __uint_as_float(r[1])) * (g ? skb : ska);
+    };
+    auto store_pair = [&](float a, int ja, float ska, float b, int jb, float skb) {
+        const float sc = finish_pair(a, ska, b, skb);
         const int j0 = g ? jb : ja;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srsrc, j0 >= 0 ? 4 * (j0 + col) : 0x7ffffff0, 0, 0);
-    };
-    // FP8: lane-half sums of two sub-tiles, a (keys ja + col, key scale ska)
-    // and b (jb, skb): one swap gives lanes 0-31 both halves of a and lanes
-    // 32-63 both halves of b, so every lane finishes and stores (or, fused,
-    // appends) one score.
-    // (The bf16 form, at higher register pressure, finishes each sub-tile in
-    // the epilogue: holding the halves spilled it.)
-    auto store_pair = [&](float a, int ja, float ska, float b, int jb, float skb) {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-        float sc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-        if constexpr (F8) sc *= g ? skb : ska;
-        const int j0 = g ? jb : ja, j = j0 + col;
-        if constexpr (TOPK) append(sc, j, j0 >= 0);
-        else if (j0 >= 0 && j <= pos) srow[j] = sc;
     };
 #pragma unroll
     for (int p = 0; p < kTileRing - 1; ++p) issue(t_lo + p, p);
@@ -329,11 +321,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         const uint8_t *kt = ktile[(t - t_lo) % kTileRing];
         // Software pipeline over 32-key sub-tiles: the MFMAs of sub-tile u share
         // a scheduling region (closed by a scheduling barrier) with the
-        // epilogue of sub-tile u-1 and its score store, a range-checked buffer
-        // store with no branch (FP8: a pair of sub-tiles at every odd u). The
-        // fused top-k appends after the tile's MFMAs, so its branches do not
-        // split those regions. Sub-tiles past this query's position compute on
-        // later or repeated keys and are not stored.
+        // epilogue of sub-tile u-1 and its score store (or, fused, its list
+        // append), a range-checked buffer store with no branch; pairs of
+        // sub-tiles finish at every odd u where the two lane halves split
+        // them. Sub-tiles past this query's position compute on later or
+        // repeated keys and are not stored.
         float sc[kKeyTile / 32], sk[kKeyTile / 32];
         int sj[kKeyTile / 32];
 #pragma unroll
@@ -355,19 +347,26 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
                     for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(qf[mb][ks], bk, acc[mb]);
                 }
             }
-            if constexpr (!TOPK) {
-                if constexpr (F8) {                      // pairs of sub-tiles, finished at odd s
-                    sc[s] = epilogue(prev);
-                    sk[s] = prev_sk;
-                    sj[s] = prev_j0;
-                    if (s & 1) store_pair_nb(sc[s - 1], sj[s - 1], sk[s - 1], sc[s], sj[s], sk[s]);
-                } else {
-                    store_nb(epilogue(prev), prev_j0);   // none before the first sub-tile
-                }
+            if constexpr (!F8 && !TOPK) {
+                store(epilogue(prev), prev_j0);          // none before the first sub-tile
             } else {
-                sc[s] = epilogue(prev);                  // garbage before the first sub-tile: not stored
+                // pairs of sub-tiles, finished at odd s (garbage before the
+                // first sub-tile: j0 < 0, not stored)
+                sc[s] = epilogue(prev);
                 if constexpr (F8) sk[s] = prev_sk;
                 sj[s] = prev_j0;
+                if (s & 1) {
+                    const int j0 = g ? sj[s] : sj[s - 1];
+                    if constexpr (!TOPK) {
+                        store_pair(sc[s - 1], sj[s - 1], sk[s - 1], sc[s], sj[s], sk[s]);
+                    } else if constexpr (F8) {
+                        append(finish_pair(sc[s - 1], sk[s - 1], sc[s], sk[s]), j0 + col, j0 >= 0);
+                    } else {
+                        // both lane halves hold each sub-tile's scores: half g
+                        // appends sub-tile s - 1 + g
+                        append(g ? sc[s] : sc[s - 1], j0 + col, j0 >= 0);
+                    }
+                }
             }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) prev[mb] = acc[mb];
@@ -375,26 +374,15 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
             prev_j0 = t0 + 32 * s;
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (F8 && TOPK) {
-#pragma unroll
-            for (int s = 0; s < kKeyTile / 32; s += 2) store_pair(sc[s], sj[s], sk[s], sc[s + 1], sj[s + 1], sk[s + 1]);
-        } else if constexpr (TOPK) {
-            // both lane halves hold each sub-tile's scores: half g appends
-            // sub-tile s + g of every pair
-#pragma unroll
-            for (int s = 0; s < kKeyTile / 32; s += 2) {
-                const int j0 = g ? sj[s + 1] : sj[s];
-                append(g ? sc[s + 1] : sc[s], j0 + col, j0 >= 0);
-            }
-        }
         if constexpr (TOPK) {
             if (__builtin_amdgcn_readfirstlane(nc) > a.cand_cap - kKeyTile) compact();
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail DMA lands before the LDS is freed
-    if constexpr (F8 && TOPK) store_pair(epilogue(prev), prev_j0, prev_sk, 0.f, -1, 0.f);
-    else if constexpr (F8) store_pair_nb(epilogue(prev), prev_j0, prev_sk, 0.f, -1, 0.f);
-    else if constexpr (!TOPK) store_nb(epilogue(prev), prev_j0);
+    // the last sub-tile (lanes 0-31 in the FP8 pair form; lane half 0 in bf16)
+    if constexpr (F8 && TOPK) append(finish_pair(epilogue(prev), prev_sk, 0.f, 0.f), prev_j0 + col, g == 0 && prev_j0 >= 0);
+    else if constexpr (F8) store_pair(epilogue(prev), prev_j0, prev_sk, 0.f, -1, 0.f);
+    else if constexpr (TOPK) append(epilogue(prev), prev_j0 + col, g == 0 && prev_j0 >= 0);
     else store(epilogue(prev), prev_j0);
     if constexpr (TOPK) {
         // the list's length for cand_select_kernel (its entries land before
