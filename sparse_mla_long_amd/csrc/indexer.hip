@@ -13,6 +13,8 @@
 // direct DMA through two 256-key tile slots shared by the eight waves (the
 // next tile loads while this one is used), 16-byte chunks XOR-swizzled by key
 // row so the B-operand reads are bank-conflict-free; one barrier per tile.
+// Scores leave through range-checked buffer stores among the MFMAs, so keys
+// past a query's position need no branch.
 //
 // FP8 variant (the same article, footnote 3: an indexer key is stored as 128
 // FP8 values plus a 4-byte scale). Queries and keys are E4M3 codes with an
@@ -39,6 +41,12 @@ constexpr int kTileRing = 2;
 // become +0, everything else passes unchanged. One instruction, where fmaxf
 // also canonicalises its operand first.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Word 3 of a buffer resource descriptor on this chip family: 32-bit data
+// format, raw (unswizzled, byte-offset) addressing. With stride 0 the
+// hardware range-checks each access against the descriptor's byte count and
+// drops a store that falls outside it.
+constexpr int kBufferWord3 = 0x00020000;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -231,7 +239,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     // lanes that do not append get an offset outside it (the hardware drops
     // such a store), so the append sits among the MFMAs
     [[maybe_unused]] const __amdgpu_buffer_rsrc_t lrsrc =
-        __builtin_amdgcn_make_buffer_rsrc(clist, (short)0, TOPK && active ? a.cand_cap * 8 : 0, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(clist, (short)0, TOPK && active ? a.cand_cap * 8 : 0, kBufferWord3);
     auto append = [&](float sc, int j, bool ok) {
         const uint32_t key = cand::order_key(sc);
         const bool app = collect && ok && j <= pos && key > tau;
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     // sub-tile's MFMAs.
     [[maybe_unused]] const __amdgpu_buffer_rsrc_t srsrc =
         __builtin_amdgcn_make_buffer_rsrc(TOPK ? (void *)a.scores : (void *)srow, (short)0,
-                                          (pos + 1) * 4, 0x00020000);
+                                          (pos + 1) * 4, kBufferWord3);
     auto store = [&](float sc, int j0) {           // bf16: sub-tile at key j0 (lane half 0 stores)
         const int off = g == 0 && j0 >= 0 ? 4 * (j0 + col) : 0x7ffffff0;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srsrc, off, 0, 0);
