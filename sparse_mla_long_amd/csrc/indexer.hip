@@ -80,7 +80,12 @@ template <> struct QOperand<true> { typedef i32x8 type; };
 // make the top k: at least k earlier keys are at or above it and win any tie
 // by their smaller index. If that leaves the list too long (a bin holding
 // most of the keys), the exact selection keeps just the top k -- ties at the
-// k-th value only with the smallest j -- and tau becomes the k-th value. The
+// k-th value only with the smallest j -- and tau becomes the k-th value.
+// Between compactions a running histogram counts the listed keys by bin;
+// after each tile's worth of new entries tau rises to the lower edge of the
+// bin where the count from the top reaches k (the same argument holds: at
+// least k listed keys are at or above it), so fewer keys are appended and
+// the next compaction takes that edge as t without a histogram pass. The
 // list therefore always holds every key that can still reach the top k, and
 // cand_select_kernel's exact selection over it (after this kernel) is the
 // top k of all the scores.
@@ -99,6 +104,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     constexpr int kSlotBytes = kTileBytes + (F8 ? 4 * kKeyTile : 0);
     __shared__ __attribute__((aligned(16))) uint8_t ktile[kTileRing][kSlotBytes];
     __shared__ uint32_t s_hist[TOPK ? kIdxWaves : 1][256];   // fused top-k: a radix histogram per wave
+    __shared__ uint32_t s_rh[TOPK ? kIdxWaves : 1][256];     // fused top-k: the list's keys by bin, per wave
     typedef typename QOperand<F8>::type QOp;
 
     const int lane = lane_id(), wv = wave_id(), g = lane >> 5, col = lane & 31;
@@ -194,10 +200,18 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     // FP8: every wave also brings 64 key scales (waves w and w + 4 write the
     // same values to the same place)
     auto issue = [&](int t, int slot) {
+        int ln = lane;                                  // fused top-k: lane terms recomputed
+        if constexpr (TOPK) asm volatile("" : "+v"(ln)); // here, not held (registers)
 #pragma unroll
         for (int u = 0; u < kDmaPerWave; ++u) {
-            const int j = min(t * kKeyTile + dma_r[u], pmax);
-            attn::dma16(kbytes + (kv0 + j) * RB + 16 * dma_c[u], &ktile[slot][(wv + kIdxWaves * u) * 1024]);
+            int dr = dma_r[u], dc = dma_c[u];
+            if constexpr (TOPK) {
+                const int sidx = (wv + kIdxWaves * u) * 64 + ln;
+                dr = sidx / CPR;
+                dc = (sidx % CPR) ^ kswz(dr);
+            }
+            const int j = min(t * kKeyTile + dr, pmax);
+            attn::dma16(kbytes + (kv0 + j) * RB + 16 * dc, &ktile[slot][(wv + kIdxWaves * u) * 1024]);
         }
         if constexpr (F8) {
             const int j = min(t * kKeyTile + 64 * (wv % (kKeyTile / 64)) + lane, pmax);
@@ -240,6 +254,21 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
     // such a store), so the append sits among the MFMAs
     [[maybe_unused]] const __amdgpu_buffer_rsrc_t lrsrc =
         __builtin_amdgcn_make_buffer_rsrc(clist, (short)0, TOPK && active ? a.cand_cap * 8 : 0, kBufferWord3);
+    // Running histogram of the listed keys (s_rh, 256 bins over a window set
+    // from the first keys this wave lists: hb = their smallest, bins of 2^hs
+    // keys, room for twice their range above, the end bins clamped). After
+    // every tile tau rises to the lower edge of the bin where the count from
+    // the top reaches k, so later appends are filtered without a pass over
+    // the list, and a compaction needs only its keep pass.
+    [[maybe_unused]] uint32_t *rh = s_rh[TOPK ? wv : 0];
+    uint32_t hb = 0u;
+    int hs = 0;
+    bool hv = false;                                    // window set (wave-uniform)
+    int tau_bin = 0;                                    // tau = edge(tau_bin) once hv
+    int nc_seen = 0;                                    // list length at the last tau update
+    auto rh_bin = [&](uint32_t key) -> uint32_t {
+        return key <= hb ? 0u : min((key - hb) >> hs, 255u);
+    };
     auto append = [&](float sc, int j, bool ok) {
         const uint32_t key = cand::order_key(sc);
         const bool app = collect && ok && j <= pos && key > tau;
@@ -250,28 +279,85 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{key, (uint32_t)j}, lrsrc, app ? 8 * at : 0x7ffffff0, 0, 0);
         lmin = app ? min(lmin, key) : lmin;
         lmax = app ? max(lmax, key) : lmax;
+        if (hv && app) atomicAdd(&rh[rh_bin(key)], 1u);
         nc += __popcll(m);
     };
-    // fused top-k: drop the entries that can no longer reach the top k
+    // rebuild the running histogram from the list as it stands
+    auto rh_rebuild = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rh[4 * lane + e] = 0u;
+        asm volatile("" ::: "memory");
+        const cand::Segments sg{clist, 0, 1, nullptr, nc};
+        cand::for_each(sg, [&](bool v, uint2 e) {
+            if (v) atomicAdd(&rh[rh_bin(cand::key_of(e))], 1u);
+        });
+        asm volatile("" ::: "memory");
+    };
+    // the lower edge of the bin where the count from the top reaches k (and
+    // that bin), or bin 0 / edge 0 while the list holds fewer than k keys
+    auto rh_threshold = [&](int &bin) -> uint32_t {
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = rh[4 * lane + e];
+        const int loc = (int)(h[0] + h[1] + h[2] + h[3]);
+        int suf = loc;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int y = __shfl_down(suf, off);
+            if (lane + off < kWave) suf += y;
+        }
+        int above = suf - loc, hit = -1;
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+            if (above < a.topk && a.topk <= above + (int)h[e]) hit = 4 * lane + e;
+            above += (int)h[e];
+        }
+        const uint64_t mh = __ballot(hit >= 0);
+        const int b = mh ? __builtin_amdgcn_readlane(hit, __ffsll((unsigned long long)mh) - 1) : 0;
+        bin = b;
+        return b == 0 ? 0u : hb + ((uint32_t)b << hs);
+    };
+    // the running histogram re-windowed to [lo, hi] (256 bins) and cleared
+    auto rh_window = [&](uint32_t lo, uint32_t hi) {
+        hb = __builtin_amdgcn_readfirstlane(lo);
+        hs = __builtin_amdgcn_readfirstlane(max(0, 32 - __clz((int)(hi - lo)) - 8));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rh[4 * lane + e] = 0u;
+        asm volatile("" ::: "memory");
+    };
+    // fused top-k: drop the entries that can no longer reach the top k. The
+    // threshold comes from the running histogram when it has one (no pass over
+    // the list), else from a histogram pass; the kept entries are counted into
+    // a histogram re-windowed to [threshold, largest listed key] as they are
+    // written back, so the bins narrow as tau rises.
     auto compact = [&]() {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's appends have landed
         uint32_t *hist = s_hist[TOPK ? wv : 0];
         const cand::Segments sg{clist, 0, 1, nullptr, nc};
-        uint32_t t = cand::wave_bin_threshold(sg, a.topk, cand::wave_umin(lmin), cand::wave_umax(lmax), hist);
-        nc = cand::wave_keep_from(sg, t, [&](int at, uint2 e) {
+        uint32_t t;
+        if (hv && tau_bin > 0) t = hb + ((uint32_t)tau_bin << hs);   // at least k listed keys >= t
+        else t = cand::wave_bin_threshold(sg, a.topk, cand::wave_umin(lmin), cand::wave_umax(lmax), hist);
+        const uint32_t top = cand::wave_umax(lmax);
+        rh_window(t, top);
+        auto keep_emit = [&](int at, uint2 e) {
             if (at < a.cand_cap) clist[at] = e;
-        });
+            atomicAdd(&rh[rh_bin(cand::key_of(e))], 1u);
+        };
+        nc = cand::wave_keep_from(sg, t, keep_emit);
         if (nc > (a.topk + a.cand_cap - kKeyTile) / 2) {   // most keys in one bin: the exact top k
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             const cand::Segments sk{clist, 0, 1, nullptr, nc};
             int need_eq;
             cand::wave_kth(sk, a.topk, hist, t, need_eq);
-            nc = cand::wave_compact(sk, t, need_eq, [&](int at, uint2 e) {
-                if (at < a.cand_cap) clist[at] = e;
-            });
+            rh_window(t, top);
+            nc = cand::wave_compact(sk, t, need_eq, keep_emit);
         }
-        tau = t;                                        // every kept key is at or above t
+        tau = max(tau, t);                              // every kept key is at or above t
+        tau_bin = 0;                                    // t is bin 0's lower edge now
         lmin = t;
+        hv = true;
+        nc_seen = nc;
     };
     f32x16 prev[MB];
     float prev_sk = 0.f;                                // FP8: scale of key prev_j0 + col
@@ -390,6 +476,24 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(IndexerArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (TOPK) {
+            if (!hv && nc > 0) {                        // first listed keys: set the window
+                hb = cand::wave_umin(lmin);
+                const uint32_t range = cand::wave_umax(lmax) - hb;
+                hs = max(0, 32 - __clz((int)range) - 7);
+                hb = __builtin_amdgcn_readfirstlane(hb);
+                hs = __builtin_amdgcn_readfirstlane(hs);
+                hv = true;
+                rh_rebuild();
+            }
+            if (hv && nc >= nc_seen + kKeyTile) {       // raise tau from the running histogram
+                nc_seen = nc;
+                int b;
+                const uint32_t th = rh_threshold(b);
+                if (b > 0 && th > tau) {
+                    tau = th;
+                    tau_bin = b;
+                }
+            }
             if (__builtin_amdgcn_readfirstlane(nc) > a.cand_cap - kKeyTile) compact();
         }
     }
