@@ -153,7 +153,7 @@ mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int6
  * batch and k (0 for an invalid batch, k < 1 or no query). It depends on the
  * current device's compute-unit count, which sets how the keys of a small
  * batch are split over workgroups: query it with the device the call will
- * run on current. About total_q * (2k + 256) * 8 bytes when the batch has at
+ * run on current. About total_q * (3k + 256) * 8 bytes when the batch has at
  * least two eight-query blocks per compute unit. */
 size_t mla_topk_workspace_size(const mla_batch_t *batch, int32_t k);
 

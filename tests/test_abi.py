@@ -246,7 +246,7 @@ def test_indexer_topk_argument_checks(lib, fp8):
     # 4 queries, one key part (no device: one CU, so no key split): lists of
     # cand_capacity(8) = 320 (key, j) entries, then the 4 list lengths
     assert size(ctypes.byref(b), 8) == (4 * 320 * 8 + 255) // 256 * 256 + 4 * 4
-    assert size(ctypes.byref(b), 2048) == 4 * 4352 * 8 + 4 * 4
+    assert size(ctypes.byref(b), 2048) == 4 * 6400 * 8 + 4 * 4
     assert size(ctypes.byref(b), 0) == 0 and size(None, 8) == 0
     bad, keep2 = make_batch(total_q=3)
     assert size(ctypes.byref(bad), 8) == 0
