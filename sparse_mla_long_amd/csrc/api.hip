@@ -282,7 +282,9 @@ mla_status_t mla_topk_select(const mla_batch_t *batch, const float *scores, int6
     a.indices = indices;
     a.k = k;
     a.max_row = batch->max_kv_len;
-    return hip_status(mla::launch_topk(a, (hipStream_t)stream), "top-k launch");
+    return hip_status(mla::launch_topk(a, batch->cu_seqlens_q_host, batch->cu_seqlens_kv_host,
+                                      (hipStream_t)stream),
+                      "top-k launch");
 }
 
 namespace {

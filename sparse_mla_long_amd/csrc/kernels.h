@@ -62,6 +62,7 @@ struct TopkArgs {
     int32_t *indices;      // [total_q, k]
     int32_t k;
     int32_t max_row;       // max_kv_len: longest possible score row
+    int32_t q_begin, q_end;  // this launch's query rows (set by launch_topk)
 };
 
 struct AttnArgs {
@@ -107,7 +108,9 @@ struct Ds656Args {
 hipError_t launch_ds656_decode(const Ds656Args &a, hipStream_t s);
 
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t s);
-hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+// cu_q_host / cu_kv_host: the batch's host cu_seqlens (the launch shape per sequence)
+hipError_t launch_topk(const TopkArgs &a, const int32_t *cu_q_host, const int32_t *cu_kv_host,
+                       hipStream_t s);
 hipError_t launch_cand_select(const CandSelectArgs &a, hipStream_t s);
 constexpr int32_t kTopkMaxRow = 1 << 19;   // longest score row top-k takes (its bitmaps sit in LDS)
 hipError_t launch_attention(const AttnArgs &a, bool fp8, hipStream_t s);

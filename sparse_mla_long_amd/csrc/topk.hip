@@ -3,8 +3,9 @@
 // nicht TP oder DP?": the indexer picks the 2,048 tokens sparse MLA attends
 // to). Ties go to the smaller key index; the kept indices come out ascending.
 //
-// One 512-thread workgroup per query row. Scores become order-preserving
-// 32-bit keys (-0 folded onto +0). A first pass over the row finds its key
+// One workgroup per query row (512 threads; 1,024 for sequences longer than
+// 64K keys, whose long rows want more loads in flight). Scores become
+// order-preserving 32-bit keys (-0 folded onto +0). A first pass over the row finds its key
 // range [kmin, kmax]; the k-th largest key T is then found by an MSD radix
 // select on v = key - kmin whose first 11-bit digit spans the row's actual
 // range, so it already splits typical score distributions finely. A classify
@@ -29,8 +30,11 @@
 namespace mla {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / kWave;
+// Threads per row: 512, or 1,024 for the rows of sequences longer than
+// kTopkWideRow keys (topk_rows picks per sequence). The digit select gives a
+// thread four bins, so a workgroup needs at least kBins / 4 threads.
+constexpr int kNarrow = 512, kWide = 1024;
+constexpr int kTopkWideRow = 65536;
 constexpr int kBins = 2048;                  // 11-bit digits
 constexpr int kDigit = 11;
 constexpr int kBatch = 8;                    // keys per thread per pass iteration
@@ -39,6 +43,7 @@ constexpr int kRankMax = 256;                // candidate lists up to this long 
 constexpr int kCandCap = 1024;               // candidate list entries (a bin this size or more: one more pass)
 // longest rows: two bitmaps of kTopkMaxRow bits plus the candidate list beside the static LDS
 static_assert(2 * (kTopkMaxRow / 32) * 4 + kCandCap * 8 + 16 * 1024 <= 160 * 1024, "top-k LDS");
+static_assert(4 * kNarrow >= kBins && kNarrow >= kRankMax, "one digit bin per thread and element");
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -59,6 +64,7 @@ __device__ __forceinline__ void hist_add(uint32_t *hist, bool pred, uint32_t d) 
 }
 
 // Exclusive prefix sum over thread order; `total` receives the block sum.
+template <int kWaves>
 __device__ __forceinline__ int block_excl_scan(int x, int *s_w, int &total) {
     const int lane = lane_id(), wv = wave_id();
     int inc = x;
@@ -81,9 +87,12 @@ __device__ __forceinline__ int block_excl_scan(int x, int *s_w, int &total) {
     return woff + inc - x;
 }
 
-// 64 VGPRs: eight waves per SIMD, several workgroups per CU
+// 64 VGPRs: eight waves per SIMD, several workgroups per CU. Rows q_end - 1
+// down to q_begin, one per workgroup, longest first.
+template <int kThreads>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void topk_kernel(TopkArgs a, int words) {
+    constexpr int kWaves = kThreads / kWave;
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ uint32_t hist[kBins];
     __shared__ int s_w[kWaves];
@@ -95,7 +104,7 @@ void topk_kernel(TopkArgs a, int words) {
     uint2 *cand = (uint2 *)(bm_eq + words);                      // [kCandCap] (key, index)
 
     const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
-    const int qi = a.batch.total_q - 1 - (int)blockIdx.x;
+    const int qi = a.q_end - 1 - (int)blockIdx.x;
     const int n = min(a.batch.q_pos[qi] + 1, a.max_row);
     const int k = a.k;
     int32_t *out = a.indices + (int64_t)qi * k;
@@ -241,7 +250,7 @@ void topk_kernel(TopkArgs a, int words) {
                     loc += (int)h[e];
                 }
                 int total;
-                const int before = block_excl_scan(loc, s_w, total);   // count in lower bins
+                const int before = block_excl_scan<kWaves>(loc, s_w, total);   // count in lower bins
                 int cum = before;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -386,7 +395,7 @@ void topk_kernel(TopkArgs a, int words) {
     int ecount = 0;
     for (int w = w0; w < w1; ++w) ecount += __popc(bm_eq[w]);
     int etot;
-    int ebefore = block_excl_scan(ecount, s_w, etot);
+    int ebefore = block_excl_scan<kWaves>(ecount, s_w, etot);
     int scount = 0;
     for (int w = w0; w < w1; ++w) {
         uint32_t eq = bm_eq[w];
@@ -404,7 +413,7 @@ void topk_kernel(TopkArgs a, int words) {
         scount += __popc(f);
     }
     int stot;
-    int pos_out = block_excl_scan(scount, s_w, stot);
+    int pos_out = block_excl_scan<kWaves>(scount, s_w, stot);
     for (int w = w0; w < w1; ++w) {
         uint32_t f = bm_sel[w];
         while (f) {
@@ -546,15 +555,41 @@ hipError_t launch_cand_select(const CandSelectArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
+namespace {
+template <int kThreads>
+hipError_t launch_rows(TopkArgs a, int q_begin, int q_end, int words, size_t lds, hipStream_t s) {
+    if (q_end <= q_begin) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute((const void *)topk_kernel<kThreads>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    a.q_begin = q_begin;
+    a.q_end = q_end;
+    hipLaunchKernelGGL(topk_kernel<kThreads>, dim3(q_end - q_begin), dim3(kThreads), lds, s, a, words);
+    return hipGetLastError();
+}
+}  // namespace
+
+// Rows of sequences with more than kTopkWideRow keys take 1,024 threads each
+// (their passes stream long rows, which more waves per row keep in flight),
+// the others 512 (short rows: more rows per CU). Consecutive sequences of one
+// kind share a launch; the launches go last sequence first, so the longest
+// rows of a causal batch start first, as inside a launch.
+hipError_t launch_topk(const TopkArgs &a, const int32_t *cu_q_host, const int32_t *cu_kv_host,
+                       hipStream_t s) {
     if (a.batch.total_q <= 0) return hipSuccess;
     const int words = (a.max_row + 31) / 32;
     const size_t lds = (size_t)2 * words * 4 + (size_t)kCandCap * 8;
-    const hipError_t e = hipFuncSetAttribute((const void *)topk_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_kernel, dim3(a.batch.total_q), dim3(kThreads), lds, s, a, words);
-    return hipGetLastError();
+    int b = a.batch.num_seqs;
+    while (b > 0) {
+        const bool wide = cu_kv_host[b] - cu_kv_host[b - 1] > kTopkWideRow;
+        int b0 = b - 1;
+        while (b0 > 0 && (cu_kv_host[b0] - cu_kv_host[b0 - 1] > kTopkWideRow) == wide) --b0;
+        const hipError_t e = wide ? launch_rows<kWide>(a, cu_q_host[b0], cu_q_host[b], words, lds, s)
+                                  : launch_rows<kNarrow>(a, cu_q_host[b0], cu_q_host[b], words, lds, s);
+        if (e != hipSuccess) return e;
+        b = b0;
+    }
+    return hipSuccess;
 }
 
 }  // namespace mla
