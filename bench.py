@@ -149,11 +149,15 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: st
         rec[key + "_factor"] = factor
         rec[key + "_copy_kib"] = kib
         for name in PATH_KERNELS[path]:
-            syms = KERNEL_SYMBOLS[name]
-            per_sym = [[float(r["Counter_Value"]) for r in rows
-                        if sym + "<" in r["Kernel_Name"] or sym + "(" in r["Kernel_Name"]]
-                       for sym in syms]
-            per_sym = [v for v in per_sym if v]
+            # one list per kernel instance (full name): a call may launch several
+            # (the top-k launches one per run of short or long sequences), so a
+            # launch's bytes are the sum over instances of their per-dispatch mean
+            per_inst = {}
+            for r in rows:
+                kn = r["Kernel_Name"]
+                if any(sym + "<" in kn or sym + "(" in kn for sym in KERNEL_SYMBOLS[name]):
+                    per_inst.setdefault(kn, []).append(float(r["Counter_Value"]))
+            per_sym = list(per_inst.values())
             if per_sym:
                 d = rec["kernels"].setdefault(name, {"source_hash": kernel_source_hash(name)})
                 kib = float(sum(np.mean(v) for v in per_sym))

@@ -5,10 +5,10 @@
 //
 // One workgroup per query row (512 threads; 1,024 for sequences longer than
 // 64K keys, whose long rows want more loads in flight). Scores become
-// order-preserving 32-bit keys (-0 folded onto +0). A first pass over the row finds its key
-// range [kmin, kmax]; the k-th largest key T is then found by an MSD radix
-// select on v = key - kmin whose first 11-bit digit spans the row's actual
-// range, so it already splits typical score distributions finely. A classify
+// order-preserving 32-bit keys (-0 folded onto +0). A first pass over the
+// row finds its key range [kmin, kmax]; the k-th largest key T is then found
+// by an MSD radix select on v = key - kmin whose first 11-bit digit spans the
+// row's actual range, so it already splits typical score distributions finely. A classify
 // pass marks every key whose first digit is above T's in a bitmap and
 // collects the keys of T's bin (usually a few dozen) into an LDS candidate
 // list; the remaining digits are resolved on that list alone (a list of up

@@ -87,6 +87,22 @@ def test_counter_ingestion_scales_by_the_copy(tmp_path, monkeypatch):
     assert "indexer" not in rec["kernels"] and "topk" not in rec["kernels"]
     assert bench.measured_traffic("sparse32k", "fp8", "indexer_topk", "bf16", "fused") == \
         pytest.approx(f["bytes"])
+    # two instances of one kernel per step (top-k rows of 512 and 1,024
+    # threads): a launch's bytes are the sum of their per-dispatch means
+    _write_csv(f_csv, [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 2 * 65536.0),
+                       ("mla::topk_kernel<1024>(x)", "FETCH_SIZE", 300.0),
+                       ("mla::topk_kernel<512>(x)", "FETCH_SIZE", 20.0),
+                       ("mla::topk_kernel<1024>(x)", "FETCH_SIZE", 100.0),
+                       ("mla::topk_kernel<512>(x)", "FETCH_SIZE", 40.0)])
+    _write_csv(w_csv, [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 65536.0),
+                       ("mla::topk_kernel<1024>(x)", "WRITE_SIZE", 6.0),
+                       ("mla::topk_kernel<512>(x)", "WRITE_SIZE", 2.0),
+                       ("mla::topk_kernel<1024>(x)", "WRITE_SIZE", 6.0),
+                       ("mla::topk_kernel<512>(x)", "WRITE_SIZE", 2.0)])
+    rec = bench.ingest_counters(str(f_csv), str(w_csv), 64, "ragged", "fp8", "cmd")
+    t = rec["kernels"]["topk"]
+    assert t["fetch_bytes"] == pytest.approx((200 + 30) * 1024 * 0.5)
+    assert t["write_bytes"] == pytest.approx(8 * 1024)
     # a changed kernel source invalidates the stored figure
     table = json.load(open(bench.TRAFFIC_FILE))
     table["sparse32k/fp8"]["kernels"]["attention"]["source_hash"] = "stale"
