@@ -31,8 +31,7 @@ namespace mla {
 namespace {
 
 // Threads per row: 512, or 1,024 for the rows of sequences longer than
-// kTopkWideRow keys (topk_rows picks per sequence). The digit select gives a
-// thread four bins, so a workgroup needs at least kBins / 4 threads.
+// kTopkWideRow keys (launch_topk picks per sequence).
 constexpr int kNarrow = 512, kWide = 1024;
 constexpr int kTopkWideRow = 65536;
 constexpr int kBins = 2048;                  // 11-bit digits
@@ -43,7 +42,6 @@ constexpr int kRankMax = 256;                // candidate lists up to this long 
 constexpr int kCandCap = 1024;               // candidate list entries (a bin this size or more: one more pass)
 // longest rows: two bitmaps of kTopkMaxRow bits plus the candidate list beside the static LDS
 static_assert(2 * (kTopkMaxRow / 32) * 4 + kCandCap * 8 + 16 * 1024 <= 160 * 1024, "top-k LDS");
-static_assert(4 * kNarrow >= kBins && kNarrow >= kRankMax, "one digit bin per thread and element");
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -93,6 +91,8 @@ template <int kThreads>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void topk_kernel(TopkArgs a, int words) {
     constexpr int kWaves = kThreads / kWave;
+    constexpr int kBinsPerThread = kBins / kThreads;   // the digit select's bins per thread
+    static_assert(kBinsPerThread * kThreads == kBins && kThreads >= kRankMax, "top-k block size");
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ uint32_t hist[kBins];
     __shared__ int s_w[kWaves];
@@ -241,11 +241,11 @@ void topk_kernel(TopkArgs a, int words) {
             // digit d with above(d) < rem <= above(d) + hist[d], above = count of larger digits
             {
                 const int nb = 1 << width;
-                uint32_t h[4];
+                uint32_t h[kBinsPerThread];
                 int loc = 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int bin = 4 * tid + e;
+                for (int e = 0; e < kBinsPerThread; ++e) {
+                    const int bin = kBinsPerThread * tid + e;
                     h[e] = bin < nb ? hist[bin] : 0u;
                     loc += (int)h[e];
                 }
@@ -253,10 +253,10 @@ void topk_kernel(TopkArgs a, int words) {
                 const int before = block_excl_scan<kWaves>(loc, s_w, total);   // count in lower bins
                 int cum = before;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < kBinsPerThread; ++e) {
                     const int above = total - cum - (int)h[e];
                     if (above < rem && rem <= above + (int)h[e]) {
-                        s_sel[0] = 4 * tid + e;
+                        s_sel[0] = kBinsPerThread * tid + e;
                         s_sel[1] = above;
                     }
                     cum += (int)h[e];
